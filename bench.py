@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of block-sparse attention with routing and residual on one MI355X.
+
+One step = the whole hot path on one attention layer: routing (pool, proxy,
+select, schedule) followed by the sparse forward with the dropped-block
+residual.  Inputs are seeded synthetic Q/K/V with the token-grid shape of the
+workload, resident in HBM before the timed region.
+
+    python bench.py [--steps K] [--warmup W] [--workload wan1.3b] [--tau-mode relative]
+
+Prints one JSON line.  value = dense-equivalent TFLOP/s = 4 B H N^2 d / step
+time.  roofline: the forward kernel's algorithmic flops per launch (exact
+kept tiles + one residual column per dropped block) over its average launch
+time measured with HIP events on its stream, against the bf16 dense MFMA peak.
+cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
+workload and extrapolated in executed query-key pairs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dense-equiv TFLOP/s & ms/call per attention layer at 1 MI355X; MFMA % of peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+FLASH_SRC = os.path.join(ROOT, "free_block_sparse_route_amd", "csrc", "sa_flash.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan1.3b")
+    ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--tau-mode", choices=("relative", "absolute"), default="relative")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 1 GiB (for scaling HBM counters)")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    return hashlib.sha256(open(FLASH_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str, tau_mode: str):
+    """HBM bytes per forward launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"flash_{workload}_{tau_mode}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("flash_source_sha256_16") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+
+
+def cpu_baseline(w, cfg, Qc, Kc, Vc, budget_s: float = 12.0):
+    """The oracle as it stands, on the host cores: routing of every head in full,
+    outputs on a seeded sample of query blocks until about budget_s seconds of
+    forward work, extrapolated linearly in executed query-key pairs."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import sparse_attn_ref as R
+
+    cores = len(os.sched_getaffinity(0))
+    p = R.RouteParams(cfg.block_q, cfg.block_k, float(np.float32(cfg.tau)), cfg.tau_mode, cfg.max_keep,
+                      cfg.min_keep, cfg.n_dense_prefix, cfg.scale)
+    n_j = R.block_counts(w.N, w.block_k)
+    m_i = R.block_counts(w.N, w.block_q)
+    with threadpool_limits(limits=cores):
+        used = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        t0 = time.perf_counter()
+        heads = {}
+        for b in range(w.B):
+            for h in range(w.H):
+                q = Qc[b, h].double().numpy()
+                k = Kc[b, h].double().numpy()
+                heads[(b, h)] = R.route_ref(q, k, p).mask
+        t_route = time.perf_counter() - t0
+
+        def pairs(mask_row, I):
+            return int(m_i[I]) * (int((n_j * mask_row).sum()) + int((~mask_row).sum()))
+
+        total_pairs = sum(pairs(m[I], I) for m in heads.values() for I in range(m.shape[0]))
+        rng = np.random.default_rng(0)
+        order = [(bh, int(I)) for bh in heads for I in range(w.n_qb)]
+        rng.shuffle(order)
+        t_fwd = 0.0
+        done_pairs = 0
+        n_blocks = 0
+        cache = {}
+        for (b, h), I in order:
+            if (b, h) not in cache:
+                cache.clear()
+                cache[(b, h)] = tuple(T[b, h].double().numpy() for T in (Qc, Kc, Vc))
+            q, k, v = cache[(b, h)]
+            t1 = time.perf_counter()
+            R.forward_ref_with_mask(q, k, v, heads[(b, h)], p, rows=[I])
+            t_fwd += time.perf_counter() - t1
+            done_pairs += pairs(heads[(b, h)][I], I)
+            n_blocks += 1
+            if t_fwd >= budget_s:
+                break
+    t_total = t_route + t_fwd * total_pairs / max(done_pairs, 1)
+    dense = 4.0 * w.B * w.H * w.N * w.N * w.d
+    return {"value": dense / t_total / 1e12, "unit": "TFLOP/s", "cores": int(used), "kind": "oracle",
+            "sample": (f"routing of all {len(heads)} heads timed in full ({t_route:.1f} s); forward on "
+                       f"{n_blocks} random query blocks ({t_fwd:.1f} s, {done_pairs / total_pairs:.2%} of the "
+                       f"executed query-key pairs), extrapolated linearly in executed pairs"),
+            "ms_per_step_extrapolated": t_total * 1e3, "host_cores_visible": cores}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not supported: "
+              "heads shard across GPUs with no exchange inside attention, so the per-GPU kernel "
+              "measured at --gpus 1 is the figure of interest.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+
+    import free_block_sparse_route_amd as sa
+    from workloads import synth as S
+
+    w = S.WORKLOADS[args.workload]
+    mode = sa.RELATIVE if args.tau_mode == "relative" else sa.ABSOLUTE
+    cfg = sa.Config(block_q=w.block_q, block_k=w.block_k, tau=w.tau if args.tau is None else args.tau,
+                    tau_mode=mode, max_keep=w.max_keep, min_keep=1, n_dense_prefix=w.n_text)
+    print(f"[bench] generating {w.name} B{w.B} H{w.H} N{w.N} d{w.d}", file=sys.stderr, flush=True)
+    Qc, Kc, Vc = S.make_qkv(w)
+    Q, K, V = Qc.cuda(), Kc.cuda(), Vc.cuda()
+    rt = sa.route(Q, K, V, cfg)
+    O = sa.forward(Q, K, V, rt, cfg)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        sa.route(Q, K, V, cfg, out=rt)
+        sa.forward(Q, K, V, rt, cfg, out=O)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        sa.route(Q, K, V, cfg, out=rt)
+        ev[i][1].record()
+        sa.forward(Q, K, V, rt, cfg, out=O)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    route_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    fwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+
+    # algorithmic work of one forward launch, from the route it consumed
+    mask = rt.mask()
+    n_j = torch.tensor([min(w.block_k, w.N - J * w.block_k) for J in range(rt.n_kb)], device=mask.device,
+                       dtype=torch.float64)
+    m_i = torch.tensor([min(w.block_q, w.N - I * w.block_q) for I in range(rt.n_qb)], device=mask.device,
+                       dtype=torch.float64)
+    kept_tok = (mask.double() * n_j).sum(-1)                  # [B,H,n_qb]
+    dropped = (~mask).double().sum(-1)
+    exact_flops = float(4.0 * w.d * (m_i * kept_tok).sum())
+    resid_flops = float(4.0 * w.d * (m_i * dropped).sum())
+    dense_flops = 4.0 * w.B * w.H * w.N * w.N * w.d
+    kept_frac = exact_flops / dense_flops
+    fwd_tflops = (exact_flops + resid_flops) / (fwd_ms * 1e-3) / 1e12
+
+    es = 2 if w.dtype == "bf16" else 4
+    route_bytes = 3.0 * w.B * w.H * w.N * w.d * es
+    route_gbs = route_bytes / (route_ms * 1e-3) / 1e9
+
+    dense_ms = None
+    if not args.no_dense:
+        Od = sa.dense_ref_gpu(Q, K, V, block_q=w.block_q)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        e0.record()
+        for _ in range(reps):
+            sa.dense_ref_gpu(Q, K, V, block_q=w.block_q, out=Od)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / reps
+
+    traffic = load_traffic(w.name, args.tau_mode)
+    out = {
+        "metric": METRIC,
+        "value": dense_flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32 in, bf16 products",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "block_q": w.block_q, "block_k": w.block_k, "tau": cfg.tau, "tau_mode": args.tau_mode,
+                   "max_keep": cfg.max_keep, "n_dense_prefix": cfg.n_dense_prefix,
+                   "kept_fraction": kept_frac},
+        "roofline": {"bound": "mfma", "achieved": fwd_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": fwd_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "kernel": "flash_kernel (sparse forward with residual)",
+                     "flops_per_launch": exact_flops + resid_flops, "avg_launch_ms": fwd_ms},
+        "route": {"ms": route_ms, "bytes_read": route_bytes, "GB/s": route_gbs,
+                  "frac_hbm": route_gbs / PEAK_HBM_GBS},
+        "forward_ms": fwd_ms,
+        "dense_ms": dense_ms,
+        "speedup_vs_dense": (dense_ms / (route_ms + fwd_ms)) if dense_ms else None,
+        "inverse_kept_fraction": 1.0 / kept_frac,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, cfg, Qc, Kc, Vc)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

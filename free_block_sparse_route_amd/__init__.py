@@ -1,0 +1,14 @@
+"""Block-sparse attention with block routing and a dropped-block residual,
+hand-written HIP for AMD Instinct MI355X (gfx950).
+
+    import free_block_sparse_route_amd as sa
+    cfg = sa.Config(block_q=128, block_k=128, tau=0.01)
+    rt = sa.route(q, k, v, cfg)          # block means, proxy rows, keep lists
+    o = sa.forward(q, k, v, rt, cfg)     # kept tiles exactly, dropped blocks by residual
+    o_dense = sa.dense_ref_gpu(q, k, v)  # same kernels, every block kept, no residual
+
+q, k, v: device tensors [B, H, N, d], bf16 or fp32, d in {64, 128}.
+"""
+from .binding import (ABSOLUTE, FLAG_NO_RESIDUAL, RELATIVE, Config, Route, SaParams, SaRoute,  # noqa: F401
+                      SparseAttnError, dense_flops, dense_ref_gpu, forward, kv_idx_cap, last_error,
+                      make_params, route, route_sizes, status_string)

@@ -1,0 +1,227 @@
+// C ABI: argument validation, buffer sizing and kernel launches.  Nothing here
+// allocates, frees or synchronises; every launch goes to the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sa_internal.h"
+#include "sparse_attn.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sa_status fail(sa_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+sa_status fail(sa_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+sa_status hip_fail(hipError_t e, const char *where) {
+    return fail(SA_ERR_HIP, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+struct Dims {
+    int n_qb, n_kb, words;
+    int64_t BH;
+};
+
+Dims dims_of(const sa_params *p) {
+    Dims d;
+    d.n_qb = (p->N + p->block_q - 1) / p->block_q;
+    d.n_kb = (p->N + p->block_k - 1) / p->block_k;
+    d.words = (d.n_kb + 31) / 32;
+    d.BH = (int64_t)p->B * p->H;
+    return d;
+}
+
+// Parameter checks common to every entry point.  `routing` adds the checks of
+// the routing fields.
+sa_status check_params(const sa_params *p, bool routing) {
+    if (!p) return fail(SA_ERR_INVALID_ARG, "params is NULL");
+    if (p->B < 1 || p->H < 1 || p->N < 1)
+        return fail(SA_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", p->B, p->H, p->N);
+    if (p->d < 1) return fail(SA_ERR_INVALID_ARG, "d must be >= 1 (got %d)", p->d);
+    if (p->block_q < 1 || p->block_k < 1)
+        return fail(SA_ERR_INVALID_ARG, "block sizes must be >= 1 (got %d, %d)", p->block_q, p->block_k);
+    if (p->dtype != SA_BF16 && p->dtype != SA_F32)
+        return fail(SA_ERR_INVALID_ARG, "dtype %d is not an sa_dtype", p->dtype);
+    if (!(p->scale >= 0.f) || isinf(p->scale))
+        return fail(SA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+    if (p->flags & ~SA_FLAG_NO_RESIDUAL) return fail(SA_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
+    const int64_t elems = (int64_t)p->B * p->H * p->N * p->d;
+    if (elems > ((int64_t)1 << 40)) return fail(SA_ERR_INVALID_ARG, "tensor too large");
+    if (routing) {
+        if (!(p->tau >= 0.f)) return fail(SA_ERR_INVALID_ARG, "tau must be >= 0 and not NaN");
+        if (p->tau_mode != SA_TAU_RELATIVE && p->tau_mode != SA_TAU_ABSOLUTE)
+            return fail(SA_ERR_INVALID_ARG, "tau_mode %d is not an sa_tau_mode", p->tau_mode);
+        if (p->max_keep < 0 || p->min_keep < 0)
+            return fail(SA_ERR_INVALID_ARG, "max_keep and min_keep must be >= 0");
+        if (p->n_dense_prefix < 0 || p->n_dense_prefix > p->N)
+            return fail(SA_ERR_INVALID_ARG, "n_dense_prefix must be in [0, N]");
+    }
+    if (p->d != 64 && p->d != 128) return fail(SA_ERR_UNSUPPORTED, "d = %d (supported: 64, 128)", p->d);
+    if ((p->block_q != 64 && p->block_q != 128) || (p->block_k != 64 && p->block_k != 128))
+        return fail(SA_ERR_UNSUPPORTED, "block sizes %d x %d (supported: 64 or 128 each)", p->block_q,
+                    p->block_k);
+    const Dims d = dims_of(p);
+    if (routing && d.n_kb > sa::kMaxKeyBlocks)
+        return fail(SA_ERR_UNSUPPORTED, "n_kb = %d exceeds %d", d.n_kb, sa::kMaxKeyBlocks);
+    if (d.BH * d.n_qb > INT32_MAX / 2) return fail(SA_ERR_UNSUPPORTED, "too many work items");
+    return SA_OK;
+}
+
+int32_t min_cap(const sa_params *p) {
+    const Dims d = dims_of(p);
+    // no cap, or a dense prefix (query block 0 then keeps every key block)
+    if (p->max_keep == 0 || p->n_dense_prefix > 0) return d.n_kb;
+    const int32_t floor_n = p->min_keep < d.n_kb ? p->min_keep : d.n_kb;
+    const int32_t lim = p->max_keep > floor_n ? p->max_keep : floor_n;
+    return lim < d.n_kb ? lim : d.n_kb;
+}
+
+sa_status check_ptr(const void *ptr, const char *name) {
+    if (!ptr) return fail(SA_ERR_INVALID_ARG, "%s is NULL", name);
+    return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sparse_attn_kv_idx_cap(const sa_params *p) {
+    const sa_status s = check_params(p, true);
+    if (s != SA_OK) return (int32_t)s;
+    return min_cap(p);
+}
+
+sa_status sparse_attn_route_sizes(const sa_params *p, int32_t kv_idx_cap, size_t *bytes) {
+    sa_status s = check_params(p, true);
+    if (s != SA_OK) return s;
+    if (!bytes) return fail(SA_ERR_INVALID_ARG, "bytes is NULL");
+    if (kv_idx_cap < min_cap(p))
+        return fail(SA_ERR_CAPACITY, "kv_idx_cap %d < required %d", kv_idx_cap, min_cap(p));
+    const Dims d = dims_of(p);
+    const size_t rows = (size_t)d.BH * d.n_qb;
+    bytes[SA_BUF_KV_COUNT] = rows * 4;
+    bytes[SA_BUF_KV_IDX] = rows * (size_t)kv_idx_cap * 4;
+    bytes[SA_BUF_KV_MASK] = rows * (size_t)d.words * 4;
+    bytes[SA_BUF_Q_MEAN] = rows * (size_t)p->d * 4;
+    bytes[SA_BUF_K_MEAN] = (size_t)d.BH * d.n_kb * p->d * 4;
+    bytes[SA_BUF_V_MEAN] = (size_t)d.BH * d.n_kb * p->d * 4;
+    bytes[SA_BUF_ROW_STATS] = rows * 2 * 4;
+    bytes[SA_BUF_COST] = rows * 4;
+    bytes[SA_BUF_WORK_ORDER] = rows * 4;
+    bytes[SA_BUF_SCHED] = (size_t)SA_SCHED_INTS * 4;
+    return SA_OK;
+}
+
+sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, const void *v,
+                            const sa_route *r, void *stream) {
+    sa_status s = check_params(p, true);
+    if (s != SA_OK) return s;
+    if ((s = check_ptr(q, "q")) || (s = check_ptr(k, "k")) || (s = check_ptr(v, "v")) ||
+        (s = check_ptr(r, "route")))
+        return s;
+    if ((s = check_ptr(r->kv_count, "route.kv_count")) || (s = check_ptr(r->kv_idx, "route.kv_idx")) ||
+        (s = check_ptr(r->kv_mask, "route.kv_mask")) || (s = check_ptr(r->q_mean, "route.q_mean")) ||
+        (s = check_ptr(r->k_mean, "route.k_mean")) || (s = check_ptr(r->v_mean, "route.v_mean")) ||
+        (s = check_ptr(r->row_stats, "route.row_stats")) || (s = check_ptr(r->cost, "route.cost")) ||
+        (s = check_ptr(r->work_order, "route.work_order")) || (s = check_ptr(r->sched, "route.sched")))
+        return s;
+    if (r->kv_idx_cap < min_cap(p))
+        return fail(SA_ERR_CAPACITY, "route.kv_idx_cap %d < required %d", r->kv_idx_cap, min_cap(p));
+    const Dims d = dims_of(p);
+    hipStream_t st = (hipStream_t)stream;
+
+    sa::PoolArgs pa;
+    pa.N = p->N; pa.block_q = p->block_q; pa.block_k = p->block_k;
+    pa.n_qb = d.n_qb; pa.n_kb = d.n_kb;
+    pa.q_mean = r->q_mean; pa.k_mean = r->k_mean; pa.v_mean = r->v_mean;
+    hipError_t e = sa::launch_pool(p->dtype, p->d, q, k, v, pa, (int)d.BH, st);
+    if (e != hipSuccess) return hip_fail(e, "route: pool launch");
+
+    sa::SelectArgs sa_;
+    sa_.N = p->N; sa_.block_q = p->block_q; sa_.block_k = p->block_k;
+    sa_.n_qb = d.n_qb; sa_.n_kb = d.n_kb; sa_.mask_words = d.words; sa_.kv_idx_cap = r->kv_idx_cap;
+    sa_.exact_tile_rows = p->dtype == SA_BF16 ? 64 : 32;
+    sa_.tau_mode = p->tau_mode; sa_.max_keep = p->max_keep; sa_.min_keep = p->min_keep;
+    sa_.n_prefix = p->n_dense_prefix;
+    sa_.scale = p->scale > 0.f ? p->scale : (float)(1.0 / sqrt((double)p->d));
+    sa_.ln_tau = p->tau > 0.f ? (float)log((double)p->tau) : -INFINITY;
+    sa_.q_mean = r->q_mean; sa_.k_mean = r->k_mean;
+    sa_.kv_count = r->kv_count; sa_.kv_idx = r->kv_idx; sa_.cost = r->cost;
+    sa_.work_order = r->work_order; sa_.hist = r->sched; sa_.kv_mask = r->kv_mask;
+    sa_.row_stats = r->row_stats;
+    e = sa::launch_select(p->d, sa_, (int)d.BH, st);
+    if (e != hipSuccess) return hip_fail(e, "route: select launch");
+    return SA_OK;
+}
+
+static sa_status run_flash(const sa_params *p, const void *q, const void *k, const void *v,
+                           const sa_route *r, void *o, float *lse, void *stream, const char *who) {
+    const Dims d = dims_of(p);
+    sa::FlashArgs fa;
+    memset(&fa, 0, sizeof fa);
+    fa.N = p->N; fa.block_q = p->block_q; fa.block_k = p->block_k;
+    fa.n_qb = d.n_qb; fa.n_kb = d.n_kb; fa.mask_words = d.words;
+    const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->d);
+    fa.scale_log2 = (float)(scale * 1.4426950408889634);
+    fa.lse = lse;
+    if (r) {
+        fa.kv_idx_cap = r->kv_idx_cap;
+        fa.residual = (p->flags & SA_FLAG_NO_RESIDUAL) ? 0 : 1;
+        fa.kv_count = r->kv_count; fa.kv_idx = r->kv_idx; fa.work_order = r->work_order;
+        fa.kv_mask = r->kv_mask; fa.k_mean = r->k_mean; fa.v_mean = r->v_mean;
+    }
+    hipError_t e = sa::launch_flash(p->dtype, p->d, p->block_q, q, k, v, o, fa, (int)d.BH,
+                                    (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, who);
+    return SA_OK;
+}
+
+sa_status sparse_attn_forward(const sa_params *p, const void *q, const void *k, const void *v,
+                              const sa_route *r, void *o, float *lse, void *stream) {
+    sa_status s = check_params(p, true);
+    if (s != SA_OK) return s;
+    if ((s = check_ptr(q, "q")) || (s = check_ptr(k, "k")) || (s = check_ptr(v, "v")) ||
+        (s = check_ptr(o, "o")) || (s = check_ptr(r, "route")))
+        return s;
+    if ((s = check_ptr(r->kv_count, "route.kv_count")) || (s = check_ptr(r->kv_idx, "route.kv_idx")) ||
+        (s = check_ptr(r->kv_mask, "route.kv_mask")) ||
+        (s = check_ptr(r->k_mean, "route.k_mean")) || (s = check_ptr(r->v_mean, "route.v_mean")) ||
+        (s = check_ptr(r->work_order, "route.work_order")))
+        return s;
+    if (r->kv_idx_cap < min_cap(p))
+        return fail(SA_ERR_CAPACITY, "route.kv_idx_cap %d < required %d", r->kv_idx_cap, min_cap(p));
+    return run_flash(p, q, k, v, r, o, lse, stream, "forward: launch");
+}
+
+sa_status sparse_attn_dense_ref_gpu(const sa_params *p, const void *q, const void *k, const void *v,
+                                    void *o, float *lse, void *stream) {
+    sa_status s = check_params(p, false);
+    if (s != SA_OK) return s;
+    if ((s = check_ptr(q, "q")) || (s = check_ptr(k, "k")) || (s = check_ptr(v, "v")) ||
+        (s = check_ptr(o, "o")))
+        return s;
+    return run_flash(p, q, k, v, nullptr, o, lse, stream, "dense: launch");
+}
+
+const char *sparse_attn_status_string(sa_status s) {
+    switch (s) {
+        case SA_OK: return "ok";
+        case SA_ERR_INVALID_ARG: return "invalid argument";
+        case SA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case SA_ERR_CAPACITY: return "kv_idx capacity too small";
+        case SA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *sparse_attn_last_error(void) { return g_err; }
+
+}  // extern "C"

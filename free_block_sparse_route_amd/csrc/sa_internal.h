@@ -1,0 +1,50 @@
+// Internal launch interfaces between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __bf16 bf16;
+
+constexpr size_t kSelectLdsBudget = 64 * 1024;   // proxy rows of one select workgroup
+constexpr int kMaxKeyBlocks = 16384 - 16;       // n_kb limit implied by that budget at G = 1
+
+struct PoolArgs {
+    int N, block_q, block_k, n_qb, n_kb;
+    float *q_mean, *k_mean, *v_mean;
+};
+
+struct SelectArgs {
+    int N, block_q, block_k, n_qb, n_kb, mask_words, kv_idx_cap;
+    int exact_tile_rows;                 // key rows per exact attention tile (cost model)
+    int tau_mode, max_keep, min_keep, n_prefix;
+    float scale, ln_tau;                 // ln_tau = -inf when tau == 0
+    const float *q_mean, *k_mean;
+    int32_t *kv_count, *kv_idx, *cost, *work_order, *hist;
+    uint32_t *kv_mask;
+    float *row_stats;
+};
+
+struct FlashArgs {
+    int N, block_q, block_k, n_qb, n_kb, mask_words, kv_idx_cap;
+    float scale_log2;                    // logit scale times log2(e)
+    int residual;                        // fold dropped blocks (route present)
+    const int32_t *kv_count, *kv_idx, *work_order;
+    const uint32_t *kv_mask;
+    const float *k_mean, *v_mean;        // fp32 block means [B,H,n_kb,d]
+    float *lse;                          // nullable
+};
+
+hipError_t launch_pool(int dtype, int D, const void *q, const void *k, const void *v,
+                       const PoolArgs &a, int BH, hipStream_t st);
+hipError_t launch_select(int D, const SelectArgs &a, int BH, hipStream_t st);
+int select_group(int n_kb, int D, int n_qb);
+size_t select_lds_bytes(int G, int n_kb, int D);
+
+// Sparse forward when a.kv_idx != nullptr, dense otherwise.
+hipError_t launch_flash(int dtype, int D, int BQ, const void *q, const void *k, const void *v,
+                        void *o, const FlashArgs &a, int BH, hipStream_t st);
+
+}  // namespace sa

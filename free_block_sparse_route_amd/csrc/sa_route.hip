@@ -1,0 +1,306 @@
+// Routing kernels: block pooling, proxy scoring and block selection, and the
+// cost-ordered work list for the attention kernel.
+//
+// pool    one workgroup per (b, h, block, tensor) reduces a block of <= 128
+//         tokens to its fp32 mean with coalesced 16-byte loads (HBM-bound; the
+//         inputs are read exactly once).  Block centroids: PARK page,
+//         section 4.1.
+// select  one workgroup per (b, h, group of G query blocks): the G proxy rows
+//         s_IJ = scale * qbar_I . kbar_J are computed in fp32 into LDS (never
+//         written to memory, Sol-Attn abstract: no materialised proxy map),
+//         then one wave per row takes the row max / log-sum-exp, compares with
+//         tau, applies the top-k cap or floor by an exact k-th-largest search
+//         over order-preserving integer keys, forces the dense prefix and
+//         compacts the kept blocks into an ascending index list and bit mask.
+// sched   counting sort of work items by cost (tiles the attention kernel
+//         will visit), most expensive first, so that the hardware dispatcher's
+//         in-order issue behaves as longest-processing-time-first scheduling.
+#include "sa_device.h"
+#include "sa_internal.h"
+
+namespace sa {
+
+constexpr int kPoolThreads = 256;
+constexpr int kSelectThreads = 256;
+constexpr int kHistBins = SA_SCHED_INTS / 2;
+
+// --------------------------------------------------------------------- pool
+template <typename T, int D>
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(const T *__restrict__ q,
+                                                            const T *__restrict__ k,
+                                                            const T *__restrict__ v,
+                                                            PoolArgs a) {
+    const int which = blockIdx.z;            // 0 = q, 1 = k, 2 = v
+    const int bh = blockIdx.y;
+    const int J = blockIdx.x;
+    const int bs = which == 0 ? a.block_q : a.block_k;
+    const int nb = which == 0 ? a.n_qb : a.n_kb;
+    if (J >= nb) return;
+    const T *X = (which == 0 ? q : which == 1 ? k : v) + (size_t)bh * a.N * D;
+    const int r0 = J * bs;
+    const int cnt = min(bs, a.N - r0);
+
+    constexpr int CH = D / 8;                 // 8-element chunks per row
+    constexpr int RG = kPoolThreads / CH;     // row groups
+    const int c = threadIdx.x % CH;
+    const int g = threadIdx.x / CH;
+
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int it = 0; it < 128 / RG; ++it) {
+        const int r = g + it * RG;
+        if (r < cnt) {
+            float x[8];
+            Ld8<T>::load_f32(X + (size_t)(r0 + r) * D + c * 8, x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += x[i];
+        }
+    }
+    __shared__ float part[RG * D];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[g * D + c * 8 + i] = acc[i];
+    __syncthreads();
+    if (threadIdx.x < D) {
+        const int col = threadIdx.x;
+        float s = 0.f;
+        for (int gg = 0; gg < RG; ++gg) s += part[gg * D + col];
+        const float m = s / (float)cnt;
+        float *dst = which == 0 ? a.q_mean : which == 1 ? a.k_mean : a.v_mean;
+        dst[((size_t)bh * nb + J) * D + col] = m;
+    }
+}
+
+// --------------------------------------------------------------------- select
+__device__ __forceinline__ uint64_t lanes_below() {
+    const int l = lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Number of row entries whose key is >= kmin (wave-uniform result).
+__device__ __forceinline__ int count_ge(const float *S, int n, uint32_t kmin) {
+    int cnt = 0;
+    for (int base = 0; base < n; base += kWave) {
+        const int J = base + lane_id();
+        const bool p = J < n && orderable(S[J]) >= kmin;
+        cnt += __popcll(__ballot(p));
+    }
+    return cnt;
+}
+
+__device__ void select_row(const float *S, int bh, int I, const SelectArgs &a) {
+    const int lane = lane_id();
+    const int n = a.n_kb;
+    float m = -INFINITY;
+    for (int J = lane; J < n; J += kWave) m = fmaxf(m, S[J]);
+    m = wave_max(m);
+    float z = 0.f;
+    for (int J = lane; J < n; J += kWave) z += expf(S[J] - m);
+    z = wave_sum(z);
+    const float lse = m + logf(z);
+    const float thr = (a.tau_mode == SA_TAU_ABSOLUTE ? lse : m) + a.ln_tau;
+
+    int n_c = 0;
+    for (int base = 0; base < n; base += kWave) {
+        const int J = base + lane;
+        n_c += __popcll(__ballot(J < n && S[J] >= thr));
+    }
+    int ksel = 0;
+    if (a.max_keep > 0 && n_c > a.max_keep) ksel = a.max_keep;
+    else if (n_c < a.min_keep) ksel = min(a.min_keep, n);
+
+    // ksel-th largest key T, built bit by bit from the top: the largest T with
+    // #{key >= T} >= ksel.  Equal keys beyond the budget are resolved by J.
+    uint32_t T = 0;
+    int take_eq = 0;
+    if (ksel > 0) {
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = T | (1u << bit);
+            if (count_ge(S, n, cand) >= ksel) T = cand;
+        }
+        const int n_gt = (T == 0xffffffffu) ? 0 : count_ge(S, n, T + 1);
+        take_eq = ksel - n_gt;
+    }
+
+    const size_t row = (size_t)bh * a.n_qb + I;
+    int32_t *idx = a.kv_idx + row * a.kv_idx_cap;
+    uint32_t *mask = a.kv_mask + row * a.mask_words;
+    const bool dense_row = (int64_t)I * a.block_q < a.n_prefix;
+    const int last_cnt = a.N - (n - 1) * a.block_k;
+    int kept = 0, eq_seen = 0, tiles = 0;
+    for (int base = 0; base < n; base += kWave) {
+        const int J = base + lane;
+        const bool valid = J < n;
+        const float sv = valid ? S[J] : 0.f;
+        bool keep;
+        if (ksel > 0) {
+            const uint32_t key = orderable(sv);
+            const bool eq = valid && key == T;
+            const uint64_t be = __ballot(eq);
+            const int rank = eq_seen + __popcll(be & lanes_below());
+            eq_seen += __popcll(be);
+            keep = valid && (key > T || (eq && rank < take_eq));
+        } else {
+            keep = valid && sv >= thr;
+        }
+        keep = valid && (keep || dense_row || (int64_t)J * a.block_k < a.n_prefix);
+        const uint64_t bk = __ballot(keep);
+        if (keep) idx[kept + __popcll(bk & lanes_below())] = J;
+        kept += __popcll(bk);
+        const int w = base / 32;
+        if (lane == 0 && w < a.mask_words) mask[w] = (uint32_t)bk;
+        if (lane == 1 && w + 1 < a.mask_words) mask[w + 1] = (uint32_t)(bk >> 32);
+        // cost: exact tiles of kept blocks, plus one residual tile per 32 pooled
+        // blocks (one mask word) that holds a dropped block
+        const int nj = (J == n - 1) ? last_cnt : a.block_k;
+        tiles += keep ? (nj + a.exact_tile_rows - 1) / a.exact_tile_rows : 0;
+        const uint64_t bd = __ballot(valid && !keep);
+        if (lane == 0) tiles += ((uint32_t)bd != 0) + ((uint32_t)(bd >> 32) != 0);
+    }
+    tiles = (int)wave_sum((float)tiles);
+    if (lane == 0) {
+        a.kv_count[row] = kept;
+        a.row_stats[row * 2 + 0] = m;
+        a.row_stats[row * 2 + 1] = lse;
+        a.cost[row] = tiles;
+        atomicAdd(&a.hist[min(tiles, kHistBins - 1)], 1);
+    }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    const int bh = blockIdx.y;
+    const int I0 = blockIdx.x * G;
+    const int g_cnt = min(G, a.n_qb - I0);
+    const int n = a.n_kb;
+    float *S = smem;                                      // [G][n]
+    float *QB = smem + ((G * n + 3) & ~3);                // [G][D]
+    for (int i = threadIdx.x; i < G * D; i += kSelectThreads)
+        QB[i] = (i / D) < g_cnt ? a.q_mean[((size_t)bh * a.n_qb + I0) * D + i] : 0.f;
+    __syncthreads();
+    const float *kb = a.k_mean + (size_t)bh * n * D;
+    for (int J = threadIdx.x; J < n; J += kSelectThreads) {
+        float acc[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g] = 0.f;
+        const float *kr = kb + (size_t)J * D;
+#pragma unroll 4
+        for (int c = 0; c < D; c += 4) {
+            const f32x4 kv = *reinterpret_cast<const f32x4 *>(kr + c);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const f32x4 qv = *reinterpret_cast<const f32x4 *>(QB + g * D + c);
+                acc[g] = fmaf(qv[0], kv[0], acc[g]);
+                acc[g] = fmaf(qv[1], kv[1], acc[g]);
+                acc[g] = fmaf(qv[2], kv[2], acc[g]);
+                acc[g] = fmaf(qv[3], kv[3], acc[g]);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) S[g * n + J] = acc[g] * a.scale;
+    }
+    __syncthreads();
+    const int wave = threadIdx.x / kWave;
+    for (int g = wave; g < g_cnt; g += kSelectThreads / kWave) select_row(S + g * n, bh, I0 + g, a);
+}
+
+// --------------------------------------------------------------------- sched
+__global__ void sched_zero_kernel(int32_t *hist) {
+    for (int i = threadIdx.x; i < SA_SCHED_INTS; i += blockDim.x) hist[i] = 0;
+}
+
+// offsets[b] = number of items with a larger cost bin (descending order).
+__global__ __launch_bounds__(256) void sched_scan_kernel(int32_t *sched) {
+    const int32_t *hist = sched;
+    int32_t *offs = sched + kHistBins;
+    constexpr int PER = kHistBins / 256;
+    __shared__ int32_t part[256];
+    const int t = threadIdx.x;
+    // thread t owns bins [kHistBins - (t+1)*PER, kHistBins - t*PER), walked downwards
+    int s = 0;
+    for (int i = 0; i < PER; ++i) s += hist[kHistBins - 1 - (t * PER + i)];
+    part[t] = s;
+    __syncthreads();
+    int before = 0;
+    for (int u = 0; u < t; ++u) before += part[u];
+    for (int i = 0; i < PER; ++i) {
+        const int b = kHistBins - 1 - (t * PER + i);
+        offs[b] = before;
+        before += hist[b];
+    }
+}
+
+__global__ void sched_scatter_kernel(const int32_t *cost, int32_t *sched, int32_t *work_order,
+                                     int n_items) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_items) return;
+    const int b = min(cost[i], kHistBins - 1);
+    const int pos = atomicAdd(&sched[kHistBins + b], 1);
+    work_order[pos] = i;
+}
+
+// --------------------------------------------------------------------- launch
+template <typename T, int D>
+static hipError_t launch_pool_t(const void *q, const void *k, const void *v, const PoolArgs &a,
+                                int BH, hipStream_t st) {
+    dim3 grid(max(a.n_qb, a.n_kb), BH, 3);
+    hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(kPoolThreads), 0, st,
+                       (const T *)q, (const T *)k, (const T *)v, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool(int dtype, int D, const void *q, const void *k, const void *v,
+                       const PoolArgs &a, int BH, hipStream_t st) {
+    if (dtype == SA_BF16) return D == 64 ? launch_pool_t<bf16, 64>(q, k, v, a, BH, st)
+                                         : launch_pool_t<bf16, 128>(q, k, v, a, BH, st);
+    return D == 64 ? launch_pool_t<float, 64>(q, k, v, a, BH, st)
+                   : launch_pool_t<float, 128>(q, k, v, a, BH, st);
+}
+
+int select_group(int n_kb, int D, int n_qb) {
+    int G = 8;
+    while (G > 1 && ((size_t)G * n_kb + 4 + (size_t)G * D) * 4 > kSelectLdsBudget) G /= 2;
+    while (G > 1 && G / 2 >= n_qb) G /= 2;
+    return G;
+}
+
+size_t select_lds_bytes(int G, int n_kb, int D) {
+    return (((size_t)G * n_kb + 3) / 4 * 4 + (size_t)G * D) * sizeof(float);
+}
+
+template <int D, int G>
+static hipError_t launch_select_t(const SelectArgs &a, int BH, hipStream_t st) {
+    const size_t lds = select_lds_bytes(G, a.n_kb, D);
+    dim3 grid((a.n_qb + G - 1) / G, BH);
+    hipLaunchKernelGGL((select_kernel<D, G>), grid, dim3(kSelectThreads), lds, st, a);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_select_d(const SelectArgs &a, int G, int BH, hipStream_t st) {
+    switch (G) {
+        case 8: return launch_select_t<D, 8>(a, BH, st);
+        case 4: return launch_select_t<D, 4>(a, BH, st);
+        case 2: return launch_select_t<D, 2>(a, BH, st);
+        default: return launch_select_t<D, 1>(a, BH, st);
+    }
+}
+
+hipError_t launch_select(int D, const SelectArgs &a, int BH, hipStream_t st) {
+    const int G = select_group(a.n_kb, D, a.n_qb);
+    hipError_t e = hipSuccess;
+    hipLaunchKernelGGL(sched_zero_kernel, dim3(1), dim3(256), 0, st, a.hist);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = D == 64 ? launch_select_d<64>(a, G, BH, st) : launch_select_d<128>(a, G, BH, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(256), 0, st, a.hist);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int n_items = BH * a.n_qb;
+    hipLaunchKernelGGL(sched_scatter_kernel, dim3((n_items + 255) / 256), dim3(256), 0, st,
+                       (const int32_t *)a.cost, a.hist, a.work_order, n_items);
+    return hipGetLastError();
+}
+
+}  // namespace sa

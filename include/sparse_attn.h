@@ -1,0 +1,172 @@
+/*
+ * sparse_attn.h: C ABI of a block-sparse attention library for AMD Instinct
+ * MI355X (gfx950) with block routing and a dropped-block residual.
+ *
+ * The operation (per batch entry b and head h, tokens [N, d]):
+ *
+ *  1. Routing.  Mean-pool queries over query blocks of block_q tokens and keys
+ *     and values over key blocks of block_k tokens (the last block of each may
+ *     be short; its mean is over its actual tokens).  Score every key block J
+ *     for every query block I with the block proxy s_IJ = scale * qbar_I . kbar_J
+ *     and keep J when the proxy clears tau (Sol-Attn abstract: blocks are
+ *     selected by comparing block proxy scores against a threshold; block
+ *     centroids as in the PARK page, section 4.1).  The compared quantity r_IJ
+ *     is either the proxy probability relative to the row's largest one,
+ *     exp(s_IJ - max_J' s_IJ') (SA_TAU_RELATIVE), or the proxy probability
+ *     softmax_J(s_I.)_J itself (SA_TAU_ABSOLUTE).  A top-k budget caps the
+ *     kept count at max_keep (rank by r descending, ties by J ascending); if
+ *     fewer than min_keep clear tau, the min_keep best-ranked blocks are kept.
+ *     Key blocks that start before n_dense_prefix tokens are always kept, and
+ *     a query block that starts before n_dense_prefix keeps every key block.
+ *     The proxy map is never written to memory; only its per-row maximum and
+ *     log-sum-exp are.
+ *
+ *  2. Exact pass.  One online-softmax pass over the kept key blocks:
+ *     logits scale * q_i . k_t for every token t of a kept block (Sol-Attn
+ *     abstract: routing, sparse computation and correction in one
+ *     online-softmax pass).
+ *
+ *  3. Residual.  Each dropped block J enters the same running max and
+ *     normaliser as a single logit scale * q_i . kbar_J + ln n_J carrying the
+ *     value vbar_J, i.e. n_J tokens with the block-mean key and value (Sol-Attn
+ *     abstract: the proxy of unselected blocks approximates their
+ *     contribution; the block-mean key gives a lower bound on the block's
+ *     log-mass, PARK page, appendix D.2).
+ *
+ *     o_i = (sum_t e^{a_it - M} v_t + sum_J e^{b_iJ - M} vbar_J) / Z,
+ *     lse_i = M + ln Z.
+ *
+ * Conventions shared by every entry point
+ *  - Q, K, V, O are [B, H, N, d] contiguous with d fastest, in the dtype of
+ *    sa_params.dtype (bf16 or fp32).  Products run on bf16 matrix cores with
+ *    fp32 accumulation; fp32 inputs are rounded to bf16 for the products.
+ *    Routing (pooling, proxy, threshold) is fp32 throughout.
+ *  - Every tensor pointer is a DEVICE pointer (hipMalloc or equivalent) of the
+ *    current HIP device.  The caller owns and frees all memory; the library
+ *    allocates nothing, frees nothing and never synchronises.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued asynchronously on it; results are ready once the caller
+ *    synchronises that stream.
+ *  - Errors: arguments are validated on the host before anything is enqueued;
+ *    a negative sa_status is returned and nothing runs.  A failed launch
+ *    returns SA_ERR_HIP.  sparse_attn_last_error() gives a message for the
+ *    last failure on the calling thread.  No exception crosses the ABI.
+ *  - Deterministic: identical inputs give bitwise identical outputs.
+ *  - Thread-safe; concurrent calls on distinct streams and distinct output
+ *    buffers do not interact.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sa_status {
+    SA_OK = 0,
+    SA_ERR_INVALID_ARG = -1,   /* a parameter or pointer is invalid                 */
+    SA_ERR_UNSUPPORTED = -2,   /* valid but not implemented (d, block size, n_kb)    */
+    SA_ERR_CAPACITY = -3,      /* kv_idx_cap smaller than sparse_attn_kv_idx_cap()   */
+    SA_ERR_HIP = -4            /* the HIP runtime reported an error                  */
+} sa_status;
+
+typedef enum sa_dtype { SA_BF16 = 0, SA_F32 = 1 } sa_dtype;
+
+typedef enum sa_tau_mode {
+    SA_TAU_RELATIVE = 0,       /* r = exp(s_IJ - max_J' s_IJ')                       */
+    SA_TAU_ABSOLUTE = 1        /* r = softmax_J(s_I.)_J                              */
+} sa_tau_mode;
+
+enum {
+    SA_FLAG_NO_RESIDUAL = 1    /* forward: dropped blocks contribute nothing         */
+};
+
+/* Problem statement: B, H, N, d, block sizes, tau and budget. */
+typedef struct sa_params {
+    int32_t B, H, N, d;        /* N >= 1; d in {64, 128}                            */
+    int32_t block_q, block_k;  /* each in {64, 128}; N need not be a multiple        */
+    float   tau;               /* >= 0; 0 keeps every block; > 1 keeps only floor    */
+    int32_t tau_mode;          /* sa_tau_mode                                        */
+    int32_t max_keep;          /* top-k cap on kept blocks per query block, 0 = none */
+    int32_t min_keep;          /* floor when fewer clear tau (clamped to n_kb)       */
+    int32_t n_dense_prefix;    /* leading always-attended tokens, 0..N               */
+    float   scale;             /* logit scale; 0 => 1/sqrt(d)                        */
+    int32_t dtype;             /* sa_dtype of Q, K, V, O                             */
+    int32_t flags;             /* SA_FLAG_*                                          */
+} sa_params;
+
+/* Buffers written by sparse_attn_route and read by sparse_attn_forward.  With
+ * n_qb = ceil(N / block_q), n_kb = ceil(N / block_k), words = ceil(n_kb / 32),
+ * W = B * H * n_qb.  All are device memory,
+ * sized by sparse_attn_route_sizes() (entry i of its output is the byte size of
+ * buffer i in the order below).  A route may serve several forward calls (mask
+ * reuse across calls): forward takes the keep mask, kept lists and block means
+ * from the route and reads q, k, v anew. */
+enum {
+    SA_BUF_KV_COUNT = 0,  /* int32 [B,H,n_qb]            kept key blocks per query block   */
+    SA_BUF_KV_IDX,        /* int32 [B,H,n_qb,kv_idx_cap] kept key-block indices, ascending;
+                                                         entries past kv_count are unspecified */
+    SA_BUF_KV_MASK,       /* uint32 [B,H,n_qb,words]     bit J%32 of word J/32: J kept     */
+    SA_BUF_Q_MEAN,        /* fp32 [B,H,n_qb,d]           query block means                  */
+    SA_BUF_K_MEAN,        /* fp32 [B,H,n_kb,d]           key block means                    */
+    SA_BUF_V_MEAN,        /* fp32 [B,H,n_kb,d]           value block means                  */
+    SA_BUF_ROW_STATS,     /* fp32 [B,H,n_qb,2]           max_J s_IJ and log-sum-exp_J s_IJ  */
+    SA_BUF_COST,          /* int32 [B,H,n_qb]            key/value tiles the forward visits */
+    SA_BUF_WORK_ORDER,    /* int32 [W]                   work items, most expensive first   */
+    SA_BUF_SCHED,         /* int32 [SA_SCHED_INTS]       schedule scratch                   */
+    SA_ROUTE_NBUF
+};
+#define SA_SCHED_INTS 8192
+
+typedef struct sa_route {
+    int32_t  *kv_count;
+    int32_t  *kv_idx;
+    uint32_t *kv_mask;
+    float    *q_mean;
+    float    *k_mean;
+    float    *v_mean;
+    float    *row_stats;
+    int32_t  *cost;
+    int32_t  *work_order;
+    int32_t  *sched;
+    int32_t   kv_idx_cap;     /* row length of kv_idx, >= sparse_attn_kv_idx_cap(p) */
+} sa_route;
+
+/* Smallest valid kv_idx_cap for p: n_kb when there is no cap or a dense prefix
+ * row exists, else min(n_kb, max(max_keep, min_keep) + prefix key blocks).
+ * Returns a negative sa_status when p is invalid.  Host only; no HIP calls. */
+int32_t sparse_attn_kv_idx_cap(const sa_params *p);
+
+/* Byte sizes of the SA_ROUTE_NBUF route buffers for p and kv_idx_cap, written
+ * to bytes[0..SA_ROUTE_NBUF-1].  Host only; no HIP calls. */
+sa_status sparse_attn_route_sizes(const sa_params *p, int32_t kv_idx_cap, size_t *bytes);
+
+/* Step 1 (routing).  Reads q, k, v once; writes every buffer of *r.  Nothing
+ * of size n_qb x n_kb is written except the kv_idx lists and the bit mask. */
+sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, const void *v,
+                            const sa_route *r, void *stream);
+
+/* Steps 2 and 3.  Writes o [B,H,N,d] (dtype of p) and, when lse is not NULL,
+ * lse [B,H,N] fp32 (natural log).  r must come from sparse_attn_route with
+ * the same p (tau and budget fields may not differ) on the same k and v. */
+sa_status sparse_attn_forward(const sa_params *p, const void *q, const void *k, const void *v,
+                              const sa_route *r, void *o, float *lse, void *stream);
+
+/* Dense softmax attention with the same kernels and conventions (every key
+ * block kept, no residual); tau, budget and prefix fields are ignored. */
+sa_status sparse_attn_dense_ref_gpu(const sa_params *p, const void *q, const void *k,
+                                    const void *v, void *o, float *lse, void *stream);
+
+/* Static description of a status code. */
+const char *sparse_attn_status_string(sa_status s);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char *sparse_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSE_ATTN_H */

@@ -181,10 +181,11 @@ def _kept_tokens(mask_row: np.ndarray, bk: int, N: int) -> np.ndarray:
 
 
 def forward_ref_with_mask(q, k, v, mask: np.ndarray, p: RouteParams, rows=None,
-                          return_weights: bool = False):
+                          return_weights: bool = False, residual: bool = True):
     """Sparse attention with residual for one head, under a given keep mask [n_qb, n_kb].
 
     rows: optional iterable of query-block indices to evaluate (others left NaN).
+    residual=False drops the dropped blocks entirely (attention over kept tokens only).
     Returns (O [N, d], LSE [N]) and, with return_weights, a list per query block of
     (token_idx, w_tokens [m_I, n_t], dropped_blocks, w_blocks [m_I, n_d]).
     """
@@ -204,7 +205,7 @@ def forward_ref_with_mask(q, k, v, mask: np.ndarray, p: RouteParams, rows=None,
         i0, i1 = I * p.block_q, min((I + 1) * p.block_q, N)
         qi = q[i0:i1]
         tok = _kept_tokens(mask[I], p.block_k, N)
-        dropped = np.flatnonzero(~mask[I])
+        dropped = np.flatnonzero(~mask[I]) if residual else np.zeros(0, dtype=np.int64)
         a = sig * (qi @ k[tok].T)                                    # exact logits
         b = sig * (qi @ kbar[dropped].T) + np.log(n_j[dropped])[None, :]   # residual logits
         M = np.full(i1 - i0, -np.inf)

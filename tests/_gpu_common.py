@@ -1,0 +1,109 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI binding
+and compare it with the CPU oracle on the same inputs."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import sparse_attn_ref as R
+from workloads import synth as S
+
+REL_FRO = 1e-2       # output tolerance at bf16 inputs: relative Frobenius error
+MAX_ABS = 3e-2       # and max-abs error
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def sa():
+    import free_block_sparse_route_amd as m
+    return m
+
+
+def cfg_for(w: S.Workload, tau=None, mode=R.RELATIVE, max_keep=None, min_keep=1, prefix=None, no_residual=False):
+    m = sa()
+    return m.Config(block_q=w.block_q, block_k=w.block_k, tau=w.tau if tau is None else tau, tau_mode=mode,
+                    max_keep=w.max_keep if max_keep is None else max_keep, min_keep=min_keep,
+                    n_dense_prefix=w.n_text if prefix is None else prefix, no_residual=no_residual)
+
+
+def oracle_params(cfg) -> R.RouteParams:
+    return R.RouteParams(cfg.block_q, cfg.block_k, float(np.float32(cfg.tau)), cfg.tau_mode, cfg.max_keep,
+                         cfg.min_keep, cfg.n_dense_prefix, cfg.scale)
+
+
+def run_gpu(Q, K, V, cfg):
+    m = sa()
+    rt = m.route(Q, K, V, cfg)
+    O, L = m.forward(Q, K, V, rt, cfg, lse=True)
+    torch.cuda.synchronize()
+    return rt, O, L
+
+
+def head_np(T: torch.Tensor, b: int, h: int) -> np.ndarray:
+    return T[b, h].double().cpu().numpy()
+
+
+def check_lists(rt) -> np.ndarray:
+    """kv_count, kv_idx and the bit mask agree; returns the mask as numpy bool."""
+    mask = rt.mask().cpu().numpy()
+    cnt = rt.kv_count.cpu().numpy()
+    idx = rt.kv_idx.cpu().numpy()
+    assert np.array_equal(cnt, mask.sum(axis=-1)), "kv_count != popcount(mask)"
+    B, H, n_qb, n_kb = mask.shape
+    for b in range(B):
+        for h in range(H):
+            for I in range(n_qb):
+                c = cnt[b, h, I]
+                assert np.array_equal(idx[b, h, I, :c], np.flatnonzero(mask[b, h, I])), (b, h, I)
+    # bits past n_kb in the last word are zero
+    words = rt.kv_mask.cpu().numpy().view(np.uint32)
+    tail = rt.n_kb % 32
+    if tail:
+        assert (words[..., -1] >> np.uint32(tail) == 0).all()
+    return mask
+
+
+def check_mask_head(gpu_mask: np.ndarray, q: np.ndarray, k: np.ndarray, cfg, row_stats=None):
+    """Bit-exact outside the rounding band; returns (oracle route, n_diff, n_exempt)."""
+    p = oracle_params(cfg)
+    rt = R.route_ref(q, k, p)
+    diff = gpu_mask != rt.mask
+    bad = diff & ~rt.exempt
+    assert not bad.any(), f"{int(bad.sum())} mask bits differ outside the 1e-4 band, first {np.argwhere(bad)[:5]}"
+    if row_stats is not None:
+        np.testing.assert_allclose(row_stats[:, 0], rt.row_max, rtol=1e-5, atol=1e-4)
+        np.testing.assert_allclose(row_stats[:, 1], rt.row_lse, rtol=1e-5, atol=1e-4)
+    return rt, int(diff.sum()), int(rt.exempt.sum())
+
+
+def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def check_out_head(O_gpu: np.ndarray, L_gpu: np.ndarray, q, k, v, mask, cfg, blocks=None, residual=True):
+    """O within REL_FRO / MAX_ABS of the oracle under the given mask (on the listed query blocks)."""
+    p = oracle_params(cfg)
+    O_ref, L_ref = R.forward_ref_with_mask(q, k, v, mask, p, rows=blocks, residual=residual)
+    sel = ~np.isnan(L_ref)
+    e_rel = rel_fro(O_gpu[sel], O_ref[sel])
+    e_abs = float(np.abs(O_gpu[sel] - O_ref[sel]).max())
+    assert e_rel <= REL_FRO and e_abs <= MAX_ABS, f"rel-Frobenius {e_rel:.3e}, max-abs {e_abs:.3e}"
+    if L_gpu is not None:
+        e_l = float(np.abs(L_gpu[sel] - L_ref[sel]).max())
+        assert e_l <= 2e-2, f"LSE max-abs {e_l:.3e}"
+    return e_rel, e_abs
+
+
+def sample_blocks(mask_h: np.ndarray, n_random: int, seed: int) -> list:
+    """Query blocks to evaluate in the oracle: first, tail, most and fewest kept, random."""
+    n_qb = mask_h.shape[0]
+    cnt = mask_h.sum(axis=1)
+    rng = np.random.default_rng(seed)
+    s = {0, n_qb - 1, int(cnt.argmax()), int(cnt.argmin())}
+    s |= set(rng.choice(n_qb, size=min(n_random, n_qb), replace=False).tolist())
+    return sorted(s)

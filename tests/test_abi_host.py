@@ -1,0 +1,126 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, agrees with a C compiler on struct layout, and rejects bad
+arguments on the host before anything is enqueued."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+sa = pytest.importorskip("free_block_sparse_route_amd")
+B = sa.binding
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_attn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) == 7, names
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "sparse_attn.h"\n'
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %d %d\\n\", sizeof(sa_params), sizeof(sa_route),"
+        " offsetof(sa_params, flags), offsetof(sa_route, kv_idx_cap), offsetof(sa_route, sched),"
+        " offsetof(sa_params, scale), SA_ROUTE_NBUF, SA_SCHED_INTS);return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    vals = [int(x) for x in out]
+    assert vals[0] == ctypes.sizeof(B.SaParams)
+    assert vals[1] == ctypes.sizeof(B.SaRoute)
+    assert vals[2] == B.SaParams.flags.offset
+    assert vals[3] == B.SaRoute.kv_idx_cap.offset
+    assert vals[4] == B.SaRoute.sched.offset
+    assert vals[5] == B.SaParams.scale.offset
+    assert vals[6] == len(B.BUFFERS)
+    assert vals[7] == B.SA_SCHED_INTS
+
+
+def params(**kw):
+    base = dict(B=1, H=2, N=1000, d=128, block_q=128, block_k=64, tau=0.01, tau_mode=0, max_keep=0, min_keep=1,
+                n_dense_prefix=0, scale=0.0, dtype=0, flags=0)
+    base.update(kw)
+    return B.SaParams(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), B.SA_ERR_INVALID_ARG), (dict(B=0), B.SA_ERR_INVALID_ARG), (dict(tau=-1.0), B.SA_ERR_INVALID_ARG),
+    (dict(tau=float("nan")), B.SA_ERR_INVALID_ARG), (dict(tau_mode=2), B.SA_ERR_INVALID_ARG),
+    (dict(max_keep=-1), B.SA_ERR_INVALID_ARG), (dict(n_dense_prefix=1001), B.SA_ERR_INVALID_ARG),
+    (dict(dtype=5), B.SA_ERR_INVALID_ARG), (dict(flags=8), B.SA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), B.SA_ERR_INVALID_ARG), (dict(d=96), B.SA_ERR_UNSUPPORTED),
+    (dict(block_q=32), B.SA_ERR_UNSUPPORTED), (dict(block_k=256), B.SA_ERR_UNSUPPORTED),
+    (dict(N=2_000_000, block_k=64), B.SA_ERR_UNSUPPORTED),
+])
+def test_invalid_params_rejected(kw, status):
+    p = params(**kw)
+    assert B.lib.sparse_attn_kv_idx_cap(ctypes.byref(p)) == status
+    arr = (ctypes.c_size_t * len(B.BUFFERS))()
+    assert B.lib.sparse_attn_route_sizes(ctypes.byref(p), 1 << 20, arr) == status
+    assert B.lib.sparse_attn_last_error().decode() != ""
+
+
+def test_kv_idx_cap_rules():
+    assert B.kv_idx_cap(params()) == 16                               # no cap: n_kb = ceil(1000/64)
+    assert B.kv_idx_cap(params(max_keep=4)) == 4
+    assert B.kv_idx_cap(params(max_keep=4, min_keep=9)) == 9
+    assert B.kv_idx_cap(params(max_keep=40)) == 16
+    assert B.kv_idx_cap(params(max_keep=4, n_dense_prefix=10)) == 16  # prefix row keeps everything
+
+
+def test_route_sizes_wan13b():
+    p = params(B=1, H=12, N=32760, d=128, block_q=128, block_k=128)
+    cap = B.kv_idx_cap(p)
+    s = dict(zip(B.BUFFERS, B.route_sizes(p, cap)))
+    assert cap == 256
+    assert s["kv_count"] == 12 * 256 * 4
+    assert s["kv_idx"] == 12 * 256 * 256 * 4
+    assert s["kv_mask"] == 12 * 256 * 8 * 4
+    assert s["k_mean"] == 12 * 256 * 128 * 4
+    assert s["sched"] == B.SA_SCHED_INTS * 4
+    with pytest.raises(B.SparseAttnError) as e:
+        B.route_sizes(p, cap - 1)
+    assert e.value.status == B.SA_ERR_CAPACITY
+
+
+def test_null_pointers_rejected_before_launch():
+    p = params()
+    r = B.SaRoute()
+    st = B.lib.sparse_attn_route(ctypes.byref(p), None, 1, 1, ctypes.byref(r), None)
+    assert st == B.SA_ERR_INVALID_ARG and "q is NULL" in B.last_error()
+    st = B.lib.sparse_attn_route(ctypes.byref(p), 1, 1, 1, ctypes.byref(r), None)
+    assert st == B.SA_ERR_INVALID_ARG and "route.kv_count" in B.last_error()
+    st = B.lib.sparse_attn_forward(ctypes.byref(p), 1, 1, 1, None, 1, None, None)
+    assert st == B.SA_ERR_INVALID_ARG and "route is NULL" in B.last_error()
+    st = B.lib.sparse_attn_dense_ref_gpu(ctypes.byref(p), 1, 1, 1, None, None, None)
+    assert st == B.SA_ERR_INVALID_ARG and "o is NULL" in B.last_error()
+    st = B.lib.sparse_attn_route(None, 1, 1, 1, ctypes.byref(r), None)
+    assert st == B.SA_ERR_INVALID_ARG
+
+
+def test_capacity_checked_before_launch():
+    p = params(max_keep=4)
+    r = B.SaRoute(*([1] * len(B.BUFFERS)), 3)
+    assert B.lib.sparse_attn_route(ctypes.byref(p), 1, 1, 1, ctypes.byref(r), None) == B.SA_ERR_CAPACITY
+    assert B.lib.sparse_attn_forward(ctypes.byref(p), 1, 1, 1, ctypes.byref(r), 1, None, None) == B.SA_ERR_CAPACITY
+
+
+def test_status_strings():
+    assert B.status_string(0) == "ok"
+    assert "capacity" in B.status_string(B.SA_ERR_CAPACITY)
+    assert B.status_string(-99) == "unknown status"

@@ -1,0 +1,218 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Masks: bit-exact except blocks whose compared quantity lies within 1e-4 of its
+cut (tau, or the budget's cut), which the oracle lists.  Outputs: relative
+Frobenius error <= 1e-2 and max-abs error <= 3e-2 against the oracle evaluated
+on the GPU's own mask (and on the oracle's mask when they agree).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sparse_attn_ref as R
+from workloads import synth as S
+
+from _gpu_common import (check_lists, check_mask_head, check_out_head, cfg_for, head_np, run_gpu, sa,
+                         sample_blocks, say)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def make(w, heads=None):
+    Q, K, V = S.make_qkv(w, heads=heads)
+    return Q, K, V, Q.cuda(), K.cuda(), V.cuda()
+
+
+def full_check(w, cfg, blocks_per_head=None, heads=None, label=""):
+    """Run route + forward on the whole workload, then check the listed heads against the oracle."""
+    say(f"[case] {label} {w.name} B{w.B} H{w.H} N{w.N} d{w.d} {w.block_q}x{w.block_k} {w.dtype} "
+        f"tau={cfg.tau} mode={cfg.tau_mode} cap={cfg.max_keep} floor={cfg.min_keep} prefix={cfg.n_dense_prefix}")
+    Qc, Kc, Vc, Q, K, V = make(w)
+    rt, O, L = run_gpu(Q, K, V, cfg)
+    mask = check_lists(rt)
+    stats = rt.row_stats.cpu().numpy()
+    Oc = O.float().cpu().numpy()
+    Lc = L.cpu().numpy()
+    assert np.isfinite(Oc).all() and np.isfinite(Lc).all()
+    heads = heads if heads is not None else [(b, h) for b in range(w.B) for h in range(w.H)]
+    tot_diff = tot_exempt = 0
+    for b, h in heads:
+        q, k, v = head_np(Qc, b, h), head_np(Kc, b, h), head_np(Vc, b, h)
+        ort, nd, ne = check_mask_head(mask[b, h], q, k, cfg, stats[b, h])
+        tot_diff += nd
+        tot_exempt += ne
+        blocks = None if blocks_per_head is None else sample_blocks(mask[b, h], blocks_per_head, 17 * h + b)
+        check_out_head(Oc[b, h], Lc[b, h], q, k, v, mask[b, h], cfg, blocks=blocks,
+                       residual=not cfg.no_residual)
+        if nd == 0 and blocks is not None:
+            pass  # same mask: the check above is also the check against the oracle's own mask
+        elif nd:
+            # the oracle's own mask differs only inside the band: outputs still agree
+            check_out_head(Oc[b, h], Lc[b, h], q, k, v, ort.mask, cfg, blocks=blocks,
+                           residual=not cfg.no_residual)
+    say(f"  kept {mask.mean():.4f}  band-exempt bits that differ {tot_diff} (of {tot_exempt} in the band)")
+    return rt, O, L, mask
+
+
+# ----------------------------------------------------------------------------- small cases
+SMALL = [
+    # name, grid, d, bq, bk, dtype, tau, mode, max_keep, min_keep, n_text, hilbert, B, H
+    ("r128", (4, 8, 32), 128, 128, 128, "bf16", 0.01, R.RELATIVE, 0, 1, 0, False, 1, 2),
+    ("ragged_cap", (5, 8, 25), 128, 128, 64, "bf16", 0.003, R.RELATIVE, 4, 1, 0, False, 1, 2),
+    ("abs", (4, 8, 32), 128, 128, 128, "bf16", 0.02, R.ABSOLUTE, 0, 1, 0, False, 1, 2),
+    ("abs_floor", (4, 8, 31), 128, 128, 64, "bf16", 0.5, R.ABSOLUTE, 0, 3, 0, False, 2, 1),
+    ("prefix_hilbert", (4, 8, 30), 128, 128, 128, "bf16", 0.01, R.RELATIVE, 0, 1, 100, True, 1, 2),
+    ("all_dropped", (3, 8, 27), 128, 128, 128, "bf16", 2.0, R.RELATIVE, 0, 0, 0, False, 1, 1),
+    ("f32_d64", (4, 8, 16), 64, 64, 64, "f32", 0.02, R.RELATIVE, 0, 1, 0, False, 1, 2),
+    ("f32_d128", (3, 7, 19), 128, 128, 64, "f32", 0.02, R.ABSOLUTE, 3, 1, 0, False, 1, 1),
+    ("d64_q128_k64", (3, 9, 21), 64, 128, 64, "bf16", 0.01, R.RELATIVE, 0, 1, 0, False, 1, 2),
+    ("d128_q64_k128", (3, 9, 21), 128, 64, 128, "bf16", 0.01, R.RELATIVE, 5, 1, 0, False, 1, 2),
+    ("multi_bh", (2, 6, 20), 128, 128, 64, "bf16", 0.02, R.RELATIVE, 0, 1, 0, False, 2, 3),
+    ("n1", (1, 1, 1), 128, 128, 128, "bf16", 0.01, R.RELATIVE, 0, 1, 0, False, 1, 1),
+    ("n63", (1, 7, 9), 64, 64, 64, "bf16", 0.05, R.RELATIVE, 0, 1, 0, False, 1, 1),
+    ("n130", (1, 10, 13), 128, 128, 64, "bf16", 0.05, R.ABSOLUTE, 0, 1, 0, False, 1, 1),
+    ("big_prefix", (2, 5, 20), 128, 128, 64, "bf16", 0.03, R.RELATIVE, 2, 1, 300, False, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_parity(case):
+    name, grid, d, bq, bk, dt, tau, mode, mk, mn, n_text, hil, B, H = case
+    w = S.small(name, B, H, d, grid, bq, bk, tau, dtype=dt, qscale=6.0, n_text=n_text, hilbert=hil)
+    cfg = cfg_for(w, mode=mode, max_keep=mk, min_keep=mn)
+    full_check(w, cfg, label="small")
+
+
+@pytest.mark.parametrize("mode", [R.RELATIVE, R.ABSOLUTE])
+def test_tiny_workload(mode):
+    w = S.WORKLOADS["tiny"]
+    full_check(w, cfg_for(w, mode=mode), label="tiny")
+
+
+def test_no_residual_flag():
+    w = S.small("nr", 1, 2, 128, (4, 8, 32), 128, 64, 0.02)
+    full_check(w, cfg_for(w, no_residual=True), label="no-residual")
+
+
+# ----------------------------------------------------------------------------- dense path
+@pytest.mark.parametrize("d,bq,bk,dt", [(128, 128, 128, "bf16"), (128, 128, 64, "bf16"), (64, 64, 64, "f32"),
+                                        (128, 64, 128, "bf16")])
+def test_dense_matches_oracle_and_tau_zero(d, bq, bk, dt):
+    m = sa()
+    w = S.small("dense", 1, 2, d, (3, 8, 21), bq, bk, 0.0, dtype=dt)
+    say(f"[case] dense d{d} {bq}x{bk} {dt} N{w.N}")
+    Qc, Kc, Vc, Q, K, V = make(w)
+    Od, Ld = m.dense_ref_gpu(Q, K, V, block_q=bq, lse=True)
+    cfg = cfg_for(w, tau=0.0)
+    rt, O, L = run_gpu(Q, K, V, cfg)
+    assert rt.mask().all()
+    # tau = 0 keeps every block in ascending order: the same tile sequence as the dense path
+    assert torch.equal(O, Od) and torch.equal(L, Ld)
+    for h in range(w.H):
+        q, k, v = head_np(Qc, 0, h), head_np(Kc, 0, h), head_np(Vc, 0, h)
+        O_ref, L_ref = R.dense_ref(q, k, v)
+        o = Od[0, h].float().cpu().numpy()
+        e_rel = np.linalg.norm(o - O_ref) / np.linalg.norm(O_ref)
+        assert e_rel <= 1e-2 and np.abs(o - O_ref).max() <= 3e-2
+        assert np.abs(Ld[0, h].cpu().numpy() - L_ref).max() <= 2e-2
+
+
+# ----------------------------------------------------------------------------- metamorphic
+def test_value_shift_and_key_shift():
+    """V + 1c^T adds c to every output row (weights sum to one); K + 1c^T shifts each
+    row's logits by a constant, leaving mask and output unchanged.  fp32 inputs so
+    that the shifted tensors are exact shifts."""
+    w = S.small("meta", 1, 2, 128, (4, 8, 32), 128, 64, 0.01, dtype="f32")
+    Qc, Kc, Vc, Q, K, V = make(w)
+    cfg = cfg_for(w)
+    rt, O, _ = run_gpu(Q, K, V, cfg)
+    mask0 = rt.mask().cpu().numpy()
+    g = torch.Generator().manual_seed(3)
+    c = torch.randn(w.d, generator=g)
+    rt2, O2, _ = run_gpu(Q, K, (Vc + c).cuda(), cfg)
+    assert np.array_equal(rt2.mask().cpu().numpy(), mask0)   # routing never looks at V
+    err = (O2.cpu() - O.cpu() - c).abs().max().item()
+    assert err <= 1e-2, err
+    ck = 0.5 * torch.randn(w.d, generator=g)
+    rt3, O3, _ = run_gpu(Q, (Kc + ck).cuda(), V, cfg)
+    d3 = rt3.mask().cpu().numpy() != mask0
+    for h in range(w.H):
+        ort = R.route_ref(head_np(Qc, 0, h), head_np(Kc, 0, h), R.RouteParams(w.block_q, w.block_k, w.tau))
+        assert not (d3[0, h] & ~ort.exempt).any()
+    if not d3.any():
+        e = (O3 - O).abs().max().item()
+        assert e <= 1e-2, e
+
+
+def test_identical_keys_make_residual_exact():
+    """Every key of a block equal to its block mean: the residual is exact, so the
+    output equals dense attention (keys chosen bf16-representable)."""
+    m = sa()
+    w = S.small("idk", 1, 2, 128, (4, 8, 30), 128, 64, 0.05)
+    Qc, Kc, Vc, _, _, _ = make(w)
+    n_kb = -(-w.N // 64)
+    reps = torch.repeat_interleave(torch.randn(1, 2, n_kb, 128, generator=torch.Generator().manual_seed(5)), 64, dim=2)
+    K2 = (reps[:, :, : w.N] * 2.0).to(torch.bfloat16)
+    Q2 = (Qc.float() * 0.5).to(torch.bfloat16)
+    cfg = cfg_for(w)
+    rt, O, L = run_gpu(Q2.cuda(), K2.cuda(), Vc.cuda(), cfg)
+    mask = rt.mask().cpu().numpy()
+    assert (~mask).any()
+    for h in range(2):
+        O_ref, L_ref = R.dense_ref(head_np(Q2, 0, h), head_np(K2, 0, h), head_np(Vc, 0, h))
+        o = O[0, h].float().cpu().numpy()
+        assert np.linalg.norm(o - O_ref) / np.linalg.norm(O_ref) <= 1e-2
+        assert np.abs(o - O_ref).max() <= 3e-2
+
+
+def test_deterministic_and_route_reuse():
+    m = sa()
+    w = S.small("det", 1, 3, 128, (4, 8, 32), 128, 64, 0.01, max_keep_frac=0.1)
+    _, _, _, Q, K, V = make(w)
+    cfg = cfg_for(w)
+    rt1, O1, L1 = run_gpu(Q, K, V, cfg)
+    rt2, O2, L2 = run_gpu(Q, K, V, cfg)
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+    for name in ("kv_count", "kv_mask", "row_stats", "q_mean", "k_mean", "v_mean", "cost"):
+        assert torch.equal(getattr(rt1, name), getattr(rt2, name)), name
+    # a route serves several forward calls, and route buffers can be refilled in place
+    O3 = m.forward(Q, K, V, rt1, cfg)
+    m.route(Q, K, V, cfg, out=rt2)
+    O4 = m.forward(Q, K, V, rt2, cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(O3, O1) and torch.equal(O4, O1)
+
+
+def test_side_stream():
+    m = sa()
+    w = S.small("stream", 1, 2, 128, (4, 8, 32), 128, 128, 0.01)
+    _, _, _, Q, K, V = make(w)
+    cfg = cfg_for(w)
+    rt0, O0, _ = run_gpu(Q, K, V, cfg)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        rt = m.route(Q, K, V, cfg)
+        O = m.forward(Q, K, V, rt, cfg)
+    s.synchronize()
+    assert torch.equal(O, O0)
+
+
+def test_work_order_is_cost_sorted_permutation():
+    w = S.small("sched", 1, 4, 128, (4, 8, 32), 128, 64, 0.01)
+    _, _, _, Q, K, V = make(w)
+    rt, _, _ = run_gpu(Q, K, V, cfg_for(w))
+    wo = rt.work_order.cpu().numpy()
+    cost = rt.cost.cpu().numpy().ravel()
+    assert np.array_equal(np.sort(wo), np.arange(wo.size))
+    assert (np.diff(cost[wo]) <= 0).all()
+    # cost = 64-token tiles of kept blocks + one residual tile per 32 pooled blocks
+    # holding a dropped block
+    mask = rt.mask().cpu().numpy().reshape(-1, rt.n_kb)
+    nj = np.minimum(np.arange(rt.n_kb) * 64 + 64, w.N) - np.arange(rt.n_kb) * 64
+    tiles = (mask * ((nj + 63) // 64)).sum(axis=1)
+    n32 = -(-rt.n_kb // 32)
+    pad = np.zeros((mask.shape[0], n32 * 32), dtype=bool)
+    pad[:, : rt.n_kb] = ~mask
+    tiles += pad.reshape(mask.shape[0], -1, 32).any(axis=2).sum(axis=1)
+    assert np.array_equal(cost, tiles)

@@ -327,6 +327,20 @@ def test_all_dropped_closed_form(N, bk):
     np.testing.assert_allclose(O, sdpa64(q, kb, vb, 1.0 / 4.0, bias=bias), rtol=0, atol=1e-12)
 
 
+def test_no_residual_is_attention_over_kept_tokens():
+    """Without the residual, each query block attends to exactly its kept tokens: compare
+    with torch SDPA over the gathered kept keys and values."""
+    q, k, v = structured_qkv(300, 8, 31, period=150)
+    p = R.RouteParams(32, 16, 0.4, R.RELATIVE)
+    rt = R.route_ref(q, k, p)
+    O, L = R.forward_ref_with_mask(q, k, v, rt.mask, p, residual=False)
+    assert (~rt.mask).any()
+    for I in range(rt.mask.shape[0]):
+        tok = np.concatenate([np.arange(J * 16, min(J * 16 + 16, 300)) for J in np.flatnonzero(rt.mask[I])])
+        rows = slice(I * 32, min(I * 32 + 32, 300))
+        np.testing.assert_allclose(O[rows], sdpa64(q[rows], k[tok], v[tok], 1 / math.sqrt(8)), rtol=0, atol=1e-12)
+
+
 def test_recall_is_one_when_all_kept():
     q, k, v = rand_qkv(128, 8, 9)
     p = R.RouteParams(32, 32, 0.0)

@@ -227,18 +227,29 @@ def iter_heads(w: Workload) -> Iterator[tuple]:
             yield b, h, head_qkv(w, b, h, sh)
 
 
-def make_qkv(w: Workload, device: str = "cpu", heads: list | None = None):
-    """Q, K, V as torch tensors [B, H, N, d] in the workload dtype (bf16 by round-to-nearest-even
-    from float64, or float32), built one head at a time so that float64 never holds more
-    than one head.  `heads` optionally restricts to a list of (b, h); others stay zero."""
+def make_qkv(w: Workload, device: str = "cpu", heads: list | None = None, workers: int | None = None):
+    """Q, K, V as torch tensors [B, H, N, d] in the workload dtype (bf16 by torch's cast
+    from float64, or float32), built one head at a time (heads in parallel threads; each
+    head has its own seed, so the result does not depend on scheduling).  `heads`
+    optionally restricts to a list of (b, h); others stay zero."""
+    import concurrent.futures as cf
+    import os
+
     import torch
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     shape = (w.B, w.H, w.N, w.d)
-    out = [torch.zeros(shape, dtype=tdt, device=device) for _ in range(3)]
+    out = [torch.zeros(shape, dtype=tdt) for _ in range(3)]
     sh = _Shared(w)
     todo = heads if heads is not None else [(b, h) for b in range(w.B) for h in range(w.H)]
-    for b, h in todo:
-        arrs = head_qkv(w, b, h, sh)
-        for dst, a in zip(out, arrs):
+
+    def one(bh):
+        b, h = bh
+        for dst, a in zip(out, head_qkv(w, b, h, sh)):
             dst[b, h].copy_(torch.from_numpy(a).to(tdt))
+
+    n = workers or min(16, len(os.sched_getaffinity(0)), max(1, len(todo)))
+    with cf.ThreadPoolExecutor(max_workers=n) as ex:
+        list(ex.map(one, todo))
+    if device != "cpu":
+        out = [t.to(device) for t in out]
     return tuple(out)
