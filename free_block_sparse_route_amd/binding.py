@@ -46,7 +46,7 @@ class SparseAttnError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m free_block_sparse_route_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python free_block_sparse_route_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, R = ctypes.POINTER(SaParams), ctypes.POINTER(SaRoute)
     vp = ctypes.c_void_p

@@ -1,6 +1,8 @@
 """Build libsparse_attn.so in-tree with hipcc for gfx950.
 
-    python -m free_block_sparse_route_amd.build [--verbose]
+    python free_block_sparse_route_amd/build.py [--verbose]
+
+(run by path: importing the package itself needs the built library)
 
 Each HIP source is compiled to an object under _build/ (in parallel), then
 linked into free_block_sparse_route_amd/libsparse_attn.so.  Every call

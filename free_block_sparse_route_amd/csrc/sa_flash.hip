@@ -128,58 +128,78 @@ struct Staging {
     u32x4 v[FC<D, BQ>::VU][4];
 };
 
-// 64 bf16 rows: K unit u = (row u/(D/8), 8 columns); V unit u = (rows 4g..4g+3, 8 columns)
-template <int D, int BQ>
-__device__ __forceinline__ void load_bf16(const bf16 *ks, const bf16 *vs, int valid, Staging<D, BQ> &st) {
-    using C = FC<D, BQ>;
-    const int tid = threadIdx.x;
-    const u32x4 zero = {};
-#pragma unroll
-    for (int i = 0; i < C::KU; ++i) {
-        const int u = tid + i * C::THREADS;
-        const int row = u / (D / 8), ch = u % (D / 8);
-        st.k[i] = (u < C::K_UNITS && row < valid) ? *reinterpret_cast<const u32x4 *>(ks + (size_t)row * D + ch * 8)
-                                                  : zero;
-    }
-#pragma unroll
-    for (int i = 0; i < C::VU; ++i) {
-        const int u = tid + i * C::THREADS;
-        const int g = u % 16, c = u / 16;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 4 * g + r;
-            st.v[i][r] = (u < C::V_UNITS && row < valid)
-                             ? *reinterpret_cast<const u32x4 *>(vs + (size_t)row * D + c * 8)
-                             : zero;
-        }
-    }
+// Buffer resource over `bytes` bytes at `base`: loads past the end return zero.
+// Rows of a tile past its valid count only ever lie past the end of a head's
+// tensor (blocks are multiples of the tile height except the last one), so the
+// hardware range check supplies the zero fill.  All offsets go in the VGPR
+// offset, which the range check covers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
-// 32 fp32 rows: K unit u = (row u/(D/4), 4 columns); V unit u = (rows 4g..4g+3, 4 columns)
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// Per-thread byte offsets of a tile's 16-byte chunks inside the tile; they
+// stay fixed for the whole pass (the tile position goes into the buffer
+// resource's base), so the offset registers are never rewritten while loads
+// are in flight.
 template <int D, int BQ>
-__device__ __forceinline__ void load_f32(const float *ks, const float *vs, int valid, Staging<D, BQ> &st) {
-    using C = FC<D, BQ>;
-    const int tid = threadIdx.x;
-    const u32x4 zero = {};
+struct TileOffsets {
+    int kb[FC<D, BQ>::KU];     // 64 bf16 rows: K unit u = (row u/(D/8), 8 columns)
+    int vb[FC<D, BQ>::VU];     //               V unit u = (rows 4g..4g+3, 8 columns), row 4g
+    int kf[FC<D, BQ>::KU];     // 32 fp32 rows: K unit u = (row u/(D/4), 4 columns)
+    int vf[FC<D, BQ>::VU];     //               V unit u = (rows 4g..4g+3, 4 columns), row 4g
+
+    __device__ void init() {
+        using C = FC<D, BQ>;
+        const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < C::KU; ++i) {
-        const int u = tid + i * C::THREADS;
-        const int row = u / (D / 4), c4 = u % (D / 4);
-        st.k[i] = (u < C::K_UNITS && row < valid) ? *reinterpret_cast<const u32x4 *>(ks + (size_t)row * D + c4 * 4)
-                                                  : zero;
-    }
+        for (int i = 0; i < C::KU; ++i) {
+            const int u = tid + i * C::THREADS;
+            kb[i] = (u / (D / 8)) * (D * 2) + (u % (D / 8)) * 16;
+            kf[i] = (u / (D / 4)) * (D * 4) + (u % (D / 4)) * 16;
+        }
 #pragma unroll
-    for (int i = 0; i < C::VU; ++i) {
-        const int u = tid + i * C::THREADS;
-        const int g = u % 8, c = u / 8;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 4 * g + r;
-            st.v[i][r] = (u < C::V_UNITS && row < valid)
-                             ? *reinterpret_cast<const u32x4 *>(vs + (size_t)row * D + c * 4)
-                             : zero;
+        for (int i = 0; i < C::VU; ++i) {
+            const int u = tid + i * C::THREADS;
+            vb[i] = (4 * (u % 16)) * (D * 2) + (u / 16) * 16;
+            vf[i] = (4 * (u % 8)) * (D * 4) + (u / 8) * 16;
         }
     }
+};
+
+template <int D, int BQ>
+__device__ __forceinline__ void load_bf16(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                          const TileOffsets<D, BQ> &to, Staging<D, BQ> &st) {
+    using C = FC<D, BQ>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < C::KU; ++i)
+        if (C::K_UNITS % C::THREADS == 0 || tid + i * C::THREADS < C::K_UNITS) st.k[i] = bload(rk, to.kb[i]);
+#pragma unroll
+    for (int i = 0; i < C::VU; ++i)
+        if (C::V_UNITS % C::THREADS == 0 || tid + i * C::THREADS < C::V_UNITS) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st.v[i][r] = __builtin_amdgcn_raw_buffer_load_b128(rv, to.vb[i], r * (D * 2), 0);
+        }
+}
+
+template <int D, int BQ>
+__device__ __forceinline__ void load_f32(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                         const TileOffsets<D, BQ> &to, Staging<D, BQ> &st) {
+    using C = FC<D, BQ>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < C::KU; ++i)
+        if (C::K_UNITS % C::THREADS == 0 || tid + i * C::THREADS < C::K_UNITS) st.k[i] = bload(rk, to.kf[i]);
+#pragma unroll
+    for (int i = 0; i < C::VU; ++i)
+        if (C::V_UNITS % C::THREADS == 0 || tid + i * C::THREADS < C::V_UNITS) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st.v[i][r] = __builtin_amdgcn_raw_buffer_load_b128(rv, to.vf[i], r * (D * 4), 0);
+        }
 }
 
 // V^T position of key 4g (the 4 keys 4g..4g+3 stay contiguous): bits 2 and 3 of
@@ -202,7 +222,7 @@ __device__ __forceinline__ void store_bf16(bf16 *buf, const Staging<D, BQ> &st) 
 #pragma unroll
     for (int i = 0; i < C::KU; ++i) {
         const int u = tid + i * C::THREADS;
-        if (u < C::K_UNITS) {
+        if (C::K_UNITS % C::THREADS == 0 || u < C::K_UNITS) {
             const int row = u / (D / 8), ch = u % (D / 8);
             *reinterpret_cast<u32x4 *>(Ks + row * C::KSTR + ch * 8) = st.k[i];
         }
@@ -210,7 +230,7 @@ __device__ __forceinline__ void store_bf16(bf16 *buf, const Staging<D, BQ> &st) 
 #pragma unroll
     for (int i = 0; i < C::VU; ++i) {
         const int u = tid + i * C::THREADS;
-        if (u < C::V_UNITS) {
+        if (C::V_UNITS % C::THREADS == 0 || u < C::V_UNITS) {
             const int g = u % 16, c = u / 16;
             const int pos = vt_pos(g);
 #pragma unroll
@@ -235,7 +255,7 @@ __device__ __forceinline__ void store_split(bf16 *buf, const Staging<D, BQ> &st)
 #pragma unroll
     for (int i = 0; i < C::KU; ++i) {
         const int u = tid + i * C::THREADS;
-        if (u < C::K_UNITS) {
+        if (C::K_UNITS % C::THREADS == 0 || u < C::K_UNITS) {
             const int row = u / (D / 4), c4 = u % (D / 4);
             float x[4], lo[4];
 #pragma unroll
@@ -250,7 +270,7 @@ __device__ __forceinline__ void store_split(bf16 *buf, const Staging<D, BQ> &st)
 #pragma unroll
     for (int i = 0; i < C::VU; ++i) {
         const int u = tid + i * C::THREADS;
-        if (u < C::V_UNITS) {
+        if (C::V_UNITS % C::THREADS == 0 || u < C::V_UNITS) {
             const int g = u % 8, c = u / 8;
             const int pos = vt_pos(g);
 #pragma unroll
@@ -282,20 +302,34 @@ template <> struct Store4<float> {
     }
 };
 
+// Key/value rows and fp32 block means of one (b, h).
+template <typename T>
+struct HeadSrc {
+    const T *k, *v;
+    const float *km, *vm;
+    int n_rows, n_means;
+};
+
+// Issue the global loads of tile t: a buffer resource starting at the tile's
+// first row and ending at the end of the head, so rows past the end read zero.
 template <typename T, int D, int BQ>
-__device__ __forceinline__ void issue_tile(const TileDesc &t, const T *k, const T *v, const float *kmean,
-                                           const float *vmean, Staging<D, BQ> &st) {
-    const size_t off = (size_t)t.row0 * D;
-    if constexpr (sizeof(T) == 2) {
-        if (t.kind == kExact) load_bf16<D, BQ>(k + off, v + off, t.valid, st);
-        else load_f32<D, BQ>(kmean + off, vmean + off, t.valid, st);
+__device__ __forceinline__ void issue_tile(const TileDesc &t, const HeadSrc<T> &hs, const TileOffsets<D, BQ> &to,
+                                           Staging<D, BQ> &st) {
+    if (t.kind == kResidual) {
+        const uint32_t bytes = (uint32_t)(hs.n_means - t.row0) * (D * 4);
+        load_f32<D, BQ>(buffer_rsrc(hs.km + (size_t)t.row0 * D, bytes), buffer_rsrc(hs.vm + (size_t)t.row0 * D, bytes),
+                        to, st);
     } else {
-        load_f32<D, BQ>(t.kind == kExactSplit ? k + off : kmean + off, t.kind == kExactSplit ? v + off : vmean + off,
-                        t.valid, st);
+        const uint32_t bytes = (uint32_t)(hs.n_rows - t.row0) * (D * sizeof(T));
+        const auto rk = buffer_rsrc(hs.k + (size_t)t.row0 * D, bytes);
+        const auto rv = buffer_rsrc(hs.v + (size_t)t.row0 * D, bytes);
+        if constexpr (sizeof(T) == 2) load_bf16<D, BQ>(rk, rv, to, st);
+        else load_f32<D, BQ>(rk, rv, to, st);
     }
 }
 
-template <typename T, int D, int BQ>
+// kSparse: kept-list and residual tiles from a route; otherwise every key tile (dense).
+template <typename T, int D, int BQ, bool kSparse>
 __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_per_eu(FC<D, BQ>::WPE, FC<D, BQ>::WPE))) void flash_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
     FlashArgs a) {
@@ -304,7 +338,7 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     bf16 *lds = reinterpret_cast<bf16 *>(smem_raw);
 
-    const int item = a.work_order ? __builtin_amdgcn_readfirstlane(a.work_order[blockIdx.x]) : (int)blockIdx.x;
+    const int item = kSparse ? __builtin_amdgcn_readfirstlane(a.work_order[blockIdx.x]) : (int)blockIdx.x;
     const int bh = item / a.n_qb;
     const int I = item - bh * a.n_qb;
     const int lane = lane_id();
@@ -345,7 +379,7 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
     ts.exact_kind = kF32 ? kExactSplit : kExact;
     ts.dense_tiles = (a.N + ts.exact_rows - 1) / ts.exact_rows;
     const size_t row_id = (size_t)bh * a.n_qb + I;
-    if (a.kv_idx) {
+    if constexpr (kSparse) {
         ts.list = a.kv_idx + row_id * a.kv_idx_cap;
         ts.cnt = __builtin_amdgcn_readfirstlane(a.kv_count[row_id]);
         ts.mask = a.kv_mask + row_id * a.mask_words;
@@ -356,21 +390,28 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
         ts.cnt = 0;
         ts.n_rt = 0;
     }
-    const float *kmean = a.k_mean ? a.k_mean + (size_t)bh * a.n_kb * D : nullptr;
-    const float *vmean = a.v_mean ? a.v_mean + (size_t)bh * a.n_kb * D : nullptr;
+    HeadSrc<T> hs;
+    hs.k = k + head;
+    hs.v = v + head;
+    hs.km = kSparse ? a.k_mean + (size_t)bh * a.n_kb * D : nullptr;
+    hs.vm = kSparse ? a.v_mean + (size_t)bh * a.n_kb * D : nullptr;
+    hs.n_rows = a.N;
+    hs.n_means = a.n_kb;
+    TileOffsets<D, BQ> to;
+    to.init();
     const float lg_bk = log2f((float)a.block_k);
     const float lg_last = log2f((float)(a.N - (a.n_kb - 1) * a.block_k));
 
     f32x16 acc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_ref = -INFINITY, l_run = 0.f;   // softmax reference (log2 units) and normaliser
 
     Staging<D, BQ> st;
     TileDesc cur, nxt;
     bool have = ts.next(cur, a);
     if (have) {
-        issue_tile<T, D, BQ>(cur, k + head, v + head, kmean, vmean, st);
+        issue_tile<T, D, BQ>(cur, hs, to, st);
         if (cur.kind == kExact) store_bf16<D, BQ>(lds, st);
         else store_split<D, BQ>(lds, st);
     }
@@ -378,7 +419,12 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
     int buf = 0;
     while (have) {
         const bool have_next = ts.next(nxt, a);
-        if (have_next) issue_tile<T, D, BQ>(nxt, k + head, v + head, kmean, vmean, st);
+        // Nothing is in flight here (the previous tile's loads were consumed by
+        // its LDS stores).  Saying so explicitly keeps the compiler from placing
+        // its loop-entry wait after the prefetch below, which would expose the
+        // prefetch latency on every tile.
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt/lgkmcnt untouched
+        if (have_next) issue_tile<T, D, BQ>(nxt, hs, to, st);
         const bf16 *Ks = lds + buf * C::BUF;
         const bf16 *Vt = Ks + C::K_ELEMS;
 
@@ -397,22 +443,29 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
         // accumulator register r of lane (h, l32) in block b holds LDS key row
         // 32b + 8(r/4) + 4h + r%4
         const bool split = cur.kind != kExact;
-        float mx = -INFINITY;
+        const float c = a.scale_log2;
+        float mx = -INFINITY;       // this lane's tile maximum, log2 units
         if (!split) {
+            if (cur.valid < kTile) {            // partial tile (uniform): drop absent keys
+                const int lim = cur.valid - 4 * h;
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+                for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kv = 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const float x = kv < cur.valid ? s[b][r] * a.scale_log2 : -INFINITY;
-                    s[b][r] = x;
-                    mx = fmaxf(mx, x);
-                }
+                    for (int r = 0; r < 16; ++r)
+                        if (32 * b + 8 * (r >> 2) + (r & 3) >= lim) s[b][r] = -INFINITY;
+            }
+            float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                m0 = fmaxf(m0, s[0][r]);
+                m1 = fmaxf(m1, s[1][r]);
+            }
+            mx = fmaxf(m0, m1) * c;             // c > 0
         } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int kv = 8 * (r >> 2) + 4 * h + (r & 3);
-                float x = (s[0][r] + s[1][r]) * a.scale_log2;
+                float x = (s[0][r] + s[1][r]) * c;
                 if (cur.kind == kResidual) {
                     const bool drop = ((cur.kept >> kv) & 1u) == 0;
                     x = drop ? x + (cur.row0 + kv == a.n_kb - 1 ? lg_last : lg_bk) : -INFINITY;
@@ -424,11 +477,20 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
             }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
-        float ps = 0.f;
+        // Lazy rescaling: the reference m_ref moves only when some row of the wave
+        // exceeds it by more than 8 (log2 units), so weights stay <= 2^8 and the
+        // accumulator rescale is skipped on most tiles.  The result is the same
+        // softmax: numerator and normaliser share the reference.
+        if (__ballot(mx > m_ref + 8.f) != 0) {
+            const float m_new = fmaxf(m_ref, mx);
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+            m_ref = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+        }
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+        float ps0 = 0.f, ps1 = 0.f;
         // P^T operands: step j takes registers 8(j&1)..8(j&1)+7 of block j/2; a
         // split tile feeds the same weights to its hi (keys 0..31) and lo (32..63) halves
         bf16x8 pb[4];
@@ -437,23 +499,21 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
             for (int b = 0; b < 2; ++b)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(s[b][r] - m_use);
-                    ps += p;
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -m_use));
+                    if (r & 1) ps1 += p; else ps0 += p;
                     pb[2 * b + (r >> 3)][r & 7] = (bf16)p;
                 }
         } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float p = __builtin_amdgcn_exp2f(s[0][r] - m_use);
-                ps += p;
+                if (r & 1) ps1 += p; else ps0 += p;
                 pb[r >> 3][r & 7] = (bf16)p;
             }
             pb[2] = pb[0];
             pb[3] = pb[1];
         }
-        l_run = l_run * alpha + ps;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+        l_run += ps0 + ps1;
         __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
@@ -489,16 +549,16 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
                 Store4<T>::st(orow + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
                               acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
         if (a.lse && h == 0)
-            a.lse[(size_t)bh * a.N + qrow] = lt > 0.f ? (m_run + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+            a.lse[(size_t)bh * a.N + qrow] = lt > 0.f ? (m_ref + log2f(lt)) * 0.69314718055994531f : -INFINITY;
     }
 }
 
-template <typename T, int D, int BQ>
+template <typename T, int D, int BQ, bool kSparse>
 static hipError_t launch_flash_t(const void *q, const void *k, const void *v, void *o,
                                  const FlashArgs &a, int BH, hipStream_t st) {
     using C = FC<D, BQ>;
     static bool attr_set = false;
-    auto kern = flash_kernel<T, D, BQ>;
+    auto kern = flash_kernel<T, D, BQ, kSparse>;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)C::LDS);
@@ -511,13 +571,20 @@ static hipError_t launch_flash_t(const void *q, const void *k, const void *v, vo
     return hipGetLastError();
 }
 
+template <typename T, int D, int BQ>
+static hipError_t launch_flash_s(const void *q, const void *k, const void *v, void *o, const FlashArgs &a,
+                                 int BH, hipStream_t st) {
+    return a.kv_idx ? launch_flash_t<T, D, BQ, true>(q, k, v, o, a, BH, st)
+                    : launch_flash_t<T, D, BQ, false>(q, k, v, o, a, BH, st);
+}
+
 template <typename T>
 static hipError_t launch_flash_dt(int D, int BQ, const void *q, const void *k, const void *v, void *o,
                                   const FlashArgs &a, int BH, hipStream_t st) {
-    if (D == 128) return BQ == 128 ? launch_flash_t<T, 128, 128>(q, k, v, o, a, BH, st)
-                                   : launch_flash_t<T, 128, 64>(q, k, v, o, a, BH, st);
-    return BQ == 128 ? launch_flash_t<T, 64, 128>(q, k, v, o, a, BH, st)
-                     : launch_flash_t<T, 64, 64>(q, k, v, o, a, BH, st);
+    if (D == 128) return BQ == 128 ? launch_flash_s<T, 128, 128>(q, k, v, o, a, BH, st)
+                                   : launch_flash_s<T, 128, 64>(q, k, v, o, a, BH, st);
+    return BQ == 128 ? launch_flash_s<T, 64, 128>(q, k, v, o, a, BH, st)
+                     : launch_flash_s<T, 64, 64>(q, k, v, o, a, BH, st);
 }
 
 hipError_t launch_flash(int dtype, int D, int BQ, const void *q, const void *k, const void *v,
