@@ -22,8 +22,8 @@ SA_BF16, SA_F32 = 0, 1
 RELATIVE, ABSOLUTE = 0, 1
 FLAG_NO_RESIDUAL = 1
 SA_SCHED_INTS = 8192
-BUFFERS = ("kv_count", "kv_idx", "kv_mask", "q_mean", "k_mean", "v_mean", "row_stats", "cost", "work_order",
-           "sched")
+BUFFERS = ("kv_count", "kv_idx", "kv_mask", "q_mean", "k_mean", "v_mean", "kv_split", "row_stats", "cost",
+           "work_order", "sched")
 
 
 class SaParams(ctypes.Structure):
@@ -145,6 +145,7 @@ class Route:
         self.q_mean = torch.empty((B, H, self.n_qb, d), dtype=torch.float32, **e)
         self.k_mean = torch.empty((B, H, self.n_kb, d), dtype=torch.float32, **e)
         self.v_mean = torch.empty((B, H, self.n_kb, d), dtype=torch.float32, **e)
+        self.kv_split = torch.empty((B, H, 2, words, 64, d), dtype=torch.bfloat16, **e)
         self.row_stats = torch.empty((B, H, self.n_qb, 2), dtype=torch.float32, **e)
         self.cost = torch.empty((B, H, self.n_qb), dtype=torch.int32, **e)
         self.work_order = torch.empty((B * H * self.n_qb,), dtype=torch.int32, **e)

@@ -113,6 +113,7 @@ sa_status sparse_attn_route_sizes(const sa_params *p, int32_t kv_idx_cap, size_t
     bytes[SA_BUF_Q_MEAN] = rows * (size_t)p->d * 4;
     bytes[SA_BUF_K_MEAN] = (size_t)d.BH * d.n_kb * p->d * 4;
     bytes[SA_BUF_V_MEAN] = (size_t)d.BH * d.n_kb * p->d * 4;
+    bytes[SA_BUF_KV_SPLIT] = (size_t)d.BH * 2 * d.words * 64 * p->d * 2;
     bytes[SA_BUF_ROW_STATS] = rows * 2 * 4;
     bytes[SA_BUF_COST] = rows * 4;
     bytes[SA_BUF_WORK_ORDER] = rows * 4;
@@ -130,7 +131,7 @@ sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, co
     if ((s = check_ptr(r->kv_count, "route.kv_count")) || (s = check_ptr(r->kv_idx, "route.kv_idx")) ||
         (s = check_ptr(r->kv_mask, "route.kv_mask")) || (s = check_ptr(r->q_mean, "route.q_mean")) ||
         (s = check_ptr(r->k_mean, "route.k_mean")) || (s = check_ptr(r->v_mean, "route.v_mean")) ||
-        (s = check_ptr(r->row_stats, "route.row_stats")) || (s = check_ptr(r->cost, "route.cost")) ||
+        (s = check_ptr(r->kv_split, "route.kv_split")) || (s = check_ptr(r->row_stats, "route.row_stats")) || (s = check_ptr(r->cost, "route.cost")) ||
         (s = check_ptr(r->work_order, "route.work_order")) || (s = check_ptr(r->sched, "route.sched")))
         return s;
     if (r->kv_idx_cap < min_cap(p))
@@ -142,6 +143,7 @@ sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, co
     pa.N = p->N; pa.block_q = p->block_q; pa.block_k = p->block_k;
     pa.n_qb = d.n_qb; pa.n_kb = d.n_kb;
     pa.q_mean = r->q_mean; pa.k_mean = r->k_mean; pa.v_mean = r->v_mean;
+    pa.kv_split = (sa::bf16 *)r->kv_split; pa.words = d.words;
     hipError_t e = sa::launch_pool(p->dtype, p->d, q, k, v, pa, (int)d.BH, st);
     if (e != hipSuccess) return hip_fail(e, "route: pool launch");
 
@@ -176,7 +178,7 @@ static sa_status run_flash(const sa_params *p, const void *q, const void *k, con
         fa.kv_idx_cap = r->kv_idx_cap;
         fa.residual = (p->flags & SA_FLAG_NO_RESIDUAL) ? 0 : 1;
         fa.kv_count = r->kv_count; fa.kv_idx = r->kv_idx; fa.work_order = r->work_order;
-        fa.kv_mask = r->kv_mask; fa.k_mean = r->k_mean; fa.v_mean = r->v_mean;
+        fa.kv_mask = r->kv_mask; fa.kv_split = (const sa::bf16 *)r->kv_split;
     }
     hipError_t e = sa::launch_flash(p->dtype, p->d, p->block_q, q, k, v, o, fa, (int)d.BH,
                                     (hipStream_t)stream);
@@ -193,7 +195,7 @@ sa_status sparse_attn_forward(const sa_params *p, const void *q, const void *k, 
         return s;
     if ((s = check_ptr(r->kv_count, "route.kv_count")) || (s = check_ptr(r->kv_idx, "route.kv_idx")) ||
         (s = check_ptr(r->kv_mask, "route.kv_mask")) ||
-        (s = check_ptr(r->k_mean, "route.k_mean")) || (s = check_ptr(r->v_mean, "route.v_mean")) ||
+        (s = check_ptr(r->kv_split, "route.kv_split")) ||
         (s = check_ptr(r->work_order, "route.work_order")))
         return s;
     if (r->kv_idx_cap < min_cap(p))

@@ -4,60 +4,63 @@
 //
 // One workgroup per (b, h, query block).  Each wave owns 32 query rows and
 // keeps them as the B operand of v_mfma_f32_32x32x16_bf16 for the whole pass.
-// The kernel walks a stream of key/value tiles:
+// The kernel walks a stream of 64-row key/value tiles:
 //   exact tiles     the tokens of the kept key blocks, in ascending block order
 //                   (64 bf16 tokens, or 32 fp32 tokens in hi/lo split form)
-//   residual tiles  32 block means (fp32, hi/lo split) with an additive logit
-//                   bias of log2(n_J) for dropped blocks and -inf for kept
-//                   ones; a tile whose 32 blocks are all kept is skipped
-// and folds both kinds into the same running max and normaliser.
+//   residual tiles  32 block means in hi/lo split form (prepared by routing)
+//                   with an additive logit bias of log2(n_J) for dropped blocks
+//                   and -inf for kept ones; a tile whose 32 blocks are all kept
+//                   is skipped
+// and folds both kinds into the same running max and normaliser.  A split tile
+// holds bf16(x) in rows 0..31 and bf16(x - bf16(x)) in rows 32..63, so the same
+// 64-column MFMA sequence yields hi + lo products (about 2^-16 relative).
 //
-// Layout choice: scores are formed transposed, S^T = K Q^T, so that the MFMA
-// accumulator gives each lane a single query row (lane & 31) and 32 of the
-// tile's keys.  The output is formed transposed too, O^T = V^T P^T: the P^T
-// operand is then exactly what each lane already holds after the softmax, and
-// the per-row max, normaliser and rescale factor are per-lane scalars (the two
-// lane halves holding the same row combine once per tile with one shuffle for
-// the max, and once at the end for the normaliser).  K is staged row-major in
-// LDS; V is staged transposed (V^T, keys contiguous per feature) with keys
-// permuted inside each group of 16 so that every operand fetch is one 16-byte
-// LDS read.  Both are padded by 16 bytes per row against bank conflicts and
-// double-buffered: the global loads of tile t+1 are in flight while tile t is
-// computed.
+// Products are formed transposed: S^T = K Q^T and O^T = V^T P^T.  The MFMA
+// accumulator then gives each lane one query row (lane & 31) and 32 of the
+// tile's keys, P^T is exactly what each lane holds after the softmax, and the
+// row max, normaliser and rescale factor are per-lane scalars.
+//
+// LDS: K and V tiles row-major (features contiguous), two stages in two arrays.  bf16 tiles
+// go straight from memory into LDS with buffer->LDS loads (no registers, no
+// LDS store instructions); the buffer range check zero-fills rows past the end
+// of a head.  16-byte chunks are XOR-swizzled per row: for K so that 16 lanes
+// reading one feature chunk of 16 rows hit distinct banks, for V so that the
+// transposing reads (ds_read_b64_tr_b16) that build V^T operands spread over
+// all banks.
 #include "sa_device.h"
 #include "sa_internal.h"
 
 namespace sa {
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 template <int D, int BQ>
 struct FC {
     static constexpr int WAVES = BQ / 32;
     static constexpr int THREADS = WAVES * kWave;
-    static constexpr int KSTR = D + 8;               // bf16 elements per K row in LDS
-    static constexpr int VSTR = kTile + 8;           // bf16 elements per V^T row in LDS
-    static constexpr int K_ELEMS = kTile * KSTR;
-    static constexpr int V_ELEMS = D * VSTR;
-    static constexpr int BUF = K_ELEMS + V_ELEMS;
-    static constexpr size_t LDS = 2 * (size_t)BUF * sizeof(bf16);
-    // 16-byte global chunks per tile: 64 bf16 rows or 32 fp32 rows of K (8D), and
-    // the same for V in 4-row groups (2D); equal for both tile formats
-    static constexpr int K_UNITS = 8 * D;
-    static constexpr int V_UNITS = 2 * D;
-    static constexpr int KU = (K_UNITS + THREADS - 1) / THREADS;
-    static constexpr int VU = (V_UNITS + THREADS - 1) / THREADS;
+    static constexpr int RB = D * 2;                    // bytes per LDS row (bf16)
+    static constexpr int NC = D / 8;                    // 16-byte chunks per row
+    static constexpr int TILE = kTile * RB;             // bytes of one K or V tile
+    static constexpr int STAGE = 2 * TILE;              // K then V
+    static constexpr int PPW = TILE / 1024 / WAVES;     // 1 KB buffer->LDS pieces per wave per tile
+    static constexpr int SU = 32 * (D / 4) / THREADS;   // 16-byte fp32 units per thread per tile
     // waves per SIMD the register budget targets: two 128-row workgroups share a
     // CU; a 64-row workgroup (2 waves) gets the full register file
     static constexpr int WPE = BQ == 128 ? 2 : 1;
 };
 
-// Tile kinds.  A "split" tile covers 32 rows of fp32 data: LDS rows 0..31 hold
-// the bf16 round-to-nearest part of each row and rows 32..63 the bf16 remainder
-// (x - hi), for both K and V, so the same 64-column MFMA sequence yields
-// hi + lo products: logits to about 2^-16 relative instead of 2^-9.
+// chunk position = logical chunk ^ swizzle(row)
+template <int D> __device__ __forceinline__ int swz_k(int r) { return r & (D / 8 - 1); }
+template <int D> __device__ __forceinline__ int swz_v(int r) {
+    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
 enum : int {
     kExact = 0,        // 64 bf16 tokens of a kept block
     kExactSplit = 1,   // 32 fp32 tokens of a kept block (fp32 inputs)
-    kResidual = 2,     // 32 block means (fp32), dropped blocks only
+    kResidual = 2,     // 32 block means, split, dropped blocks only
 };
 
 struct TileDesc {
@@ -68,7 +71,9 @@ struct TileDesc {
 };
 
 // The tile sequence of one work item; every thread steps it identically and
-// every field is wave-uniform.
+// every field is wave-uniform.  The kept-block index and the mask word are
+// fetched one step ahead, so their memory latency is hidden behind a tile
+// instead of delaying the next tile's loads.
 struct TileStream {
     const int32_t *list;
     const uint32_t *mask;
@@ -76,6 +81,15 @@ struct TileStream {
     int exact_rows, exact_kind;
     int dense_tiles, t;
     int rt, n_rt;
+    int J_cur, J_pf;          // kept blocks li and li + 1
+    uint32_t w_cur, w_pf;     // mask words rt and rt + 1
+
+    __device__ void prime() {
+        J_cur = cnt > 0 ? __builtin_amdgcn_readfirstlane(list[0]) : 0;
+        J_pf = cnt > 1 ? __builtin_amdgcn_readfirstlane(list[1]) : 0;
+        w_cur = n_rt > 0 ? (uint32_t)__builtin_amdgcn_readfirstlane(mask[0]) : 0u;
+        w_pf = n_rt > 1 ? (uint32_t)__builtin_amdgcn_readfirstlane(mask[1]) : 0u;
+    }
 
     __device__ bool next(TileDesc &o, const FlashArgs &a) {
         if (!list) {
@@ -89,14 +103,15 @@ struct TileStream {
             return false;
         }
         while (li < cnt) {
-            const int J = __builtin_amdgcn_readfirstlane(list[li]);
-            const int b0 = J * a.block_k;
+            const int b0 = J_cur * a.block_k;
             const int b1 = min(b0 + a.block_k, a.N);
             const int tok0 = b0 + sub * exact_rows;
             ++sub;
             if (b0 + sub * exact_rows >= b1) {
                 ++li;
                 sub = 0;
+                J_cur = J_pf;
+                J_pf = li + 1 < cnt ? __builtin_amdgcn_readfirstlane(list[li + 1]) : 0;
             }
             if (tok0 < b1) {
                 o.kind = exact_kind;
@@ -107,13 +122,15 @@ struct TileStream {
         }
         while (rt < n_rt) {
             const int cur = rt++;
-            const uint32_t bits = (uint32_t)__builtin_amdgcn_readfirstlane(mask[cur]);
+            const uint32_t bits = w_cur;
+            w_cur = w_pf;
+            w_pf = rt + 1 < n_rt ? (uint32_t)__builtin_amdgcn_readfirstlane(mask[rt + 1]) : 0u;
             const int lim = a.n_kb - cur * 32;
             const uint32_t vmask = lim >= 32 ? ~0u : ((1u << lim) - 1u);
             if ((~bits & vmask) != 0) {
                 o.kind = kResidual;
                 o.row0 = cur * 32;
-                o.valid = min(32, lim);
+                o.valid = kTile;
                 o.kept = bits | ~vmask;
                 return true;
             }
@@ -122,90 +139,65 @@ struct TileStream {
     }
 };
 
-template <int D, int BQ>
-struct Staging {
-    u32x4 k[FC<D, BQ>::KU];
-    u32x4 v[FC<D, BQ>::VU][4];
-};
-
-// Buffer resource over `bytes` bytes at `base`: loads past the end return zero.
-// Rows of a tile past its valid count only ever lie past the end of a head's
-// tensor (blocks are multiples of the tile height except the last one), so the
-// hardware range check supplies the zero fill.  All offsets go in the VGPR
-// offset, which the range check covers.
+// Buffer resource over `bytes` bytes at `base`: loads past the end return zero
+// (also when they go straight to LDS).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-
-// Per-thread byte offsets of a tile's 16-byte chunks inside the tile; they
-// stay fixed for the whole pass (the tile position goes into the buffer
-// resource's base), so the offset registers are never rewritten while loads
-// are in flight.
+// Per-lane constants of the pass: source offsets of the buffer->LDS pieces (a
+// wave's piece i covers LDS bytes [(w + WAVES i) KB, +1 KB) of a tile, lane l
+// its 16 bytes at l*16, holding the swizzled chunk of that slot), and the LDS
+// read bases of the K and V^T operands.
 template <int D, int BQ>
-struct TileOffsets {
-    int kb[FC<D, BQ>::KU];     // 64 bf16 rows: K unit u = (row u/(D/8), 8 columns)
-    int vb[FC<D, BQ>::VU];     //               V unit u = (rows 4g..4g+3, 8 columns), row 4g
-    int kf[FC<D, BQ>::KU];     // 32 fp32 rows: K unit u = (row u/(D/4), 4 columns)
-    int vf[FC<D, BQ>::VU];     //               V unit u = (rows 4g..4g+3, 4 columns), row 4g
+struct Lanes {
+    int ksrc[FC<D, BQ>::PPW], vsrc[FC<D, BQ>::PPW];
+    int kread[D / 16];         // K operand of step c: row l32, features 16c + 8h (swizzled)
+    int vread[D / 32];         // V^T operand of feature block db (rows 4h + (i>>2))
 
-    __device__ void init() {
+    __device__ void init(int wave, int lane) {
         using C = FC<D, BQ>;
-        const int tid = threadIdx.x;
+        constexpr int RPK = 1024 / C::RB;              // rows per 1 KB piece
+        constexpr int SPR = C::RB / 16;                // 16-byte slots per row
 #pragma unroll
-        for (int i = 0; i < C::KU; ++i) {
-            const int u = tid + i * C::THREADS;
-            kb[i] = (u / (D / 8)) * (D * 2) + (u % (D / 8)) * 16;
-            kf[i] = (u / (D / 4)) * (D * 4) + (u % (D / 4)) * 16;
+        for (int i = 0; i < C::PPW; ++i) {
+            const int q = wave + C::WAVES * i;
+            const int r = q * RPK + lane / SPR;
+            const int p = lane % SPR;
+            ksrc[i] = r * C::RB + 16 * (p ^ swz_k<D>(r));
+            vsrc[i] = r * C::RB + 16 * (p ^ swz_v<D>(r));
         }
+        const int h = lane >> 5, l32 = lane & 31;
+        const int fk = swz_k<D>(l32);      // equal for rows l32 and 32 + l32
 #pragma unroll
-        for (int i = 0; i < C::VU; ++i) {
-            const int u = tid + i * C::THREADS;
-            vb[i] = (4 * (u % 16)) * (D * 2) + (u / 16) * 16;
-            vf[i] = (4 * (u % 8)) * (D * 4) + (u / 8) * 16;
-        }
+        for (int c = 0; c < D / 16; ++c) kread[c] = l32 * C::RB + 16 * ((2 * c + h) ^ fk);
+        const int G = lane >> 4, i = lane & 15;
+        const int vrow = 4 * h + (i >> 2);
+        const int cl = 2 * (G & 1) + ((i & 3) >> 1);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            vread[db] = vrow * C::RB + 16 * ((4 * db + cl) ^ swz_v<D>(vrow)) + 8 * (i & 1);
     }
 };
 
+// fp32 split tiles go through registers: K/V unit u = (row u/(D/4), 4 features)
 template <int D, int BQ>
-__device__ __forceinline__ void load_bf16(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                          const TileOffsets<D, BQ> &to, Staging<D, BQ> &st) {
-    using C = FC<D, BQ>;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < C::KU; ++i)
-        if (C::K_UNITS % C::THREADS == 0 || tid + i * C::THREADS < C::K_UNITS) st.k[i] = bload(rk, to.kb[i]);
-#pragma unroll
-    for (int i = 0; i < C::VU; ++i)
-        if (C::V_UNITS % C::THREADS == 0 || tid + i * C::THREADS < C::V_UNITS) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) st.v[i][r] = __builtin_amdgcn_raw_buffer_load_b128(rv, to.vb[i], r * (D * 2), 0);
-        }
-}
+struct Staging {
+    u32x4 k[FC<D, BQ>::SU];
+    u32x4 v[FC<D, BQ>::SU];
+};
 
 template <int D, int BQ>
-__device__ __forceinline__ void load_f32(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                         const TileOffsets<D, BQ> &to, Staging<D, BQ> &st) {
+__device__ __forceinline__ void load_split(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, Staging<D, BQ> &st) {
     using C = FC<D, BQ>;
-    const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < C::KU; ++i)
-        if (C::K_UNITS % C::THREADS == 0 || tid + i * C::THREADS < C::K_UNITS) st.k[i] = bload(rk, to.kf[i]);
-#pragma unroll
-    for (int i = 0; i < C::VU; ++i)
-        if (C::V_UNITS % C::THREADS == 0 || tid + i * C::THREADS < C::V_UNITS) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) st.v[i][r] = __builtin_amdgcn_raw_buffer_load_b128(rv, to.vf[i], r * (D * 4), 0);
-        }
+    for (int i = 0; i < C::SU; ++i) {
+        const int u = threadIdx.x + i * C::THREADS;
+        const int off = (u / (D / 4)) * (D * 4) + (u % (D / 4)) * 16;
+        st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+        st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    }
 }
-
-// V^T position of key 4g (the 4 keys 4g..4g+3 stay contiguous): bits 2 and 3 of
-// the key offset inside its group of 16 are swapped, so that the 8 keys a lane
-// contributes to one P^T operand are adjacent.
-__device__ __forceinline__ int vt_pos(int g) { return 16 * (g >> 2) + 4 * (((g & 1) << 1) | ((g >> 1) & 1)); }
 
 __device__ __forceinline__ bf16x4 bf16x4_of(float a, float b, float c, float d) {
     bf16x4 x;
@@ -214,78 +206,47 @@ __device__ __forceinline__ bf16x4 bf16x4_of(float a, float b, float c, float d) 
 }
 
 template <int D, int BQ>
-__device__ __forceinline__ void store_bf16(bf16 *buf, const Staging<D, BQ> &st) {
+__device__ __forceinline__ void store_split(unsigned char *stage, const Staging<D, BQ> &st) {
     using C = FC<D, BQ>;
-    const int tid = threadIdx.x;
-    bf16 *Ks = buf;
-    bf16 *Vt = buf + C::K_ELEMS;
 #pragma unroll
-    for (int i = 0; i < C::KU; ++i) {
-        const int u = tid + i * C::THREADS;
-        if (C::K_UNITS % C::THREADS == 0 || u < C::K_UNITS) {
-            const int row = u / (D / 8), ch = u % (D / 8);
-            *reinterpret_cast<u32x4 *>(Ks + row * C::KSTR + ch * 8) = st.k[i];
-        }
-    }
+    for (int i = 0; i < C::SU; ++i) {
+        const int u = threadIdx.x + i * C::THREADS;
+        const int row = u / (D / 4), c4 = u % (D / 4);
 #pragma unroll
-    for (int i = 0; i < C::VU; ++i) {
-        const int u = tid + i * C::THREADS;
-        if (C::V_UNITS % C::THREADS == 0 || u < C::V_UNITS) {
-            const int g = u % 16, c = u / 16;
-            const int pos = vt_pos(g);
+        for (int t = 0; t < 2; ++t) {
+            const u32x4 w = t == 0 ? st.k[i] : st.v[i];
+            const int pos = (c4 >> 1) ^ (t == 0 ? swz_k<D>(row) : swz_v<D>(row));
+            unsigned char *base = stage + t * C::TILE + 16 * pos + 8 * (c4 & 1);
+            float x[4], lo[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                // bf16 j of each row: 16-bit half (j & 1) of 32-bit word j / 2
-                const int sh = 16 * (j & 1);
-                u32x2 x;
-                x[0] = ((st.v[i][0][j >> 1] >> sh) & 0xffffu) | (((st.v[i][1][j >> 1] >> sh) & 0xffffu) << 16);
-                x[1] = ((st.v[i][2][j >> 1] >> sh) & 0xffffu) | (((st.v[i][3][j >> 1] >> sh) & 0xffffu) << 16);
-                *reinterpret_cast<u32x2 *>(Vt + (8 * c + j) * C::VSTR + pos) = x;
+            for (int e = 0; e < 4; ++e) {
+                x[e] = __uint_as_float(w[e]);
+                lo[e] = x[e] - (float)(bf16)x[e];
             }
+            *reinterpret_cast<bf16x4 *>(base + row * C::RB) = bf16x4_of(x[0], x[1], x[2], x[3]);
+            *reinterpret_cast<bf16x4 *>(base + (row + 32) * C::RB) = bf16x4_of(lo[0], lo[1], lo[2], lo[3]);
         }
     }
 }
 
+// 16 bytes per lane from a buffer straight into LDS at lds_base + 16 * lane.
+__device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char *lds_base, int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base, 16, voffset, 0, 0,
+                                             0);
+#endif
+}
+
+// One buffer->LDS piece per (i, tensor): 1 KB of the tile at the wave's slot.
 template <int D, int BQ>
-__device__ __forceinline__ void store_split(bf16 *buf, const Staging<D, BQ> &st) {
+__device__ __forceinline__ void load_direct(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                            unsigned char *stage, const Lanes<D, BQ> &ln, int wave) {
     using C = FC<D, BQ>;
-    const int tid = threadIdx.x;
-    bf16 *Ks = buf;
-    bf16 *Vt = buf + C::K_ELEMS;
 #pragma unroll
-    for (int i = 0; i < C::KU; ++i) {
-        const int u = tid + i * C::THREADS;
-        if (C::K_UNITS % C::THREADS == 0 || u < C::K_UNITS) {
-            const int row = u / (D / 4), c4 = u % (D / 4);
-            float x[4], lo[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[e] = __uint_as_float(st.k[i][e]);
-                lo[e] = x[e] - (float)(bf16)x[e];
-            }
-            *reinterpret_cast<bf16x4 *>(Ks + row * C::KSTR + c4 * 4) = bf16x4_of(x[0], x[1], x[2], x[3]);
-            *reinterpret_cast<bf16x4 *>(Ks + (row + 32) * C::KSTR + c4 * 4) = bf16x4_of(lo[0], lo[1], lo[2], lo[3]);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < C::VU; ++i) {
-        const int u = tid + i * C::THREADS;
-        if (C::V_UNITS % C::THREADS == 0 || u < C::V_UNITS) {
-            const int g = u % 8, c = u / 8;
-            const int pos = vt_pos(g);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float x[4], lo[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    x[r] = __uint_as_float(st.v[i][r][j]);
-                    lo[r] = x[r] - (float)(bf16)x[r];
-                }
-                bf16 *row = Vt + (4 * c + j) * C::VSTR;
-                *reinterpret_cast<bf16x4 *>(row + pos) = bf16x4_of(x[0], x[1], x[2], x[3]);
-                *reinterpret_cast<bf16x4 *>(row + pos + 32) = bf16x4_of(lo[0], lo[1], lo[2], lo[3]);
-            }
-        }
+    for (int i = 0; i < C::PPW; ++i) {
+        const int piece = (wave + C::WAVES * i) * 1024;
+        buffer_to_lds(rk, stage + piece, ln.ksrc[i]);
+        buffer_to_lds(rv, stage + C::TILE + piece, ln.vsrc[i]);
     }
 }
 
@@ -302,29 +263,29 @@ template <> struct Store4<float> {
     }
 };
 
-// Key/value rows and fp32 block means of one (b, h).
+// Key/value rows and residual tiles of one (b, h).
 template <typename T>
 struct HeadSrc {
     const T *k, *v;
-    const float *km, *vm;
-    int n_rows, n_means;
+    const bf16 *ks, *vs;      // split block means: 64-row tiles
+    int n_rows;
 };
 
-// Issue the global loads of tile t: a buffer resource starting at the tile's
-// first row and ending at the end of the head, so rows past the end read zero.
+// Start the loads of tile t into `stage`: direct for bf16 tiles, into `st` for
+// fp32 split tiles (stored by store_split once the current tile is done).
 template <typename T, int D, int BQ>
-__device__ __forceinline__ void issue_tile(const TileDesc &t, const HeadSrc<T> &hs, const TileOffsets<D, BQ> &to,
-                                           Staging<D, BQ> &st) {
+__device__ __forceinline__ void issue_tile(const TileDesc &t, const HeadSrc<T> &hs, const Lanes<D, BQ> &ln,
+                                           unsigned char *stage, int wave, Staging<D, BQ> &st) {
     if (t.kind == kResidual) {
-        const uint32_t bytes = (uint32_t)(hs.n_means - t.row0) * (D * 4);
-        load_f32<D, BQ>(buffer_rsrc(hs.km + (size_t)t.row0 * D, bytes), buffer_rsrc(hs.vm + (size_t)t.row0 * D, bytes),
-                        to, st);
+        const size_t off = (size_t)(t.row0 / 32) * kTile * D;
+        load_direct<D, BQ>(buffer_rsrc(hs.ks + off, kTile * D * 2), buffer_rsrc(hs.vs + off, kTile * D * 2), stage, ln,
+                           wave);
     } else {
         const uint32_t bytes = (uint32_t)(hs.n_rows - t.row0) * (D * sizeof(T));
         const auto rk = buffer_rsrc(hs.k + (size_t)t.row0 * D, bytes);
         const auto rv = buffer_rsrc(hs.v + (size_t)t.row0 * D, bytes);
-        if constexpr (sizeof(T) == 2) load_bf16<D, BQ>(rk, rv, to, st);
-        else load_f32<D, BQ>(rk, rv, to, st);
+        if constexpr (sizeof(T) == 2) load_direct<D, BQ>(rk, rv, stage, ln, wave);
+        else load_split<D, BQ>(rk, rv, st);
     }
 }
 
@@ -335,40 +296,44 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
     FlashArgs a) {
     using C = FC<D, BQ>;
     constexpr bool kF32 = sizeof(T) == 4;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    bf16 *lds = reinterpret_cast<bf16 *>(smem_raw);
+    __shared__ __attribute__((aligned(1024))) unsigned char lds0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds1[C::STAGE];
 
     const int item = kSparse ? __builtin_amdgcn_readfirstlane(a.work_order[blockIdx.x]) : (int)blockIdx.x;
     const int bh = item / a.n_qb;
     const int I = item - bh * a.n_qb;
     const int lane = lane_id();
     const int h = lane >> 5, l32 = lane & 31;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const size_t head = (size_t)bh * a.N * D;
     const int qrow = I * a.block_q + wave * 32 + l32;
     const bool row_ok = qrow < a.N;
 
-    // this wave's 32 query rows, as B operands (lane: row l32, features 16c + 8h + 0..7);
-    // fp32 inputs also keep the bf16 remainder of each query element
+    Lanes<D, BQ> ln;
+    ln.init(wave, lane);
+
+    // this wave's 32 query rows as B operands: in step c the lane holds features
+    // 16c + 8h + 0..7 of row l32; fp32 inputs also keep the bf16 remainder
     bf16x8 qf[D / 16];
     bf16x8 ql[kF32 ? D / 16 : 1];
     {
         const bf16x8 zero = {};
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
+        for (int c2 = 0; c2 < D / 16; ++c2) {
+            const size_t off = head + (size_t)qrow * D + 16 * c2 + 8 * h;
             if constexpr (kF32) {
                 float x[8];
-                if (row_ok) Ld8<float>::load_f32(reinterpret_cast<const float *>(q) + head + (size_t)qrow * D + 16 * c + 8 * h, x);
+                if (row_ok) Ld8<float>::load_f32(reinterpret_cast<const float *>(q) + off, x);
                 else
 #pragma unroll
                     for (int e = 0; e < 8; ++e) x[e] = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    qf[c][e] = (bf16)x[e];
-                    ql[c][e] = (bf16)(x[e] - (float)qf[c][e]);
+                    qf[c2][e] = (bf16)x[e];
+                    ql[c2][e] = (bf16)(x[e] - (float)qf[c2][e]);
                 }
             } else {
-                qf[c] = row_ok ? Ld8<T>::load(q + head + (size_t)qrow * D + 16 * c + 8 * h) : zero;
+                qf[c2] = row_ok ? Ld8<T>::load(q + off) : zero;
             }
         }
     }
@@ -383,22 +348,20 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
         ts.list = a.kv_idx + row_id * a.kv_idx_cap;
         ts.cnt = __builtin_amdgcn_readfirstlane(a.kv_count[row_id]);
         ts.mask = a.kv_mask + row_id * a.mask_words;
-        ts.n_rt = a.residual ? a.mask_words : 0;
+        ts.n_rt = (a.residual && ts.cnt < a.n_kb) ? a.mask_words : 0;   // all kept: no residual
     } else {
         ts.list = nullptr;
         ts.mask = nullptr;
         ts.cnt = 0;
         ts.n_rt = 0;
     }
+    ts.prime();
     HeadSrc<T> hs;
     hs.k = k + head;
     hs.v = v + head;
-    hs.km = kSparse ? a.k_mean + (size_t)bh * a.n_kb * D : nullptr;
-    hs.vm = kSparse ? a.v_mean + (size_t)bh * a.n_kb * D : nullptr;
+    hs.ks = kSparse ? a.kv_split + (size_t)bh * 2 * a.mask_words * kTile * D : nullptr;
+    hs.vs = kSparse ? hs.ks + (size_t)a.mask_words * kTile * D : nullptr;
     hs.n_rows = a.N;
-    hs.n_means = a.n_kb;
-    TileOffsets<D, BQ> to;
-    to.init();
     const float lg_bk = log2f((float)a.block_k);
     const float lg_last = log2f((float)(a.N - (a.n_kb - 1) * a.block_k));
 
@@ -411,34 +374,36 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
     TileDesc cur, nxt;
     bool have = ts.next(cur, a);
     if (have) {
-        issue_tile<T, D, BQ>(cur, hs, to, st);
-        if (cur.kind == kExact) store_bf16<D, BQ>(lds, st);
-        else store_split<D, BQ>(lds, st);
+        issue_tile<T, D, BQ>(cur, hs, ln, lds0, wave, st);
+        if constexpr (kF32) {
+            if (cur.kind == kExactSplit) store_split<D, BQ>(lds0, st);
+        }
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this thread's loads have landed
     __syncthreads();
-    int buf = 0;
-    while (have) {
+    // One pipeline step: compute the tile in cur_stage while the next tile streams
+    // into nxt_stage.  The loop below alternates two distinct LDS arrays so that
+    // every LDS access names its stage statically: the compiler can then see that
+    // reads of the current stage do not alias the buffer->LDS loads in flight.
+    auto step = [&](const unsigned char *cur_stage, unsigned char *nxt_stage) -> bool {
         const bool have_next = ts.next(nxt, a);
-        // Nothing is in flight here (the previous tile's loads were consumed by
-        // its LDS stores).  Saying so explicitly keeps the compiler from placing
-        // its loop-entry wait after the prefetch below, which would expose the
-        // prefetch latency on every tile.
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt/lgkmcnt untouched
-        if (have_next) issue_tile<T, D, BQ>(nxt, hs, to, st);
-        const bf16 *Ks = lds + buf * C::BUF;
-        const bf16 *Vt = Ks + C::K_ELEMS;
+        // Nothing is in flight here.  Saying so explicitly keeps the compiler from
+        // placing its loop-entry wait after the prefetch below.
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        if (have_next) issue_tile<T, D, BQ>(nxt, hs, ln, nxt_stage, wave, st);
+        const unsigned char *Ks = cur_stage;
+        const unsigned char *Vs = cur_stage + C::TILE;
 
         // S^T for LDS key rows 0..31 (s[0]) and 32..63 (s[1])
         f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-            const bf16x8 k0 = *reinterpret_cast<const bf16x8 *>(Ks + l32 * C::KSTR + 16 * c + 8 * h);
-            const bf16x8 k1 = *reinterpret_cast<const bf16x8 *>(Ks + (32 + l32) * C::KSTR + 16 * c + 8 * h);
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[c], s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[c], s[1], 0, 0, 0);
-            if constexpr (kF32) s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ql[c], s[0], 0, 0, 0);
+        for (int c2 = 0; c2 < D / 16; ++c2) {
+            const bf16x8 k0 = *reinterpret_cast<const bf16x8 *>(Ks + ln.kread[c2]);
+            const bf16x8 k1 = *reinterpret_cast<const bf16x8 *>(Ks + ln.kread[c2] + 32 * C::RB);
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[c2], s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[c2], s[1], 0, 0, 0);
+            if constexpr (kF32) s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ql[c2], s[0], 0, 0, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);
 
         // accumulator register r of lane (h, l32) in block b holds LDS key row
         // 32b + 8(r/4) + 4h + r%4
@@ -514,27 +479,37 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
             pb[3] = pb[1];
         }
         l_run += ps0 + ps1;
-        __builtin_amdgcn_sched_barrier(0);
 
+        // O^T += V^T P^T: the V^T operand of step j (keys 16j..16j+15) comes from two
+        // transposing reads: keys 16j + 4h + e and 16j + 8 + 4h + e (e = 0..3)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const bf16x8 va = *reinterpret_cast<const bf16x8 *>(Vt + (32 * db + l32) * C::VSTR + 16 * j + 8 * h);
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(Vs + ln.vread[db] + 16 * j * C::RB));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(Vs + ln.vread[db] + (16 * j + 8) * C::RB));
+                // whole-vector reinterpretation: per-element bit casts of __bf16 vector
+                // elements are mis-compiled by this toolchain (splat of element 0)
+                const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                const bf16x8 va = __builtin_bit_cast(bf16x8, both);
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[j], acc[db], 0, 0, 0);
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
 
-        if (have_next) {
-            bf16 *dst = lds + (buf ^ 1) * C::BUF;
-            if (nxt.kind == kExact) store_bf16<D, BQ>(dst, st);
-            else store_split<D, BQ>(dst, st);
+        if constexpr (kF32) {
+            if (have_next && nxt.kind == kExactSplit) store_split<D, BQ>(nxt_stage, st);
         }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the next tile has landed in LDS
         __syncthreads();
-        buf ^= 1;
         cur = nxt;
-        have = have_next;
+        return have_next;
+    };
+    while (have) {
+        have = step(lds0, lds1);
+        if (!have) break;
+        have = step(lds1, lds0);
     }
 
     // epilogue: O^T accumulator register r of block db holds feature 32db + 8(r/4) + 4h + r%4
@@ -557,16 +532,9 @@ template <typename T, int D, int BQ, bool kSparse>
 static hipError_t launch_flash_t(const void *q, const void *k, const void *v, void *o,
                                  const FlashArgs &a, int BH, hipStream_t st) {
     using C = FC<D, BQ>;
-    static bool attr_set = false;
     auto kern = flash_kernel<T, D, BQ, kSparse>;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)C::LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
     const int items = BH * a.n_qb;
-    hipLaunchKernelGGL(kern, dim3(items), dim3(C::THREADS), C::LDS, st, (const T *)q, (const T *)k,
+    hipLaunchKernelGGL(kern, dim3(items), dim3(C::THREADS), 0, st, (const T *)q, (const T *)k,
                        (const T *)v, (T *)o, a);
     return hipGetLastError();
 }

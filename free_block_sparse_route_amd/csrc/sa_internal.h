@@ -12,8 +12,9 @@ constexpr size_t kSelectLdsBudget = 64 * 1024;   // proxy rows of one select wor
 constexpr int kMaxKeyBlocks = 16384 - 16;       // n_kb limit implied by that budget at G = 1
 
 struct PoolArgs {
-    int N, block_q, block_k, n_qb, n_kb;
+    int N, block_q, block_k, n_qb, n_kb, words;
     float *q_mean, *k_mean, *v_mean;
+    bf16 *kv_split;                      // [BH][2][words][64][D] hi/lo residual tiles
 };
 
 struct SelectArgs {
@@ -33,7 +34,7 @@ struct FlashArgs {
     int residual;                        // fold dropped blocks (route present)
     const int32_t *kv_count, *kv_idx, *work_order;
     const uint32_t *kv_mask;
-    const float *k_mean, *v_mean;        // fp32 block means [B,H,n_kb,d]
+    const bf16 *kv_split;                // [BH][2][words][64][D] hi/lo residual tiles
     float *lse;                          // nullable
 };
 

@@ -69,6 +69,20 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const T *__restrict_
         const float m = s / (float)cnt;
         float *dst = which == 0 ? a.q_mean : which == 1 ? a.k_mean : a.v_mean;
         dst[((size_t)bh * nb + J) * D + col] = m;
+        if (which != 0) {
+            // residual tile rows: block J -> group J/32, row J%32 (bf16 of the mean)
+            // and row 32 + J%32 (bf16 of what that rounding left)
+            bf16 *sp = a.kv_split + (((size_t)bh * 2 + (which - 1)) * a.words + J / 32) * 64 * D;
+            const bf16 hi = (bf16)m;
+            sp[(size_t)(J % 32) * D + col] = hi;
+            sp[(size_t)(32 + J % 32) * D + col] = (bf16)(m - (float)hi);
+            if (J == nb - 1) {
+                for (int r = J % 32 + 1; r < 32; ++r) {
+                    sp[(size_t)r * D + col] = (bf16)0.f;
+                    sp[(size_t)(32 + r) * D + col] = (bf16)0.f;
+                }
+            }
+        }
     }
 }
 

@@ -113,6 +113,11 @@ enum {
     SA_BUF_Q_MEAN,        /* fp32 [B,H,n_qb,d]           query block means                  */
     SA_BUF_K_MEAN,        /* fp32 [B,H,n_kb,d]           key block means                    */
     SA_BUF_V_MEAN,        /* fp32 [B,H,n_kb,d]           value block means                  */
+    SA_BUF_KV_SPLIT,      /* bf16 [B,H,2,words,64,d]     residual tiles: for each group of 32
+                                                         key blocks, 32 rows of block means
+                                                         rounded to bf16, then 32 rows of their
+                                                         bf16 remainders (keys, then values);
+                                                         rows past n_kb are zero            */
     SA_BUF_ROW_STATS,     /* fp32 [B,H,n_qb,2]           max_J s_IJ and log-sum-exp_J s_IJ  */
     SA_BUF_COST,          /* int32 [B,H,n_qb]            key/value tiles the forward visits */
     SA_BUF_WORK_ORDER,    /* int32 [W]                   work items, most expensive first   */
@@ -128,6 +133,7 @@ typedef struct sa_route {
     float    *q_mean;
     float    *k_mean;
     float    *v_mean;
+    void     *kv_split;
     float    *row_stats;
     int32_t  *cost;
     int32_t  *work_order;
