@@ -21,9 +21,8 @@ SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_CAPACITY, SA_ERR_HIP = 0, 
 SA_BF16, SA_F32 = 0, 1
 RELATIVE, ABSOLUTE = 0, 1
 FLAG_NO_RESIDUAL = 1
-SA_SCHED_INTS = 8192
 BUFFERS = ("kv_count", "kv_idx", "kv_mask", "q_mean", "k_mean", "v_mean", "kv_split", "row_stats", "cost",
-           "work_order", "sched")
+           "work_order")
 
 
 class SaParams(ctypes.Structure):
@@ -149,7 +148,6 @@ class Route:
         self.row_stats = torch.empty((B, H, self.n_qb, 2), dtype=torch.float32, **e)
         self.cost = torch.empty((B, H, self.n_qb), dtype=torch.int32, **e)
         self.work_order = torch.empty((B * H * self.n_qb,), dtype=torch.int32, **e)
-        self.sched = torch.empty((SA_SCHED_INTS,), dtype=torch.int32, **e)
         for name, nbytes in zip(BUFFERS, sizes):
             t = getattr(self, name)
             if t.numel() * t.element_size() != nbytes:

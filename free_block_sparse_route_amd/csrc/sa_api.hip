@@ -117,7 +117,6 @@ sa_status sparse_attn_route_sizes(const sa_params *p, int32_t kv_idx_cap, size_t
     bytes[SA_BUF_ROW_STATS] = rows * 2 * 4;
     bytes[SA_BUF_COST] = rows * 4;
     bytes[SA_BUF_WORK_ORDER] = rows * 4;
-    bytes[SA_BUF_SCHED] = (size_t)SA_SCHED_INTS * 4;
     return SA_OK;
 }
 
@@ -132,7 +131,7 @@ sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, co
         (s = check_ptr(r->kv_mask, "route.kv_mask")) || (s = check_ptr(r->q_mean, "route.q_mean")) ||
         (s = check_ptr(r->k_mean, "route.k_mean")) || (s = check_ptr(r->v_mean, "route.v_mean")) ||
         (s = check_ptr(r->kv_split, "route.kv_split")) || (s = check_ptr(r->row_stats, "route.row_stats")) || (s = check_ptr(r->cost, "route.cost")) ||
-        (s = check_ptr(r->work_order, "route.work_order")) || (s = check_ptr(r->sched, "route.sched")))
+        (s = check_ptr(r->work_order, "route.work_order")))
         return s;
     if (r->kv_idx_cap < min_cap(p))
         return fail(SA_ERR_CAPACITY, "route.kv_idx_cap %d < required %d", r->kv_idx_cap, min_cap(p));
@@ -157,7 +156,7 @@ sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, co
     sa_.ln_tau = p->tau > 0.f ? (float)log((double)p->tau) : -INFINITY;
     sa_.q_mean = r->q_mean; sa_.k_mean = r->k_mean;
     sa_.kv_count = r->kv_count; sa_.kv_idx = r->kv_idx; sa_.cost = r->cost;
-    sa_.work_order = r->work_order; sa_.hist = r->sched; sa_.kv_mask = r->kv_mask;
+    sa_.work_order = r->work_order; sa_.kv_mask = r->kv_mask;
     sa_.row_stats = r->row_stats;
     e = sa::launch_select(p->d, sa_, (int)d.BH, st);
     if (e != hipSuccess) return hip_fail(e, "route: select launch");

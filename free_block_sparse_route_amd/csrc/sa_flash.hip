@@ -289,17 +289,15 @@ __device__ __forceinline__ void issue_tile(const TileDesc &t, const HeadSrc<T> &
     }
 }
 
-// kSparse: kept-list and residual tiles from a route; otherwise every key tile (dense).
+// One work item: the query block I of head bh = item / n_qb, from its first
+// tile to its output rows.  kSparse: kept-list and residual tiles from a route;
+// otherwise every key tile (dense).
 template <typename T, int D, int BQ, bool kSparse>
-__global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_per_eu(FC<D, BQ>::WPE, FC<D, BQ>::WPE))) void flash_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
-    FlashArgs a) {
+__device__ __forceinline__ void run_item(int item, const T *__restrict__ q, const T *__restrict__ k,
+                                         const T *__restrict__ v, T *__restrict__ o, const FlashArgs &a,
+                                         unsigned char *lds0, unsigned char *lds1) {
     using C = FC<D, BQ>;
     constexpr bool kF32 = sizeof(T) == 4;
-    __shared__ __attribute__((aligned(1024))) unsigned char lds0[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char lds1[C::STAGE];
-
-    const int item = kSparse ? __builtin_amdgcn_readfirstlane(a.work_order[blockIdx.x]) : (int)blockIdx.x;
     const int bh = item / a.n_qb;
     const int I = item - bh * a.n_qb;
     const int lane = lane_id();
@@ -528,14 +526,45 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
     }
 }
 
+// Workgroup i runs on GPU die i % 8: the dispatcher deals workgroups to the 8
+// dies (XCDs) in turn.  In each group of 8 * kDieRun consecutive workgroups, die
+// x takes the kDieRun consecutive work positions x * kDieRun + 0..kDieRun-1 of
+// the group, so that neighbouring query blocks, which keep mostly the same key
+// blocks, meet in one die's L2, while the order of the work list holds at the
+// scale of a group.  The last, partial group keeps the plain order.
+constexpr int kDieRun = 16;
+
+__device__ __forceinline__ int grid_position(int i, int W) {
+    constexpr int kGroup = 8 * kDieRun;
+    const int base = i - i % kGroup;
+    if (base + kGroup > W) return i;
+    const int r = i - base;
+    return base + (r & 7) * kDieRun + (r >> 3);
+}
+
+// One workgroup per work item (query block); kSparse takes the item from the
+// route's work order, the dense path in plain order.
+template <typename T, int D, int BQ, bool kSparse>
+__global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_per_eu(FC<D, BQ>::WPE, FC<D, BQ>::WPE))) void flash_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
+    FlashArgs a) {
+    using C = FC<D, BQ>;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds1[C::STAGE];
+    const int p = grid_position(blockIdx.x, a.n_items);
+    const int item = kSparse ? __builtin_amdgcn_readfirstlane(a.work_order[p]) : p;
+    run_item<T, D, BQ, kSparse>(item, q, k, v, o, a, lds0, lds1);
+}
+
 template <typename T, int D, int BQ, bool kSparse>
 static hipError_t launch_flash_t(const void *q, const void *k, const void *v, void *o,
                                  const FlashArgs &a, int BH, hipStream_t st) {
     using C = FC<D, BQ>;
     auto kern = flash_kernel<T, D, BQ, kSparse>;
-    const int items = BH * a.n_qb;
-    hipLaunchKernelGGL(kern, dim3(items), dim3(C::THREADS), 0, st, (const T *)q, (const T *)k,
-                       (const T *)v, (T *)o, a);
+    FlashArgs args = a;
+    args.n_items = BH * a.n_qb;
+    hipLaunchKernelGGL(kern, dim3(args.n_items), dim3(C::THREADS), 0, st, (const T *)q, (const T *)k,
+                       (const T *)v, (T *)o, args);
     return hipGetLastError();
 }
 

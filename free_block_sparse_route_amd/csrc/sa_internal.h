@@ -23,7 +23,7 @@ struct SelectArgs {
     int tau_mode, max_keep, min_keep, n_prefix;
     float scale, ln_tau;                 // ln_tau = -inf when tau == 0
     const float *q_mean, *k_mean;
-    int32_t *kv_count, *kv_idx, *cost, *work_order, *hist;
+    int32_t *kv_count, *kv_idx, *cost, *work_order;
     uint32_t *kv_mask;
     float *row_stats;
 };
@@ -33,6 +33,7 @@ struct FlashArgs {
     float scale_log2;                    // logit scale times log2(e)
     int residual;                        // fold dropped blocks (route present)
     const int32_t *kv_count, *kv_idx, *work_order;
+    int n_items;                         // B * H * n_qb
     const uint32_t *kv_mask;
     const bf16 *kv_split;                // [BH][2][words][64][D] hi/lo residual tiles
     float *lse;                          // nullable

@@ -12,9 +12,14 @@
 //         tau, applies the top-k cap or floor by an exact k-th-largest search
 //         over order-preserving integer keys, forces the dense prefix and
 //         compacts the kept blocks into an ascending index list and bit mask.
-// sched   counting sort of work items by cost (tiles the attention kernel
-//         will visit), most expensive first, so that the hardware dispatcher's
-//         in-order issue behaves as longest-processing-time-first scheduling.
+// order   work order for the attention kernel: a stable counting sort of the
+//         query blocks by cost band floor(log2(cost)), cost = tiles the
+//         attention kernel will visit, highest band first.  The dispatcher
+//         issues workgroups roughly in order, so expensive blocks start early
+//         and cheap ones fill the end (close to longest-processing-time-first
+//         scheduling, which matters where a row may keep most key blocks),
+//         while within a band the blocks stay in ascending order: neighbouring
+//         query blocks keep mostly the same key blocks and meet in the L2.
 #include "sa_device.h"
 #include "sa_internal.h"
 
@@ -22,7 +27,8 @@ namespace sa {
 
 constexpr int kPoolThreads = 256;
 constexpr int kSelectThreads = 256;
-constexpr int kHistBins = SA_SCHED_INTS / 2;
+constexpr int kOrderThreads = 512;
+constexpr int kBands = 32;               // floor(log2(cost)) of a non-negative int32
 
 // --------------------------------------------------------------------- pool
 template <typename T, int D>
@@ -178,7 +184,6 @@ __device__ void select_row(const float *S, int bh, int I, const SelectArgs &a) {
         a.row_stats[row * 2 + 0] = m;
         a.row_stats[row * 2 + 1] = lse;
         a.cost[row] = tiles;
-        atomicAdd(&a.hist[min(tiles, kHistBins - 1)], 1);
     }
 }
 
@@ -220,39 +225,46 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     for (int g = wave; g < g_cnt; g += kSelectThreads / kWave) select_row(S + g * n, bh, I0 + g, a);
 }
 
-// --------------------------------------------------------------------- sched
-__global__ void sched_zero_kernel(int32_t *hist) {
-    for (int i = threadIdx.x; i < SA_SCHED_INTS; i += blockDim.x) hist[i] = 0;
-}
+// --------------------------------------------------------------------- order
+__device__ __forceinline__ int cost_band(int32_t c) { return c > 1 ? 31 - __clz(c) : 0; }
 
-// offsets[b] = number of items with a larger cost bin (descending order).
-__global__ __launch_bounds__(256) void sched_scan_kernel(int32_t *sched) {
-    const int32_t *hist = sched;
-    int32_t *offs = sched + kHistBins;
-    constexpr int PER = kHistBins / 256;
-    __shared__ int32_t part[256];
+// One workgroup.  Thread t owns the items of one contiguous chunk; cnt[r][t]
+// counts its items in row r = kBands-1-band (row 0: highest band).  The
+// exclusive prefix over cnt in (row, thread) order is then where thread t
+// writes its first item of row r, which makes the sort stable.
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *cost, int32_t *work_order, int W) {
+    __shared__ int32_t cnt[kBands * kOrderThreads];
+    __shared__ int32_t part[kOrderThreads];
     const int t = threadIdx.x;
-    // thread t owns bins [kHistBins - (t+1)*PER, kHistBins - t*PER), walked downwards
-    int s = 0;
-    for (int i = 0; i < PER; ++i) s += hist[kHistBins - 1 - (t * PER + i)];
-    part[t] = s;
+    const int chunk = (W + kOrderThreads - 1) / kOrderThreads;
+    const int i0 = min(W, t * chunk), i1 = min(W, i0 + chunk);
+    for (int r = 0; r < kBands; ++r) cnt[r * kOrderThreads + t] = 0;
+    for (int i = i0; i < i1; ++i) ++cnt[(kBands - 1 - cost_band(cost[i])) * kOrderThreads + t];
     __syncthreads();
-    int before = 0;
-    for (int u = 0; u < t; ++u) before += part[u];
-    for (int i = 0; i < PER; ++i) {
-        const int b = kHistBins - 1 - (t * PER + i);
-        offs[b] = before;
-        before += hist[b];
+    // thread t scans the kBands consecutive entries [t*kBands, (t+1)*kBands) of cnt
+    constexpr int kPer = kBands;   // kBands * kOrderThreads entries / kOrderThreads threads
+    int32_t *mine = cnt + t * kPer;
+    int sum = 0;
+    for (int e = 0; e < kPer; ++e) sum += mine[e];
+    part[t] = sum;
+    __syncthreads();
+    for (int off = 1; off < kOrderThreads; off <<= 1) {       // inclusive scan of part
+        const int v = t >= off ? part[t - off] : 0;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
     }
-}
-
-__global__ void sched_scatter_kernel(const int32_t *cost, int32_t *sched, int32_t *work_order,
-                                     int n_items) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n_items) return;
-    const int b = min(cost[i], kHistBins - 1);
-    const int pos = atomicAdd(&sched[kHistBins + b], 1);
-    work_order[pos] = i;
+    int run = t > 0 ? part[t - 1] : 0;
+    for (int e = 0; e < kPer; ++e) {
+        const int c = mine[e];
+        mine[e] = run;
+        run += c;
+    }
+    __syncthreads();
+    for (int i = i0; i < i1; ++i) {
+        const int slot = (kBands - 1 - cost_band(cost[i])) * kOrderThreads + t;
+        work_order[cnt[slot]++] = i;
+    }
 }
 
 // --------------------------------------------------------------------- launch
@@ -305,15 +317,10 @@ static hipError_t launch_select_d(const SelectArgs &a, int G, int BH, hipStream_
 hipError_t launch_select(int D, const SelectArgs &a, int BH, hipStream_t st) {
     const int G = select_group(a.n_kb, D, a.n_qb);
     hipError_t e = hipSuccess;
-    hipLaunchKernelGGL(sched_zero_kernel, dim3(1), dim3(256), 0, st, a.hist);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     e = D == 64 ? launch_select_d<64>(a, G, BH, st) : launch_select_d<128>(a, G, BH, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(256), 0, st, a.hist);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int n_items = BH * a.n_qb;
-    hipLaunchKernelGGL(sched_scatter_kernel, dim3((n_items + 255) / 256), dim3(256), 0, st,
-                       (const int32_t *)a.cost, a.hist, a.work_order, n_items);
+    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, st, (const int32_t *)a.cost, a.work_order,
+                       BH * a.n_qb);
     return hipGetLastError();
 }
 

@@ -120,11 +120,12 @@ enum {
                                                          rows past n_kb are zero            */
     SA_BUF_ROW_STATS,     /* fp32 [B,H,n_qb,2]           max_J s_IJ and log-sum-exp_J s_IJ  */
     SA_BUF_COST,          /* int32 [B,H,n_qb]            key/value tiles the forward visits */
-    SA_BUF_WORK_ORDER,    /* int32 [W]                   work items, most expensive first   */
-    SA_BUF_SCHED,         /* int32 [SA_SCHED_INTS]       schedule scratch                   */
+    SA_BUF_WORK_ORDER,    /* int32 [W]                   work items b*H*n_qb + h*n_qb + I
+                                                         by cost band floor(log2(cost)),
+                                                         highest band first, ascending item
+                                                         within a band                      */
     SA_ROUTE_NBUF
 };
-#define SA_SCHED_INTS 8192
 
 typedef struct sa_route {
     int32_t  *kv_count;
@@ -137,7 +138,6 @@ typedef struct sa_route {
     float    *row_stats;
     int32_t  *cost;
     int32_t  *work_order;
-    int32_t  *sched;
     int32_t   kv_idx_cap;     /* row length of kv_idx, >= sparse_attn_kv_idx_cap(p) */
 } sa_route;
 

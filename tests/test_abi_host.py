@@ -33,9 +33,9 @@ def test_struct_layout_matches_c(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "sparse_attn.h"\n'
-        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %d %d\\n\", sizeof(sa_params), sizeof(sa_route),"
-        " offsetof(sa_params, flags), offsetof(sa_route, kv_idx_cap), offsetof(sa_route, sched),"
-        " offsetof(sa_params, scale), SA_ROUTE_NBUF, SA_SCHED_INTS);return 0;}\n")
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %d\\n\", sizeof(sa_params), sizeof(sa_route),"
+        " offsetof(sa_params, flags), offsetof(sa_route, kv_idx_cap), offsetof(sa_route, work_order),"
+        " offsetof(sa_params, scale), SA_ROUTE_NBUF);return 0;}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
                    check=True)
@@ -45,10 +45,9 @@ def test_struct_layout_matches_c(tmp_path):
     assert vals[1] == ctypes.sizeof(B.SaRoute)
     assert vals[2] == B.SaParams.flags.offset
     assert vals[3] == B.SaRoute.kv_idx_cap.offset
-    assert vals[4] == B.SaRoute.sched.offset
+    assert vals[4] == B.SaRoute.work_order.offset
     assert vals[5] == B.SaParams.scale.offset
     assert vals[6] == len(B.BUFFERS)
-    assert vals[7] == B.SA_SCHED_INTS
 
 
 def params(**kw):
@@ -92,7 +91,7 @@ def test_route_sizes_wan13b():
     assert s["kv_idx"] == 12 * 256 * 256 * 4
     assert s["kv_mask"] == 12 * 256 * 8 * 4
     assert s["k_mean"] == 12 * 256 * 128 * 4
-    assert s["sched"] == B.SA_SCHED_INTS * 4
+    assert s["work_order"] == 12 * 256 * 4
     with pytest.raises(B.SparseAttnError) as e:
         B.route_sizes(p, cap - 1)
     assert e.value.status == B.SA_ERR_CAPACITY

@@ -198,14 +198,15 @@ def test_side_stream():
     assert torch.equal(O, O0)
 
 
-def test_work_order_is_cost_sorted_permutation():
+def test_work_order_by_cost_band():
+    """Forward schedule written by route: the cost of each query block, and the items
+    sorted stably by cost band floor(log2(cost)), highest band first."""
     w = S.small("sched", 1, 4, 128, (4, 8, 32), 128, 64, 0.01)
+    say(f"[case] schedule {w.name} H{w.H} N{w.N}")
     _, _, _, Q, K, V = make(w)
-    rt, _, _ = run_gpu(Q, K, V, cfg_for(w))
+    rt, O1, _ = run_gpu(Q, K, V, cfg_for(w))
     wo = rt.work_order.cpu().numpy()
-    cost = rt.cost.cpu().numpy().ravel()
-    assert np.array_equal(np.sort(wo), np.arange(wo.size))
-    assert (np.diff(cost[wo]) <= 0).all()
+    cost = rt.cost.cpu().numpy().ravel().astype(np.int64)
     # cost = 64-token tiles of kept blocks + one residual tile per 32 pooled blocks
     # holding a dropped block
     mask = rt.mask().cpu().numpy().reshape(-1, rt.n_kb)
@@ -216,3 +217,22 @@ def test_work_order_is_cost_sorted_permutation():
     pad[:, : rt.n_kb] = ~mask
     tiles += pad.reshape(mask.shape[0], -1, 32).any(axis=2).sum(axis=1)
     assert np.array_equal(cost, tiles)
+    band = np.floor(np.log2(np.maximum(cost, 1))).astype(np.int64)
+    assert len(np.unique(band)) > 1          # the case exercises more than one band
+    assert np.array_equal(wo, np.lexsort((np.arange(cost.size), -band)))
+    # the order is a pure function of the costs: a second route gives the same list
+    rt2 = sa().route(Q, K, V, cfg_for(w))
+    torch.cuda.synchronize()
+    assert torch.equal(rt2.work_order, rt.work_order)
+
+
+def test_work_order_many_items():
+    """More items than the ordering workgroup has threads, with ragged chunks."""
+    w = S.small("sched_many", 2, 6, 64, (5, 12, 45), 64, 64, 0.02)
+    say(f"[case] schedule {w.name} B{w.B} H{w.H} N{w.N}")
+    _, _, _, Q, K, V = make(w)
+    rt, _, _ = run_gpu(Q, K, V, cfg_for(w))
+    cost = rt.cost.cpu().numpy().ravel().astype(np.int64)
+    assert cost.size > 512 and cost.size % 512
+    band = np.floor(np.log2(np.maximum(cost, 1))).astype(np.int64)
+    assert np.array_equal(rt.work_order.cpu().numpy(), np.lexsort((np.arange(cost.size), -band)))
