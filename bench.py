@@ -43,8 +43,13 @@ def parse():
     ap.add_argument("--tau-mode", choices=("relative", "absolute"), default="relative")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain device copy of 1 GiB (for scaling HBM counters)")
+    ap.add_argument("--with-copy", action="store_true",
+                    help="after the bench, run a plain 1 GiB device copy twice (scale of the HBM counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/flash_<workload>_<tau-mode>_traffic.{json,md} from the counter "
+                         "collections of two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of this "
+                         "script with --with-copy, then exit")
+    ap.add_argument("--pmc-command", default="", help="the command the counter runs used (recorded)")
     return ap.parse_args()
 
 
@@ -64,16 +69,78 @@ def load_traffic(workload: str, tau_mode: str):
     return rec.get("bytes_per_launch")
 
 
+COPY_BYTES = 1 << 30
+
+
 def copy_calibration():
+    """A plain device copy of COPY_BYTES (reads and writes that many bytes), twice."""
     import torch
-    n = 1 << 30
-    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1)
-    for _ in range(5):
+    for _ in range(2):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+
+
+def _pmc_rows(path: str, counter: str):
+    import csv
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    if not rows:
+        raise SystemExit(f"{path}: no {counter} rows")
+    return rows
+
+
+def _mean_kib(rows, pred):
+    vals = [float(r["Counter_Value"]) for r in rows if pred(r)]
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def pmc_summary(args):
+    """HBM traffic of the sparse forward kernel per launch from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads for
+    the plain 1 GiB copy in the same run."""
+    fetch_rows = _pmc_rows(args.pmc_summary[0], "FETCH_SIZE")
+    write_rows = _pmc_rows(args.pmc_summary[1], "WRITE_SIZE")
+    is_flash = lambda r: "flash_kernel" in r["Kernel_Name"] and "Lb1E" in r["Kernel_Name"]
+    # the copy: the dispatch of a kernel named for copying whose counter is the largest
+    def copy_kib(rows):
+        cands = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
+        if not cands:
+            raise SystemExit("no copy dispatch in the counter collection (run with --with-copy)")
+        return max(cands)
+    f_kib, nf = _mean_kib(fetch_rows, is_flash)
+    w_kib, nw = _mean_kib(write_rows, is_flash)
+    if not nf or not nw:
+        raise SystemExit("no sparse flash_kernel dispatch in the counter collections")
+    copy_f, copy_w = copy_kib(fetch_rows), copy_kib(write_rows)
+    scale_f = COPY_BYTES / (copy_f * 1024.0)
+    scale_w = COPY_BYTES / (copy_w * 1024.0)
+    rd = f_kib * 1024.0 * scale_f
+    wr = w_kib * 1024.0 * scale_w
+    rec = {"kernel": "flash_kernel (sparse forward with residual)", "workload": args.workload,
+           "tau_mode": args.tau_mode, "flash_source_sha256_16": source_hash(),
+           "bytes_per_launch": rd + wr, "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+           "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
+           "copy_fetch_kib": copy_f, "copy_write_kib": copy_w, "fetch_scale": scale_f, "write_scale": scale_w,
+           "command": args.pmc_command}
+    base = os.path.join(ROOT, "profiles", f"flash_{args.workload}_{args.tau_mode}_traffic")
+    with open(base + ".json", "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    with open(base + ".md", "w") as f:
+        f.write(f"# HBM traffic of the sparse forward kernel: {args.workload}, {args.tau_mode} tau\n\n")
+        f.write("Counter runs (one counter per pass, each over the same command):\n\n")
+        f.write(f"    {args.pmc_command}\n\n")
+        f.write("| quantity | value |\n|---|---|\n")
+        f.write(f"| FETCH_SIZE per flash dispatch | {f_kib:,.0f} KiB (mean of {nf}) |\n")
+        f.write(f"| WRITE_SIZE per flash dispatch | {w_kib:,.0f} KiB (mean of {nw}) |\n")
+        f.write(f"| FETCH_SIZE of the 1 GiB copy | {copy_f:,.0f} KiB -> scale {scale_f:.4f} |\n")
+        f.write(f"| WRITE_SIZE of the 1 GiB copy | {copy_w:,.0f} KiB -> scale {scale_w:.4f} |\n")
+        f.write(f"| read bytes per launch (scaled) | {rd / 1e9:.3f} GB |\n")
+        f.write(f"| written bytes per launch (scaled) | {wr / 1e9:.3f} GB |\n")
+        f.write(f"| kernel source sha256[:16] | {rec['flash_source_sha256_16']} |\n")
+    print(json.dumps(rec))
 
 
 def cpu_baseline(w, cfg, Qc, Kc, Vc, budget_s: float = 12.0):
@@ -141,8 +208,8 @@ def main():
               "heads shard across GPUs with no exchange inside attention, so the per-GPU kernel "
               "measured at --gpus 1 is the figure of interest.", file=sys.stderr)
         sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
+    if args.pmc_summary:
+        pmc_summary(args)
         return
 
     import torch
@@ -247,6 +314,8 @@ def main():
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+    if args.with_copy:
+        copy_calibration()
 
 
 if __name__ == "__main__":
