@@ -148,10 +148,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
 // Per-lane constants of the pass: source offsets of the buffer->LDS pieces (a
 // wave's piece i covers LDS bytes [(w + WAVES i) KB, +1 KB) of a tile, lane l
 // its 16 bytes at l*16, holding the swizzled chunk of that slot), and the LDS
-// read bases of the K and V^T operands.
+// read bases of the K and V^T operands.  When the rows of piece i + 1 lie a
+// whole number of swizzle periods past those of piece i (kFold), the offsets of
+// piece i are those of piece 0 plus i * kPieceStride and only piece 0's are kept.
 template <int D, int BQ>
 struct Lanes {
-    int ksrc[FC<D, BQ>::PPW], vsrc[FC<D, BQ>::PPW];
+    static constexpr int kRowsPerStep = FC<D, BQ>::WAVES * (1024 / FC<D, BQ>::RB);
+    static constexpr bool kFold = kRowsPerStep % (D / 8) == 0 && kRowsPerStep % 4 == 0;
+    static constexpr int kPieceStride = kRowsPerStep * FC<D, BQ>::RB;
+    static constexpr int NSRC = kFold ? 1 : FC<D, BQ>::PPW;
+    int ksrc[NSRC], vsrc[NSRC];
     int kread[D / 16];         // K operand of step c: row l32, features 16c + 8h (swizzled)
     int vread[D / 32];         // V^T operand of feature block db (rows 4h + (i>>2))
 
@@ -160,7 +166,7 @@ struct Lanes {
         constexpr int RPK = 1024 / C::RB;              // rows per 1 KB piece
         constexpr int SPR = C::RB / 16;                // 16-byte slots per row
 #pragma unroll
-        for (int i = 0; i < C::PPW; ++i) {
+        for (int i = 0; i < NSRC; ++i) {
             const int q = wave + C::WAVES * i;
             const int r = q * RPK + lane / SPR;
             const int p = lane % SPR;
@@ -206,7 +212,7 @@ __device__ __forceinline__ bf16x4 bf16x4_of(float a, float b, float c, float d) 
 }
 
 template <int D, int BQ>
-__device__ __forceinline__ void store_split(unsigned char *stage, const Staging<D, BQ> &st) {
+__device__ __forceinline__ void store_split(unsigned char *Kst, unsigned char *Vst, const Staging<D, BQ> &st) {
     using C = FC<D, BQ>;
 #pragma unroll
     for (int i = 0; i < C::SU; ++i) {
@@ -216,7 +222,7 @@ __device__ __forceinline__ void store_split(unsigned char *stage, const Staging<
         for (int t = 0; t < 2; ++t) {
             const u32x4 w = t == 0 ? st.k[i] : st.v[i];
             const int pos = (c4 >> 1) ^ (t == 0 ? swz_k<D>(row) : swz_v<D>(row));
-            unsigned char *base = stage + t * C::TILE + 16 * pos + 8 * (c4 & 1);
+            unsigned char *base = (t == 0 ? Kst : Vst) + 16 * pos + 8 * (c4 & 1);
             float x[4], lo[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -230,23 +236,23 @@ __device__ __forceinline__ void store_split(unsigned char *stage, const Staging<
 }
 
 // 16 bytes per lane from a buffer straight into LDS at lds_base + 16 * lane.
-__device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char *lds_base, int voffset) {
+__device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char *lds_base, int voffset,
+                                              int soffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base, 16, voffset, 0, 0,
-                                             0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base, 16, voffset,
+                                             soffset, 0, 0);
 #endif
 }
 
-// One buffer->LDS piece per (i, tensor): 1 KB of the tile at the wave's slot.
+// One tile of K or V: the wave's buffer->LDS pieces, 1 KB each, at its slots.
 template <int D, int BQ>
-__device__ __forceinline__ void load_direct(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                            unsigned char *stage, const Lanes<D, BQ> &ln, int wave) {
+__device__ __forceinline__ void load_direct(__amdgpu_buffer_rsrc_t r, unsigned char *dst, const int *src, int wave) {
     using C = FC<D, BQ>;
+    using L = Lanes<D, BQ>;
 #pragma unroll
     for (int i = 0; i < C::PPW; ++i) {
-        const int piece = (wave + C::WAVES * i) * 1024;
-        buffer_to_lds(rk, stage + piece, ln.ksrc[i]);
-        buffer_to_lds(rv, stage + C::TILE + piece, ln.vsrc[i]);
+        if constexpr (L::kFold) buffer_to_lds(r, dst + (wave + C::WAVES * i) * 1024, src[0], i * L::kPieceStride);
+        else buffer_to_lds(r, dst + (wave + C::WAVES * i) * 1024, src[i], 0);
     }
 }
 
@@ -271,31 +277,284 @@ struct HeadSrc {
     int n_rows;
 };
 
-// Start the loads of tile t into `stage`: direct for bf16 tiles, into `st` for
-// fp32 split tiles (stored by store_split once the current tile is done).
-template <typename T, int D, int BQ>
-__device__ __forceinline__ void issue_tile(const TileDesc &t, const HeadSrc<T> &hs, const Lanes<D, BQ> &ln,
-                                           unsigned char *stage, int wave, Staging<D, BQ> &st) {
+// Buffer resource of the K (value = false) or V rows of tile t.
+template <typename T, int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const TileDesc &t, const HeadSrc<T> &hs, bool value) {
     if (t.kind == kResidual) {
         const size_t off = (size_t)(t.row0 / 32) * kTile * D;
-        load_direct<D, BQ>(buffer_rsrc(hs.ks + off, kTile * D * 2), buffer_rsrc(hs.vs + off, kTile * D * 2), stage, ln,
-                           wave);
-    } else {
-        const uint32_t bytes = (uint32_t)(hs.n_rows - t.row0) * (D * sizeof(T));
-        const auto rk = buffer_rsrc(hs.k + (size_t)t.row0 * D, bytes);
-        const auto rv = buffer_rsrc(hs.v + (size_t)t.row0 * D, bytes);
-        if constexpr (sizeof(T) == 2) load_direct<D, BQ>(rk, rv, stage, ln, wave);
-        else load_split<D, BQ>(rk, rv, st);
+        return buffer_rsrc((value ? hs.vs : hs.ks) + off, kTile * D * 2);
     }
+    const uint32_t bytes = (uint32_t)(hs.n_rows - t.row0) * (D * sizeof(T));
+    return buffer_rsrc((value ? hs.v : hs.k) + (size_t)t.row0 * D, bytes);
+}
+
+// Start the loads of tile t: straight to LDS for bf16 rows and residual tiles,
+// into `st` for fp32 rows (stored by store_split once the current tile is done).
+template <typename T, int D, int BQ>
+__device__ __forceinline__ void issue_tile(const TileDesc &t, const HeadSrc<T> &hs, const Lanes<D, BQ> &ln,
+                                           unsigned char *Kst, unsigned char *Vst, int wave, Staging<D, BQ> &st) {
+    const auto rk = tile_rsrc<T, D>(t, hs, false);
+    const auto rv = tile_rsrc<T, D>(t, hs, true);
+    if (sizeof(T) == 2 || t.kind == kResidual) {
+        load_direct<D, BQ>(rk, Kst, ln.ksrc, wave);
+        load_direct<D, BQ>(rv, Vst, ln.vsrc, wave);
+    } else {
+        load_split<D, BQ>(rk, rv, st);
+    }
+}
+
+// S^T = K Q^T over one tile: s[0] holds LDS key rows 0..31, s[1] rows 32..63.
+// The K operands are read two steps ahead of the MFMAs that take them.
+template <int D, int BQ, bool kF32>
+__device__ __forceinline__ void qk_tile(const unsigned char *Ks, const Lanes<D, BQ> &ln, const bf16x8 *qf,
+                                        const bf16x8 *ql, f32x16 (&s)[2]) {
+    using C = FC<D, BQ>;
+    constexpr int NS = D / 16;
+    bf16x8 k0v[NS], k1v[NS];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+        k0v[c2] = *reinterpret_cast<const bf16x8 *>(Ks + ln.kread[c2]);
+        k1v[c2] = *reinterpret_cast<const bf16x8 *>(Ks + ln.kread[c2] + 32 * C::RB);
+    }
+#pragma unroll
+    for (int c2 = 0; c2 < NS; ++c2) {
+        if (c2 + 2 < NS) {
+            k0v[c2 + 2] = *reinterpret_cast<const bf16x8 *>(Ks + ln.kread[c2 + 2]);
+            k1v[c2 + 2] = *reinterpret_cast<const bf16x8 *>(Ks + ln.kread[c2 + 2] + 32 * C::RB);
+        }
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0v[c2], qf[c2], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1v[c2], qf[c2], s[1], 0, 0, 0);
+        if constexpr (kF32) s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0v[c2], ql[c2], s[0], 0, 0, 0);
+    }
+}
+
+// S^T for the 32 LDS key rows 32hb.. of a tile (one accumulator block); the K
+// operands are read two steps ahead of the MFMAs that take them.
+template <int D, int BQ>
+__device__ __forceinline__ f32x16 qk_half(const unsigned char *Ks, int hb, const Lanes<D, BQ> &ln, const bf16x8 *qf) {
+    using C = FC<D, BQ>;
+    constexpr int NS = D / 16;
+    const unsigned char *base = Ks + 32 * hb * C::RB;
+    bf16x8 kv[NS];
+    f32x16 s = {};
+    kv[0] = *reinterpret_cast<const bf16x8 *>(base + ln.kread[0]);
+    kv[1] = *reinterpret_cast<const bf16x8 *>(base + ln.kread[1]);
+#pragma unroll
+    for (int c2 = 0; c2 < NS; ++c2) {
+        if (c2 + 2 < NS) kv[c2 + 2] = *reinterpret_cast<const bf16x8 *>(base + ln.kread[c2 + 2]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[c2], qf[c2], s, 0, 0, 0);
+    }
+    return s;
+}
+
+// O^T += V^T P^T over the 32 keys 32hb.. of a tile: steps j = 2hb + n / NB with
+// P^T operands pa (j even) and pc (j odd), features 32(n % NB)..; V^T operands
+// read two steps ahead.
+template <int D, int BQ>
+__device__ __forceinline__ void pv_half(const unsigned char *Vs, int hb, const Lanes<D, BQ> &ln, const bf16x8 &pa,
+                                        const bf16x8 &pc, f32x16 (&acc)[D / 32]) {
+    using C = FC<D, BQ>;
+    constexpr int NB = D / 32, NP = 2 * NB;
+    bf16x8 vop[NP];
+    auto vload = [&](int n) -> bf16x8 {
+        const int db = n % NB, j = 2 * hb + n / NB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(Vs + ln.vread[db] + 16 * j * C::RB));
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(Vs + ln.vread[db] + (16 * j + 8) * C::RB));
+        const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, both);
+    };
+    vop[0] = vload(0);
+    vop[1] = vload(1);
+#pragma unroll
+    for (int n = 0; n < NP; ++n) {
+        if (n + 2 < NP) vop[n + 2] = vload(n + 2);
+        acc[n % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[n], n < NB ? pa : pc, acc[n % NB], 0, 0, 0);
+    }
+}
+
+// max over the two lanes (l, l ^ 32) that hold one query row
+__device__ __forceinline__ float row_pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float row_pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Online-softmax state of the wave's 32 rows (per lane: its row, log2 units).
+// Lazy rescaling: the reference m_ref moves only when some row of the wave
+// exceeds it by more than 8, so weights stay <= 2^8 and the accumulator rescale
+// is skipped on most tiles.  Numerator and normaliser share the reference, so
+// the softmax is unchanged.
+template <int D>
+struct SoftState {
+    f32x16 acc[D / 32];
+    float m_ref, l_run;
+
+    __device__ __forceinline__ float m_use() const { return m_ref == -INFINITY ? 0.f : m_ref; }
+
+    // New reference from this tile's row maxima (row_max: both lanes of a row
+    // agree); rescales the normaliser and returns the factor for the accumulator.
+    __device__ __forceinline__ float move_ref_l(float row_max) {
+        const float m_new = fmaxf(m_ref, row_max);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
+        return alpha;
+    }
+    __device__ __forceinline__ void scale_acc(float alpha) {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+    }
+    __device__ __forceinline__ void move_ref(float row_max) { scale_acc(move_ref_l(row_max)); }
+};
+
+// An empty instruction that reads x: x must be computed before this point.
+__device__ __forceinline__ void pin(const bf16x8 &x) {
+    const u32x4 w = __builtin_bit_cast(u32x4, x);
+    asm volatile("" ::"v"(w));
+}
+__device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
+
+// Lane maximum of one accumulator block (32 keys of a full exact tile), log2 units.
+__device__ __forceinline__ float half_max(const f32x16 &s, float c) {
+    float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+        m0 = fmaxf(m0, s[r]);
+        m1 = fmaxf(m1, s[r + 1]);
+    }
+    return fmaxf(m0, m1) * c;           // c > 0
+}
+
+// Weights of one accumulator block against the reference m_use: the P^T
+// operands of its two steps and their sum.  Straight-line code, so that it can
+// share a scheduling region with MFMAs.
+__device__ __forceinline__ void weights_half(const f32x16 &s, float c, float m_use, bf16x8 &pa, bf16x8 &pc,
+                                             float &psum) {
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -m_use));
+        if (r & 1) ps1 += p; else ps0 += p;
+        if (r < 8) pa[r] = (bf16)p; else pc[r - 8] = (bf16)p;
+    }
+    psum = ps0 + ps1;
+}
+
+// Keys of an accumulator block at or past `lim` (lane-relative) are absent.
+__device__ __forceinline__ void drop_absent(f32x16 &s, int lim) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) >= lim) s[r] = -INFINITY;
+}
+
+// An exact tile in four scheduling regions: S^T of key rows 0..31; S^T of rows
+// 32..63 while the weights of rows 0..31 are formed; P V of keys 0..31 while
+// the weights of keys 32..63 are formed; P V of keys 32..63.  The MFMAs of one
+// half run while the exponentials of the other are computed.  Before the
+// weights of a half, a row that passes the reference moves it (rare).  Rows at
+// or past `valid` (a partial last tile) are dropped.  Accumulator register r of
+// lane (h, l32) holds key row 8(r/4) + 4h + r%4 of its 32-row block.
+template <int D, int BQ>
+__device__ __forceinline__ void tile_exact(const unsigned char *Ks, const unsigned char *Vs, const Lanes<D, BQ> &ln,
+                                           const bf16x8 *qf, float c, int valid, int h, SoftState<D> &sm) {
+    constexpr int NS = D / 16, NB = D / 32;
+    f32x16 s0 = qk_half<D, BQ>(Ks, 0, ln, qf);
+    if (valid < kTile) drop_absent(s0, valid - 4 * h);
+    const float mx_a = half_max(s0, c);
+    if (__ballot(mx_a > sm.m_ref + 8.f) != 0) sm.move_ref(row_pair_max(mx_a));
+    bf16x8 p0, p1, p2, p3;
+    float ps_a, ps_b;
+    f32x16 s1 = qk_half<D, BQ>(Ks, 1, ln, qf);
+    weights_half(s0, c, sm.m_use(), p0, p1, ps_a);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int m = 0; m < NS; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 48 / NS, 0);
+        if (m + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    // keep the weights in this region: without a use here the compiler sinks
+    // them past the branches below, away from the MFMAs they should overlap
+    pin(p0);
+    pin(p1);
+    pin(ps_a);
+    sm.l_run += ps_a;
+    if (valid < kTile) drop_absent(s1, valid - 32 - 4 * h);
+    const float mx_b = half_max(s1, c);
+    // the weights of keys 0..31 are relative to the old reference: the
+    // accumulator is rescaled only after their P V has been added
+    const bool move_b = __ballot(mx_b > sm.m_ref + 8.f) != 0;
+    float alpha_b = 1.f;
+    if (move_b) alpha_b = sm.move_ref_l(row_pair_max(mx_b));
+    pv_half<D, BQ>(Vs, 0, ln, p0, p1, sm.acc);
+    weights_half(s1, c, sm.m_use(), p2, p3, ps_b);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int m = 0; m < 2 * NB; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 24 / NB, 1);
+        if (m + 2 < 2 * NB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    pin(p2);
+    pin(p3);
+    pin(ps_b);
+    if (move_b) sm.scale_acc(alpha_b);
+    sm.l_run += ps_b;
+    pv_half<D, BQ>(Vs, 1, ln, p2, p3, sm.acc);
+}
+
+// A split tile (fp32 rows or residual block means): S^T of its hi rows (0..31)
+// plus its lo rows (32..63) gives the logits of its 32 keys; residual tiles add
+// the logit bias log2(n_J) of dropped blocks and drop kept ones, fp32 tiles drop
+// absent rows.  The P^T operands pa, pc of the 32 keys serve both halves.
+// Updates the state.  The lane's keys are 4h + kr, kr = 8(r/4) + r%4: the lane
+// part is folded into per-tile values so that each register tests a constant kr.
+template <int D>
+__device__ __forceinline__ void weights_split(f32x16 &s0, const f32x16 &s1, const TileDesc &cur, float c,
+                                              float lg_bk, float lg_last, int n_kb, int h, SoftState<D> &sm,
+                                              bf16x8 &pa, bf16x8 &pc) {
+    const uint32_t kh = cur.kept >> (4 * h);
+    const int last = n_kb - 1 - cur.row0 - 4 * h;
+    const int vlim = cur.valid - 4 * h;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int kr = 8 * (r >> 2) + (r & 3);
+        float x = (s0[r] + s1[r]) * c;
+        if (cur.kind == kResidual) {
+            const bool drop = ((kh >> kr) & 1u) == 0;
+            x = drop ? x + (kr == last ? lg_last : lg_bk) : -INFINITY;
+        } else {
+            x = kr < vlim ? x : -INFINITY;
+        }
+        s0[r] = x;
+        mx = fmaxf(mx, x);
+    }
+    if (__ballot(mx > sm.m_ref + 8.f) != 0) sm.move_ref(row_pair_max(mx));
+    const float m_use = sm.m_use();
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(s0[r] - m_use);
+        if (r & 1) ps1 += p; else ps0 += p;
+        if (r < 8) pa[r] = (bf16)p; else pc[r - 8] = (bf16)p;
+    }
+    sm.l_run += ps0 + ps1;
 }
 
 // One work item: the query block I of head bh = item / n_qb, from its first
 // tile to its output rows.  kSparse: kept-list and residual tiles from a route;
-// otherwise every key tile (dense).
+// otherwise every key tile (dense).  LDS: K0/V0 and K1/V1, one tile each.
 template <typename T, int D, int BQ, bool kSparse>
 __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, const T *__restrict__ k,
                                          const T *__restrict__ v, T *__restrict__ o, const FlashArgs &a,
-                                         unsigned char *lds0, unsigned char *lds1) {
+                                         unsigned char *K0, unsigned char *V0, unsigned char *K1, unsigned char *V1) {
     using C = FC<D, BQ>;
     constexpr bool kF32 = sizeof(T) == 4;
     const int bh = item / a.n_qb;
@@ -362,156 +621,86 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
     hs.n_rows = a.N;
     const float lg_bk = log2f((float)a.block_k);
     const float lg_last = log2f((float)(a.N - (a.n_kb - 1) * a.block_k));
+    const float c = a.scale_log2;
 
-    f32x16 acc[D / 32];
+    SoftState<D> sm;
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
-    float m_ref = -INFINITY, l_run = 0.f;   // softmax reference (log2 units) and normaliser
-
+    for (int i = 0; i < D / 32; ++i) sm.acc[i] = f32x16{};
+    sm.m_ref = -INFINITY;
+    sm.l_run = 0.f;
     Staging<D, BQ> st;
+
     TileDesc cur, nxt;
     bool have = ts.next(cur, a);
     if (have) {
-        issue_tile<T, D, BQ>(cur, hs, ln, lds0, wave, st);
+        issue_tile<T, D, BQ>(cur, hs, ln, K0, V0, wave, st);
         if constexpr (kF32) {
-            if (cur.kind == kExactSplit) store_split<D, BQ>(lds0, st);
+            if (cur.kind == kExactSplit) store_split<D, BQ>(K0, V0, st);
         }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this thread's loads have landed
     __syncthreads();
-    // One pipeline step: compute the tile in cur_stage while the next tile streams
-    // into nxt_stage.  The loop below alternates two distinct LDS arrays so that
-    // every LDS access names its stage statically: the compiler can then see that
-    // reads of the current stage do not alias the buffer->LDS loads in flight.
-    auto step = [&](const unsigned char *cur_stage, unsigned char *nxt_stage) -> bool {
+    // One pipeline step: compute the tile in (Kc, Vc) while the next tile streams
+    // into (Kn, Vn).  The loops below alternate two sets of LDS arrays so that
+    // every LDS access names its buffer statically: the compiler can then see
+    // that reads of the current tile do not alias the buffer->LDS loads in flight.
+    auto step = [&](const unsigned char *Kc, const unsigned char *Vc, unsigned char *Kn, unsigned char *Vn,
+                    auto &&compute) -> bool {
         const bool have_next = ts.next(nxt, a);
         // Nothing is in flight here.  Saying so explicitly keeps the compiler from
         // placing its loop-entry wait after the prefetch below.
         __builtin_amdgcn_s_waitcnt(0x0F70);
-        if (have_next) issue_tile<T, D, BQ>(nxt, hs, ln, nxt_stage, wave, st);
-        const unsigned char *Ks = cur_stage;
-        const unsigned char *Vs = cur_stage + C::TILE;
-
-        // S^T for LDS key rows 0..31 (s[0]) and 32..63 (s[1])
-        f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-        for (int c2 = 0; c2 < D / 16; ++c2) {
-            const bf16x8 k0 = *reinterpret_cast<const bf16x8 *>(Ks + ln.kread[c2]);
-            const bf16x8 k1 = *reinterpret_cast<const bf16x8 *>(Ks + ln.kread[c2] + 32 * C::RB);
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[c2], s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[c2], s[1], 0, 0, 0);
-            if constexpr (kF32) s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, ql[c2], s[0], 0, 0, 0);
-        }
-
-        // accumulator register r of lane (h, l32) in block b holds LDS key row
-        // 32b + 8(r/4) + 4h + r%4
-        const bool split = cur.kind != kExact;
-        const float c = a.scale_log2;
-        float mx = -INFINITY;       // this lane's tile maximum, log2 units
-        if (!split) {
-            if (cur.valid < kTile) {            // partial tile (uniform): drop absent keys
-                const int lim = cur.valid - 4 * h;
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (32 * b + 8 * (r >> 2) + (r & 3) >= lim) s[b][r] = -INFINITY;
-            }
-            float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                m0 = fmaxf(m0, s[0][r]);
-                m1 = fmaxf(m1, s[1][r]);
-            }
-            mx = fmaxf(m0, m1) * c;             // c > 0
-        } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int kv = 8 * (r >> 2) + 4 * h + (r & 3);
-                float x = (s[0][r] + s[1][r]) * c;
-                if (cur.kind == kResidual) {
-                    const bool drop = ((cur.kept >> kv) & 1u) == 0;
-                    x = drop ? x + (cur.row0 + kv == a.n_kb - 1 ? lg_last : lg_bk) : -INFINITY;
-                } else {
-                    x = kv < cur.valid ? x : -INFINITY;
-                }
-                s[0][r] = x;
-                mx = fmaxf(mx, x);
-            }
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        // Lazy rescaling: the reference m_ref moves only when some row of the wave
-        // exceeds it by more than 8 (log2 units), so weights stay <= 2^8 and the
-        // accumulator rescale is skipped on most tiles.  The result is the same
-        // softmax: numerator and normaliser share the reference.
-        if (__ballot(mx > m_ref + 8.f) != 0) {
-            const float m_new = fmaxf(m_ref, mx);
-            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-            m_ref = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
-        }
-        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-        float ps0 = 0.f, ps1 = 0.f;
-        // P^T operands: step j takes registers 8(j&1)..8(j&1)+7 of block j/2; a
-        // split tile feeds the same weights to its hi (keys 0..31) and lo (32..63) halves
-        bf16x8 pb[4];
-        if (!split) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -m_use));
-                    if (r & 1) ps1 += p; else ps0 += p;
-                    pb[2 * b + (r >> 3)][r & 7] = (bf16)p;
-                }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(s[0][r] - m_use);
-                if (r & 1) ps1 += p; else ps0 += p;
-                pb[r >> 3][r & 7] = (bf16)p;
-            }
-            pb[2] = pb[0];
-            pb[3] = pb[1];
-        }
-        l_run += ps0 + ps1;
-
-        // O^T += V^T P^T: the V^T operand of step j (keys 16j..16j+15) comes from two
-        // transposing reads: keys 16j + 4h + e and 16j + 8 + 4h + e (e = 0..3)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(Vs + ln.vread[db] + 16 * j * C::RB));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(Vs + ln.vread[db] + (16 * j + 8) * C::RB));
-                // whole-vector reinterpretation: per-element bit casts of __bf16 vector
-                // elements are mis-compiled by this toolchain (splat of element 0)
-                const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                const bf16x8 va = __builtin_bit_cast(bf16x8, both);
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[j], acc[db], 0, 0, 0);
-            }
-        }
-
+        if (have_next) issue_tile<T, D, BQ>(nxt, hs, ln, Kn, Vn, wave, st);
+        compute(Kc, Vc);
         if constexpr (kF32) {
-            if (have_next && nxt.kind == kExactSplit) store_split<D, BQ>(nxt_stage, st);
+            if (have_next && nxt.kind == kExactSplit) store_split<D, BQ>(Kn, Vn, st);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the next tile has landed in LDS
         __syncthreads();
         cur = nxt;
         return have_next;
     };
+    auto exact = [&](const unsigned char *Kc, const unsigned char *Vc) {
+        tile_exact<D, BQ>(Kc, Vc, ln, qf, c, cur.valid, h, sm);
+    };
+    auto split = [&](const unsigned char *Kc, const unsigned char *Vc) {
+        f32x16 s0, s1;
+        if constexpr (kF32) {
+            f32x16 s2[2];
+            qk_tile<D, BQ, true>(Kc, ln, qf, ql, s2);
+            s0 = s2[0];
+            s1 = s2[1];
+        } else {
+            s0 = qk_half<D, BQ>(Kc, 0, ln, qf);
+            s1 = qk_half<D, BQ>(Kc, 1, ln, qf);
+        }
+        bf16x8 pa, pc;
+        weights_split<D>(s0, s1, cur, c, lg_bk, lg_last, a.n_kb, h, sm, pa, pc);
+        pv_half<D, BQ>(Vc, 0, ln, pa, pc, sm.acc);
+        pv_half<D, BQ>(Vc, 1, ln, pa, pc, sm.acc);
+    };
+    // The stream gives the exact tiles of the kept blocks first, then the split
+    // tiles (all tiles of fp32 inputs, the residual tiles of bf16 ones).
+    bool odd = false;        // the current tile sits in (K1, V1)
+    if constexpr (!kF32) {
+        while (have && cur.kind == kExact) {
+            have = step(K0, V0, K1, V1, exact);
+            if (!have || cur.kind != kExact) {
+                odd = true;
+                break;
+            }
+            have = step(K1, V1, K0, V0, exact);
+        }
+    }
+    if (have && odd) have = step(K1, V1, K0, V0, split);
     while (have) {
-        have = step(lds0, lds1);
+        have = step(K0, V0, K1, V1, split);
         if (!have) break;
-        have = step(lds1, lds0);
+        have = step(K1, V1, K0, V0, split);
     }
 
     // epilogue: O^T accumulator register r of block db holds feature 32db + 8(r/4) + 4h + r%4
-    const float lt = l_run + __shfl_xor(l_run, 32, kWave);
+    const float lt = row_pair_sum(sm.l_run);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (row_ok) {
         T *orow = o + head + (size_t)qrow * D;
@@ -519,10 +708,10 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                Store4<T>::st(orow + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
-                              acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+                Store4<T>::st(orow + 32 * db + 8 * g + 4 * h, sm.acc[db][4 * g] * inv, sm.acc[db][4 * g + 1] * inv,
+                              sm.acc[db][4 * g + 2] * inv, sm.acc[db][4 * g + 3] * inv);
         if (a.lse && h == 0)
-            a.lse[(size_t)bh * a.N + qrow] = lt > 0.f ? (m_ref + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+            a.lse[(size_t)bh * a.N + qrow] = lt > 0.f ? (sm.m_ref + log2f(lt)) * 0.69314718055994531f : -INFINITY;
     }
 }
 
@@ -549,11 +738,13 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
     FlashArgs a) {
     using C = FC<D, BQ>;
-    __shared__ __attribute__((aligned(1024))) unsigned char lds0[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char lds1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char K0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char V0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char K1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char V1[C::TILE];
     const int p = grid_position(blockIdx.x, a.n_items);
     const int item = kSparse ? __builtin_amdgcn_readfirstlane(a.work_order[p]) : p;
-    run_item<T, D, BQ, kSparse>(item, q, k, v, o, a, lds0, lds1);
+    run_item<T, D, BQ, kSparse>(item, q, k, v, o, a, K0, V0, K1, V1);
 }
 
 template <typename T, int D, int BQ, bool kSparse>
