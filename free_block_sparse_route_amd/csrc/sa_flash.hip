@@ -46,10 +46,14 @@ struct FC {
     static constexpr int STAGE = 2 * TILE;              // K then V
     static constexpr int PPW = TILE / 1024 / WAVES;     // 1 KB buffer->LDS pieces per wave per tile
     static constexpr int SU = 32 * (D / 4) / THREADS;   // 16-byte fp32 units per thread per tile
-    // waves per SIMD the register budget targets: two 128-row workgroups share a
-    // CU; a 64-row workgroup (2 waves) gets the full register file
-    static constexpr int WPE = BQ == 128 ? 2 : 1;
 };
+
+// Waves per SIMD the register budget targets.  bf16, 128-row workgroups: three
+// share a CU (48 KB of LDS each: K double-buffered, V single-buffered).  fp32
+// rows need more registers: two 128-row workgroups (64 KB of LDS each).  A
+// 64-row workgroup (2 waves) gets the full register file.
+template <typename T, int BQ>
+constexpr int kWavesPerEU = BQ == 128 ? (sizeof(T) == 2 ? 3 : 2) : 1;
 
 // chunk position = logical chunk ^ swizzle(row)
 template <int D> __device__ __forceinline__ int swz_k(int r) { return r & (D / 8 - 1); }
@@ -458,11 +462,13 @@ __device__ __forceinline__ void drop_absent(f32x16 &s, int lim) {
 // the weights of keys 32..63 are formed; P V of keys 32..63.  The MFMAs of one
 // half run while the exponentials of the other are computed.  Before the
 // weights of a half, a row that passes the reference moves it (rare).  Rows at
-// or past `valid` (a partial last tile) are dropped.  Accumulator register r of
-// lane (h, l32) holds key row 8(r/4) + 4h + r%4 of its 32-row block.
-template <int D, int BQ>
+// or past `valid` (a partial last tile) are dropped.  wait_v() runs before the
+// first read of Vs.  Accumulator register r of lane (h, l32) holds key row
+// 8(r/4) + 4h + r%4 of its 32-row block.
+template <int D, int BQ, typename WaitV>
 __device__ __forceinline__ void tile_exact(const unsigned char *Ks, const unsigned char *Vs, const Lanes<D, BQ> &ln,
-                                           const bf16x8 *qf, float c, int valid, int h, SoftState<D> &sm) {
+                                           const bf16x8 *qf, float c, int valid, int h, SoftState<D> &sm,
+                                           WaitV &&wait_v) {
     constexpr int NS = D / 16, NB = D / 32;
     f32x16 s0 = qk_half<D, BQ>(Ks, 0, ln, qf);
     if (valid < kTile) drop_absent(s0, valid - 4 * h);
@@ -492,6 +498,7 @@ __device__ __forceinline__ void tile_exact(const unsigned char *Ks, const unsign
     const bool move_b = __ballot(mx_b > sm.m_ref + 8.f) != 0;
     float alpha_b = 1.f;
     if (move_b) alpha_b = sm.move_ref_l(row_pair_max(mx_b));
+    wait_v();                           // this tile's values are in LDS from here on
     pv_half<D, BQ>(Vs, 0, ln, p0, p1, sm.acc);
     weights_half(s1, c, sm.m_use(), p2, p3, ps_b);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
@@ -512,7 +519,7 @@ __device__ __forceinline__ void tile_exact(const unsigned char *Ks, const unsign
 // A split tile (fp32 rows or residual block means): S^T of its hi rows (0..31)
 // plus its lo rows (32..63) gives the logits of its 32 keys; residual tiles add
 // the logit bias log2(n_J) of dropped blocks and drop kept ones, fp32 tiles drop
-// absent rows.  The P^T operands pa, pc of the 32 keys serve both halves.
+// absent rows.  The P^T operands pa, pc serve the 32 keys of either half.
 // Updates the state.  The lane's keys are 4h + kr, kr = 8(r/4) + r%4: the lane
 // part is folded into per-tile values so that each register tests a constant kr.
 template <int D>
@@ -632,38 +639,58 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
 
     TileDesc cur, nxt;
     bool have = ts.next(cur, a);
-    if (have) {
-        issue_tile<T, D, BQ>(cur, hs, ln, K0, V0, wave, st);
-        if constexpr (kF32) {
+    if constexpr (kF32) {
+        if (have) {
+            issue_tile<T, D, BQ>(cur, hs, ln, K0, V0, wave, st);
             if (cur.kind == kExactSplit) store_split<D, BQ>(K0, V0, st);
         }
+    } else {
+        // bf16: K is double-buffered; the single V buffer takes a tile's values
+        // at the start of that tile's step
+        if (have) load_direct<D, BQ>(tile_rsrc<T, D>(cur, hs, false), K0, ln.ksrc, wave);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this thread's loads have landed
     __syncthreads();
     // One pipeline step: compute the tile in (Kc, Vc) while the next tile streams
-    // into (Kn, Vn).  The loops below alternate two sets of LDS arrays so that
-    // every LDS access names its buffer statically: the compiler can then see
-    // that reads of the current tile do not alias the buffer->LDS loads in flight.
+    // into Kn (and Vn for fp32 rows).  The loops below alternate two sets of LDS
+    // arrays so that every LDS access names its buffer statically: the compiler
+    // can then see that reads of the current tile do not alias the buffer->LDS
+    // loads in flight.  bf16: the step starts the loads of the current tile's
+    // values (first) and the next tile's keys; wait_v lets the values land.
     auto step = [&](const unsigned char *Kc, const unsigned char *Vc, unsigned char *Kn, unsigned char *Vn,
                     auto &&compute) -> bool {
         const bool have_next = ts.next(nxt, a);
         // Nothing is in flight here.  Saying so explicitly keeps the compiler from
         // placing its loop-entry wait after the prefetch below.
         __builtin_amdgcn_s_waitcnt(0x0F70);
-        if (have_next) issue_tile<T, D, BQ>(nxt, hs, ln, Kn, Vn, wave, st);
-        compute(Kc, Vc);
+        if constexpr (kF32) {
+            if (have_next) issue_tile<T, D, BQ>(nxt, hs, ln, Kn, Vn, wave, st);
+        } else {
+            load_direct<D, BQ>(tile_rsrc<T, D>(cur, hs, true), const_cast<unsigned char *>(Vc), ln.vsrc, wave);
+            if (have_next) load_direct<D, BQ>(tile_rsrc<T, D>(nxt, hs, false), Kn, ln.ksrc, wave);
+        }
+        auto wait_v = [&]() {
+            if constexpr (!kF32) {
+                // the PPW value pieces were issued before the PPW key pieces
+                static_assert(C::PPW <= 15, "vmcnt field");
+                if (have_next) __builtin_amdgcn_s_waitcnt(0x0F70 | C::PPW);
+                else __builtin_amdgcn_s_waitcnt(0x0F70);
+                __syncthreads();
+            }
+        };
+        compute(Kc, Vc, wait_v);
         if constexpr (kF32) {
             if (have_next && nxt.kind == kExactSplit) store_split<D, BQ>(Kn, Vn, st);
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the next tile has landed in LDS
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the next keys have landed in LDS
         __syncthreads();
         cur = nxt;
         return have_next;
     };
-    auto exact = [&](const unsigned char *Kc, const unsigned char *Vc) {
-        tile_exact<D, BQ>(Kc, Vc, ln, qf, c, cur.valid, h, sm);
+    auto exact = [&](const unsigned char *Kc, const unsigned char *Vc, auto &wait_v) {
+        tile_exact<D, BQ>(Kc, Vc, ln, qf, c, cur.valid, h, sm, wait_v);
     };
-    auto split = [&](const unsigned char *Kc, const unsigned char *Vc) {
+    auto split = [&](const unsigned char *Kc, const unsigned char *Vc, auto &wait_v) {
         f32x16 s0, s1;
         if constexpr (kF32) {
             f32x16 s2[2];
@@ -676,8 +703,13 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
         }
         bf16x8 pa, pc;
         weights_split<D>(s0, s1, cur, c, lg_bk, lg_last, a.n_kb, h, sm, pa, pc);
+        wait_v();
         pv_half<D, BQ>(Vc, 0, ln, pa, pc, sm.acc);
-        pv_half<D, BQ>(Vc, 1, ln, pa, pc, sm.acc);
+        // Residual tiles take their block-mean values in bf16 (the hi rows): the
+        // rounding moves an output by at most 2^-9 of the mean's magnitude times
+        // the dropped blocks' weight, unlike a key-mean rounding, which the
+        // exponential amplifies.  fp32 rows keep both halves.
+        if (cur.kind == kExactSplit) pv_half<D, BQ>(Vc, 1, ln, pa, pc, sm.acc);
     };
     // The stream gives the exact tiles of the kept blocks first, then the split
     // tiles (all tiles of fp32 inputs, the residual tiles of bf16 ones).
@@ -734,17 +766,21 @@ __device__ __forceinline__ int grid_position(int i, int W) {
 // One workgroup per work item (query block); kSparse takes the item from the
 // route's work order, the dense path in plain order.
 template <typename T, int D, int BQ, bool kSparse>
-__global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_per_eu(FC<D, BQ>::WPE, FC<D, BQ>::WPE))) void flash_kernel(
+__global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<T, BQ>, kWavesPerEU<T, BQ>))) void flash_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
     FlashArgs a) {
     using C = FC<D, BQ>;
-    __shared__ __attribute__((aligned(1024))) unsigned char K0[C::TILE];
-    __shared__ __attribute__((aligned(1024))) unsigned char V0[C::TILE];
-    __shared__ __attribute__((aligned(1024))) unsigned char K1[C::TILE];
-    __shared__ __attribute__((aligned(1024))) unsigned char V1[C::TILE];
     const int p = grid_position(blockIdx.x, a.n_items);
     const int item = kSparse ? __builtin_amdgcn_readfirstlane(a.work_order[p]) : p;
-    run_item<T, D, BQ, kSparse>(item, q, k, v, o, a, K0, V0, K1, V1);
+    __shared__ __attribute__((aligned(1024))) unsigned char K0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char K1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char V0[C::TILE];
+    if constexpr (sizeof(T) == 2) {
+        run_item<T, D, BQ, kSparse>(item, q, k, v, o, a, K0, V0, K1, V0);
+    } else {
+        __shared__ __attribute__((aligned(1024))) unsigned char V1[C::TILE];
+        run_item<T, D, BQ, kSparse>(item, q, k, v, o, a, K0, V0, K1, V1);
+    }
 }
 
 template <typename T, int D, int BQ, bool kSparse>

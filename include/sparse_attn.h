@@ -117,7 +117,9 @@ enum {
                                                          key blocks, 32 rows of block means
                                                          rounded to bf16, then 32 rows of their
                                                          bf16 remainders (keys, then values);
-                                                         rows past n_kb are zero            */
+                                                         rows past n_kb are zero; the forward
+                                                         of bf16 inputs reads the value
+                                                         remainders of no tile             */
     SA_BUF_ROW_STATS,     /* fp32 [B,H,n_qb,2]           max_J s_IJ and log-sum-exp_J s_IJ  */
     SA_BUF_COST,          /* int32 [B,H,n_qb]            key/value tiles the forward visits */
     SA_BUF_WORK_ORDER,    /* int32 [W]                   work items b*H*n_qb + h*n_qb + I
