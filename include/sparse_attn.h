@@ -39,8 +39,9 @@
  * Conventions shared by every entry point
  *  - Q, K, V, O are [B, H, N, d] contiguous with d fastest, in the dtype of
  *    sa_params.dtype (bf16 or fp32).  Products run on bf16 matrix cores with
- *    fp32 accumulation; fp32 inputs are rounded to bf16 for the products.
- *    Routing (pooling, proxy, threshold) is fp32 throughout.
+ *    fp32 accumulation; fp32 inputs enter them as bf16 pairs (the rounded
+ *    value and its remainder), the softmax weights as bf16.  Routing
+ *    (pooling, proxy, threshold) is fp32 throughout.
  *  - Every tensor pointer is a DEVICE pointer (hipMalloc or equivalent) of the
  *    current HIP device.  The caller owns and frees all memory; the library
  *    allocates nothing, frees nothing and never synchronises.
