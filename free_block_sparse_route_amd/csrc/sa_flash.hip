@@ -389,11 +389,16 @@ __device__ __forceinline__ float row_pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Lazy rescaling: the reference m_ref of the online softmax moves only when
+// some row of the wave exceeds it by more than kLazy (log2 units), so the
+// accumulator rescale is skipped on almost every tile.  Weights stay below
+// 2^kLazy; fp32 sums and bf16 weights keep their relative precision at any
+// such scale, and with at most 2^24 keys a row's sums stay below 2^(kLazy+30),
+// far from overflow.  Numerator and normaliser share the reference, so the
+// softmax is unchanged.
+constexpr float kLazy = 32.f;
+
 // Online-softmax state of the wave's 32 rows (per lane: its row, log2 units).
-// Lazy rescaling: the reference m_ref moves only when some row of the wave
-// exceeds it by more than 8, so weights stay <= 2^8 and the accumulator rescale
-// is skipped on most tiles.  Numerator and normaliser share the reference, so
-// the softmax is unchanged.
 template <int D>
 struct SoftState {
     f32x16 acc[D / 32];
@@ -473,7 +478,7 @@ __device__ __forceinline__ void tile_exact(const unsigned char *Ks, const unsign
     f32x16 s0 = qk_half<D, BQ>(Ks, 0, ln, qf);
     if (valid < kTile) drop_absent(s0, valid - 4 * h);
     const float mx_a = half_max(s0, c);
-    if (__ballot(mx_a > sm.m_ref + 8.f) != 0) sm.move_ref(row_pair_max(mx_a));
+    if (__ballot(mx_a > sm.m_ref + kLazy) != 0) sm.move_ref(row_pair_max(mx_a));
     bf16x8 p0, p1, p2, p3;
     float ps_a, ps_b;
     f32x16 s1 = qk_half<D, BQ>(Ks, 1, ln, qf);
@@ -495,7 +500,7 @@ __device__ __forceinline__ void tile_exact(const unsigned char *Ks, const unsign
     const float mx_b = half_max(s1, c);
     // the weights of keys 0..31 are relative to the old reference: the
     // accumulator is rescaled only after their P V has been added
-    const bool move_b = __ballot(mx_b > sm.m_ref + 8.f) != 0;
+    const bool move_b = __ballot(mx_b > sm.m_ref + kLazy) != 0;
     float alpha_b = 1.f;
     if (move_b) alpha_b = sm.move_ref_l(row_pair_max(mx_b));
     wait_v();                           // this tile's values are in LDS from here on
@@ -543,7 +548,7 @@ __device__ __forceinline__ void weights_split(f32x16 &s0, const f32x16 &s1, cons
         s0[r] = x;
         mx = fmaxf(mx, x);
     }
-    if (__ballot(mx > sm.m_ref + 8.f) != 0) sm.move_ref(row_pair_max(mx));
+    if (__ballot(mx > sm.m_ref + kLazy) != 0) sm.move_ref(row_pair_max(mx));
     const float m_use = sm.m_use();
     float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
