@@ -109,7 +109,8 @@ __device__ __forceinline__ int count_ge(const float *S, int n, uint32_t kmin) {
     return cnt;
 }
 
-__device__ void select_row(const float *S, int bh, int I, const SelectArgs &a) {
+// Rows longer than 20 * 64 key blocks: the same steps, reading the row from LDS.
+__device__ void select_row_lds(const float *S, int bh, int I, const SelectArgs &a) {
     const int lane = lane_id();
     const int n = a.n_kb;
     float m = -INFINITY;
@@ -187,6 +188,105 @@ __device__ void select_row(const float *S, int bh, int I, const SelectArgs &a) {
     }
 }
 
+// One proxy row: statistics, the tau test, the cap or floor, the kept list,
+// bit mask and cost.  The lane holds scores J = lane + 64 i, i < R, in registers
+// (R * 64 >= n_kb): every pass over the row, in particular the 32 counting
+// passes of the cap's k-th-largest search, runs on registers.
+template <int R>
+__device__ void select_row(const float *S, int bh, int I, const SelectArgs &a) {
+    const int lane = lane_id();
+    const int n = a.n_kb;
+    // absent entries (J >= n) hold -inf and key 0, below every real key
+    float sv[R];
+    uint32_t key[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int J = i * kWave + lane;
+        sv[i] = J < n ? S[J] : -INFINITY;
+        key[i] = J < n ? orderable(sv[i]) : 0u;
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < R; ++i) m = fmaxf(m, sv[i]);
+    m = wave_max(m);
+    float z = 0.f;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        if (key[i] != 0u) z += expf(sv[i] - m);
+    z = wave_sum(z);
+    const float lse = m + logf(z);
+    const float thr = (a.tau_mode == SA_TAU_ABSOLUTE ? lse : m) + a.ln_tau;
+
+    int n_c = 0;
+#pragma unroll
+    for (int i = 0; i < R; ++i) n_c += __popcll(__ballot(key[i] != 0u && sv[i] >= thr));
+    int ksel = 0;
+    if (a.max_keep > 0 && n_c > a.max_keep) ksel = a.max_keep;
+    else if (n_c < a.min_keep) ksel = min(a.min_keep, n);
+
+    // ksel-th largest key T, built bit by bit from the top: the largest T with
+    // #{key >= T} >= ksel.  Every candidate is >= 1, so absent entries never
+    // count.  Equal keys beyond the budget are resolved by J.
+    uint32_t T = 0;
+    int take_eq = 0;
+    if (ksel > 0) {
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = T | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < R; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+            if (cnt >= ksel) T = cand;
+        }
+        int n_gt = 0;
+        if (T != 0xffffffffu)
+#pragma unroll
+            for (int i = 0; i < R; ++i) n_gt += __popcll(__ballot(key[i] > T));
+        take_eq = ksel - n_gt;
+    }
+
+    const size_t row = (size_t)bh * a.n_qb + I;
+    int32_t *idx = a.kv_idx + row * a.kv_idx_cap;
+    uint32_t *mask = a.kv_mask + row * a.mask_words;
+    const bool dense_row = (int64_t)I * a.block_q < a.n_prefix;
+    const int last_cnt = a.N - (n - 1) * a.block_k;
+    int kept = 0, eq_seen = 0, tiles = 0;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int J = i * kWave + lane;
+        const bool valid = key[i] != 0u;
+        bool keep;
+        if (ksel > 0) {
+            const bool eq = valid && key[i] == T;
+            const uint64_t be = __ballot(eq);
+            const int rank = eq_seen + __popcll(be & lanes_below());
+            eq_seen += __popcll(be);
+            keep = valid && (key[i] > T || (eq && rank < take_eq));
+        } else {
+            keep = valid && sv[i] >= thr;
+        }
+        keep = valid && (keep || dense_row || (int64_t)J * a.block_k < a.n_prefix);
+        const uint64_t bk = __ballot(keep);
+        if (keep) idx[kept + __popcll(bk & lanes_below())] = J;
+        kept += __popcll(bk);
+        const int w = 2 * i;
+        if (lane == 0 && w < a.mask_words) mask[w] = (uint32_t)bk;
+        if (lane == 1 && w + 1 < a.mask_words) mask[w + 1] = (uint32_t)(bk >> 32);
+        // cost: exact tiles of kept blocks, plus one residual tile per 32 pooled
+        // blocks (one mask word) that holds a dropped block
+        const int nj = (J == n - 1) ? last_cnt : a.block_k;
+        tiles += keep ? (nj + a.exact_tile_rows - 1) / a.exact_tile_rows : 0;
+        const uint64_t bd = __ballot(valid && !keep);
+        if (lane == 0) tiles += ((uint32_t)bd != 0) + ((uint32_t)(bd >> 32) != 0);
+    }
+    tiles = (int)wave_sum((float)tiles);
+    if (lane == 0) {
+        a.kv_count[row] = kept;
+        a.row_stats[row * 2 + 0] = m;
+        a.row_stats[row * 2 + 1] = lse;
+        a.cost[row] = tiles;
+    }
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -222,7 +322,16 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     }
     __syncthreads();
     const int wave = threadIdx.x / kWave;
-    for (int g = wave; g < g_cnt; g += kSelectThreads / kWave) select_row(S + g * n, bh, I0 + g, a);
+    const int chunks = (n + kWave - 1) / kWave;        // uniform over the launch
+    for (int g = wave; g < g_cnt; g += kSelectThreads / kWave) {
+        const float *row = S + g * n;
+        if (chunks <= 2) select_row<2>(row, bh, I0 + g, a);
+        else if (chunks <= 4) select_row<4>(row, bh, I0 + g, a);
+        else if (chunks <= 8) select_row<8>(row, bh, I0 + g, a);
+        else if (chunks <= 16) select_row<16>(row, bh, I0 + g, a);
+        else if (chunks <= 20) select_row<20>(row, bh, I0 + g, a);
+        else select_row_lds(row, bh, I0 + g, a);
+    }
 }
 
 // --------------------------------------------------------------------- order

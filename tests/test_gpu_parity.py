@@ -166,6 +166,36 @@ def test_identical_keys_make_residual_exact():
         assert np.abs(o - O_ref).max() <= 3e-2
 
 
+@pytest.mark.parametrize("dt,bq,bk", [("bf16", 128, 64), ("f32", 64, 128)])
+def test_route_means_and_residual_tiles(dt, bq, bk):
+    """The route's block means against the oracle's pooling (fp32 accumulation
+    against fp64: relative 1e-5), and the residual tiles: hi rows = bf16 of the
+    mean, lo rows = bf16 of the remainder, zero rows past the last block."""
+    w = S.small("means", 1, 2, 64 if dt == "f32" else 128, (3, 7, 19), bq, bk, 0.01, dtype=dt)
+    say(f"[case] means {dt} {bq}x{bk} N{w.N}")
+    Qc, Kc, Vc, Q, K, V = make(w)
+    rt, _, _ = run_gpu(Q, K, V, cfg_for(w))
+    qm, km, vm = (t.cpu().double().numpy() for t in (rt.q_mean, rt.k_mean, rt.v_mean))
+    split = rt.kv_split.cpu()
+    for h in range(w.H):
+        q, k, v = head_np(Qc, 0, h), head_np(Kc, 0, h), head_np(Vc, 0, h)
+        for got, ref in ((qm[0, h], R.pool(q, bq)), (km[0, h], R.pool(k, bk)), (vm[0, h], R.pool(v, bk))):
+            scale = np.abs(ref).max()
+            assert np.abs(got - ref).max() <= 1e-5 * scale
+        for which, means in ((0, km[0, h]), (1, vm[0, h])):
+            t = split[0, h, which].reshape(-1, 64, w.d)          # [groups, 64, d]
+            n_kb = means.shape[0]
+            mf = torch.from_numpy(means).float()
+            hi = mf.to(torch.bfloat16)
+            lo = (mf - hi.float()).to(torch.bfloat16)
+            for J in range(t.shape[0] * 32):
+                g, r = divmod(J, 32)
+                if J < n_kb:
+                    assert torch.equal(t[g, r], hi[J]) and torch.equal(t[g, 32 + r], lo[J])
+                else:
+                    assert not t[g, r].any() and not t[g, 32 + r].any()
+
+
 def test_deterministic_and_route_reuse():
     m = sa()
     w = S.small("det", 1, 3, 128, (4, 8, 32), 128, 64, 0.01, max_keep_frac=0.1)
