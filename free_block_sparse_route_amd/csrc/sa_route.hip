@@ -1,9 +1,9 @@
 // Routing kernels: block pooling, proxy scoring and block selection, and the
 // cost-ordered work list for the attention kernel.
 //
-// pool    one workgroup per (b, h, block, tensor) reduces a block of <= 128
-//         tokens to its fp32 mean with coalesced 16-byte loads (HBM-bound; the
-//         inputs are read exactly once).  Block centroids: PARK page,
+// pool    one workgroup per (b, h, 128-token span, tensor) reduces the span's
+//         one or two blocks to fp32 means with coalesced 16-byte loads
+//         (HBM-bound; the inputs are read exactly once).  Block centroids: PARK page,
 //         section 4.1.
 // select  one workgroup per (b, h, group of G query blocks): the G proxy rows
 //         s_IJ = scale * qbar_I . kbar_J are computed in fp32 into LDS (never
@@ -36,42 +36,50 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const T *__restrict_
                                                             const T *__restrict__ k,
                                                             const T *__restrict__ v,
                                                             PoolArgs a) {
+    // one workgroup per 128-token span of one tensor: one block of 128 or two of 64
     const int which = blockIdx.z;            // 0 = q, 1 = k, 2 = v
     const int bh = blockIdx.y;
-    const int J = blockIdx.x;
     const int bs = which == 0 ? a.block_q : a.block_k;
     const int nb = which == 0 ? a.n_qb : a.n_kb;
-    if (J >= nb) return;
+    const int r0 = blockIdx.x * 128;
+    if (r0 >= a.N) return;
     const T *X = (which == 0 ? q : which == 1 ? k : v) + (size_t)bh * a.N * D;
-    const int r0 = J * bs;
-    const int cnt = min(bs, a.N - r0);
+    const int span = min(128, a.N - r0);
 
     constexpr int CH = D / 8;                 // 8-element chunks per row
     constexpr int RG = kPoolThreads / CH;     // row groups
     const int c = threadIdx.x % CH;
     const int g = threadIdx.x / CH;
 
-    float acc[8];
+    float acc[2][8];                          // the span's first and second block
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[b][i] = 0.f;
 #pragma unroll
     for (int it = 0; it < 128 / RG; ++it) {
         const int r = g + it * RG;
-        if (r < cnt) {
+        if (r < span) {
             float x[8];
             Ld8<T>::load_f32(X + (size_t)(r0 + r) * D + c * 8, x);
+            const int b = r >= bs;             // RG divides bs: uniform per iteration
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += x[i];
+            for (int i = 0; i < 8; ++i) acc[b][i] += x[i];
         }
     }
-    __shared__ float part[RG * D];
+    __shared__ float part[2][RG * D];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) part[g * D + c * 8 + i] = acc[i];
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part[b][g * D + c * 8 + i] = acc[b][i];
     __syncthreads();
-    if (threadIdx.x < D) {
-        const int col = threadIdx.x;
-        float s = 0.f;
-        for (int gg = 0; gg < RG; ++gg) s += part[gg * D + col];
+    const int nblk = (span + bs - 1) / bs;
+    if (threadIdx.x < nblk * D) {
+        const int b = threadIdx.x / D, col = threadIdx.x % D;
+        const int J = (r0 + b * bs) / bs;
+        const int cnt = min(bs, a.N - J * bs);
+        float s = 0.f;                    // other blocks' rows left zeros here
+        for (int gg = 0; gg < RG; ++gg) s += part[b][gg * D + col];
         const float m = s / (float)cnt;
         float *dst = which == 0 ? a.q_mean : which == 1 ? a.k_mean : a.v_mean;
         dst[((size_t)bh * nb + J) * D + col] = m;
@@ -380,7 +388,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *cos
 template <typename T, int D>
 static hipError_t launch_pool_t(const void *q, const void *k, const void *v, const PoolArgs &a,
                                 int BH, hipStream_t st) {
-    dim3 grid(max(a.n_qb, a.n_kb), BH, 3);
+    dim3 grid((a.N + 127) / 128, BH, 3);
     hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(kPoolThreads), 0, st,
                        (const T *)q, (const T *)k, (const T *)v, a);
     return hipGetLastError();
