@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan1.3b")
     ap.add_argument("--tau", type=float, default=None)
-    ap.add_argument("--tau-mode", choices=("relative", "absolute"), default="relative")
+    ap.add_argument("--tau-mode", choices=("relative", "absolute", "topp"), default="relative")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--with-copy", action="store_true",
@@ -218,7 +218,7 @@ def main():
     from workloads import synth as S
 
     w = S.WORKLOADS[args.workload]
-    mode = sa.RELATIVE if args.tau_mode == "relative" else sa.ABSOLUTE
+    mode = {"relative": sa.RELATIVE, "absolute": sa.ABSOLUTE, "topp": sa.TOPP}[args.tau_mode]
     cfg = sa.Config(block_q=w.block_q, block_k=w.block_k, tau=w.tau if args.tau is None else args.tau,
                     tau_mode=mode, max_keep=w.max_keep, min_keep=1, n_dense_prefix=w.n_text)
     print(f"[bench] generating {w.name} B{w.B} H{w.H} N{w.N} d{w.d}", file=sys.stderr, flush=True)

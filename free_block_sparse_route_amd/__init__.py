@@ -9,6 +9,6 @@ hand-written HIP for AMD Instinct MI355X (gfx950).
 
 q, k, v: device tensors [B, H, N, d], bf16 or fp32, d in {64, 128}.
 """
-from .binding import (ABSOLUTE, FLAG_NO_RESIDUAL, RELATIVE, Config, Route, SaParams, SaRoute,  # noqa: F401
+from .binding import (ABSOLUTE, FLAG_NO_RESIDUAL, RELATIVE, TOPP, Config, Route, SaParams, SaRoute,  # noqa: F401
                       SparseAttnError, dense_flops, dense_ref_gpu, forward, kv_idx_cap, last_error,
                       make_params, route, route_sizes, status_string)

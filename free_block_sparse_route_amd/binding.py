@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libsparse_attn.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_CAPACITY, SA_ERR_HIP = 0, -1, -2, -3, -4
 SA_BF16, SA_F32 = 0, 1
-RELATIVE, ABSOLUTE = 0, 1
+RELATIVE, ABSOLUTE, TOPP = 0, 1, 2
 FLAG_NO_RESIDUAL = 1
 BUFFERS = ("kv_count", "kv_idx", "kv_mask", "q_mean", "k_mean", "v_mean", "kv_split", "row_stats", "cost",
            "work_order")

@@ -57,7 +57,7 @@ sa_status check_params(const sa_params *p, bool routing) {
     if (elems > ((int64_t)1 << 40)) return fail(SA_ERR_INVALID_ARG, "tensor too large");
     if (routing) {
         if (!(p->tau >= 0.f)) return fail(SA_ERR_INVALID_ARG, "tau must be >= 0 and not NaN");
-        if (p->tau_mode != SA_TAU_RELATIVE && p->tau_mode != SA_TAU_ABSOLUTE)
+        if (p->tau_mode != SA_TAU_RELATIVE && p->tau_mode != SA_TAU_ABSOLUTE && p->tau_mode != SA_TAU_TOPP)
             return fail(SA_ERR_INVALID_ARG, "tau_mode %d is not an sa_tau_mode", p->tau_mode);
         if (p->max_keep < 0 || p->min_keep < 0)
             return fail(SA_ERR_INVALID_ARG, "max_keep and min_keep must be >= 0");
@@ -154,6 +154,7 @@ sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, co
     sa_.n_prefix = p->n_dense_prefix;
     sa_.scale = p->scale > 0.f ? p->scale : (float)(1.0 / sqrt((double)p->d));
     sa_.ln_tau = p->tau > 0.f ? (float)log((double)p->tau) : -INFINITY;
+    sa_.topp_target = 1.f - p->tau;
     sa_.q_mean = r->q_mean; sa_.k_mean = r->k_mean;
     sa_.kv_count = r->kv_count; sa_.kv_idx = r->kv_idx; sa_.cost = r->cost;
     sa_.work_order = r->work_order; sa_.kv_mask = r->kv_mask;

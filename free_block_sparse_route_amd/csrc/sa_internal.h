@@ -22,6 +22,7 @@ struct SelectArgs {
     int exact_tile_rows;                 // key rows per exact attention tile (cost model)
     int tau_mode, max_keep, min_keep, n_prefix;
     float scale, ln_tau;                 // ln_tau = -inf when tau == 0
+    float topp_target;                   // 1 - tau: proxy mass the TOPP mode retains
     const float *q_mean, *k_mean;
     int32_t *kv_count, *kv_idx, *cost, *work_order;
     uint32_t *kv_mask;

@@ -117,8 +117,16 @@ __device__ __forceinline__ int count_ge(const float *S, int n, uint32_t kmin) {
     return cnt;
 }
 
+// Proxy probability mass of the row entries whose key is >= kmin (wave-uniform).
+__device__ __forceinline__ float mass_ge(const float *S, int n, uint32_t kmin, float lse) {
+    float ms = 0.f;
+    for (int J = lane_id(); J < n; J += kWave)
+        if (orderable(S[J]) >= kmin) ms += expf(S[J] - lse);
+    return wave_sum(ms);
+}
+
 // Rows longer than 20 * 64 key blocks: the same steps, reading the row from LDS.
-__device__ void select_row_lds(const float *S, int bh, int I, const SelectArgs &a) {
+__device__ __forceinline__ void select_row_lds(const float *S, int bh, int I, const SelectArgs &a) {
     const int lane = lane_id();
     const int n = a.n_kb;
     float m = -INFINITY;
@@ -131,13 +139,41 @@ __device__ void select_row_lds(const float *S, int bh, int I, const SelectArgs &
     const float thr = (a.tau_mode == SA_TAU_ABSOLUTE ? lse : m) + a.ln_tau;
 
     int n_c = 0;
-    for (int base = 0; base < n; base += kWave) {
-        const int J = base + lane;
-        n_c += __popcll(__ballot(J < n && S[J] >= thr));
+    if (a.tau_mode == SA_TAU_TOPP) {
+        // length of the ranking prefix whose preceding proxy mass stays below
+        // the target (see the register version below)
+        const float target = a.topp_target;
+        if (target > 0.f) {
+            uint32_t Ts = 0;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t cand = Ts | (1u << bit);
+                if (mass_ge(S, n, cand, lse) >= target) Ts = cand;
+            }
+            if (Ts == 0u) {
+                n_c = n;
+            } else {
+                const float mgt = Ts == 0xffffffffu ? 0.f : mass_ge(S, n, Ts + 1, lse);
+                const int ngt = Ts == 0xffffffffu ? 0 : count_ge(S, n, Ts + 1);
+                const int neq = count_ge(S, n, Ts) - ngt;
+                float peq = 0.f;
+                for (int J = lane; J < n; J += kWave)
+                    if (orderable(S[J]) == Ts) peq = expf(S[J] - lse);
+                peq = wave_max(peq);
+                int teq = 1;
+                while (teq < neq && mgt + (float)teq * peq < target) ++teq;
+                n_c = ngt + teq;
+            }
+        }
+    } else {
+        for (int base = 0; base < n; base += kWave) {
+            const int J = base + lane;
+            n_c += __popcll(__ballot(J < n && S[J] >= thr));
+        }
     }
     int ksel = 0;
     if (a.max_keep > 0 && n_c > a.max_keep) ksel = a.max_keep;
     else if (n_c < a.min_keep) ksel = min(a.min_keep, n);
+    else if (a.tau_mode == SA_TAU_TOPP) ksel = n_c;         // a ranking prefix of n_c blocks
 
     // ksel-th largest key T, built bit by bit from the top: the largest T with
     // #{key >= T} >= ksel.  Equal keys beyond the budget are resolved by J.
@@ -171,7 +207,7 @@ __device__ void select_row_lds(const float *S, int bh, int I, const SelectArgs &
             eq_seen += __popcll(be);
             keep = valid && (key > T || (eq && rank < take_eq));
         } else {
-            keep = valid && sv >= thr;
+            keep = valid && a.tau_mode != SA_TAU_TOPP && sv >= thr;   // TOPP: n_c = 0
         }
         keep = valid && (keep || dense_row || (int64_t)J * a.block_k < a.n_prefix);
         const uint64_t bk = __ballot(keep);
@@ -201,7 +237,7 @@ __device__ void select_row_lds(const float *S, int bh, int I, const SelectArgs &
 // (R * 64 >= n_kb): every pass over the row, in particular the 32 counting
 // passes of the cap's k-th-largest search, runs on registers.
 template <int R>
-__device__ void select_row(const float *S, int bh, int I, const SelectArgs &a) {
+__device__ __forceinline__ void select_row(const float *S, int bh, int I, const SelectArgs &a) {
     const int lane = lane_id();
     const int n = a.n_kb;
     // absent entries (J >= n) hold -inf and key 0, below every real key
@@ -226,18 +262,64 @@ __device__ void select_row(const float *S, int bh, int I, const SelectArgs &a) {
     const float thr = (a.tau_mode == SA_TAU_ABSOLUTE ? lse : m) + a.ln_tau;
 
     int n_c = 0;
+    uint32_t T = 0;
+    int take_eq = 0;
+    bool topp_cut = false;      // T, take_eq already give the TOPP prefix
+    if (a.tau_mode == SA_TAU_TOPP) {
+        // ranking prefix whose preceding proxy mass stays below the target:
+        // Ts = the largest key with mass(key >= Ts) >= target; blocks above Ts
+        // are kept, then ties at Ts in J order while the mass before them is
+        // below the target
+        const float target = a.topp_target;
+        float pv[R];
 #pragma unroll
-    for (int i = 0; i < R; ++i) n_c += __popcll(__ballot(key[i] != 0u && sv[i] >= thr));
+        for (int i = 0; i < R; ++i) pv[i] = key[i] != 0u ? expf(sv[i] - lse) : 0.f;
+        if (target > 0.f) {
+            uint32_t Ts = 0;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t cand = Ts | (1u << bit);
+                float ms = 0.f;
+#pragma unroll
+                for (int i = 0; i < R; ++i) ms += key[i] >= cand ? pv[i] : 0.f;
+                if (wave_sum(ms) >= target) Ts = cand;
+            }
+            if (Ts == 0u) {
+                n_c = n;                                    // the whole row is needed
+            } else {
+                float mgt = 0.f, peq = 0.f;
+                int ngt = 0, neq = 0;
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    mgt += key[i] > Ts ? pv[i] : 0.f;
+                    peq = key[i] == Ts ? pv[i] : peq;
+                    ngt += __popcll(__ballot(key[i] > Ts));
+                    neq += __popcll(__ballot(key[i] == Ts));
+                }
+                mgt = wave_sum(mgt);
+                peq = wave_max(peq);
+                int teq = 1;
+                while (teq < neq && mgt + (float)teq * peq < target) ++teq;
+                n_c = ngt + teq;
+                T = Ts;
+                take_eq = teq;
+                topp_cut = true;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i) n_c += __popcll(__ballot(key[i] != 0u && sv[i] >= thr));
+    }
     int ksel = 0;
     if (a.max_keep > 0 && n_c > a.max_keep) ksel = a.max_keep;
     else if (n_c < a.min_keep) ksel = min(a.min_keep, n);
+    else if (a.tau_mode == SA_TAU_TOPP) ksel = n_c;         // a ranking prefix of n_c blocks
 
     // ksel-th largest key T, built bit by bit from the top: the largest T with
     // #{key >= T} >= ksel.  Every candidate is >= 1, so absent entries never
     // count.  Equal keys beyond the budget are resolved by J.
-    uint32_t T = 0;
-    int take_eq = 0;
-    if (ksel > 0) {
+    if (ksel > 0 && !(topp_cut && ksel == n_c)) {
+        T = 0;
+        take_eq = 0;
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t cand = T | (1u << bit);
             int cnt = 0;
@@ -270,7 +352,7 @@ __device__ void select_row(const float *S, int bh, int I, const SelectArgs &a) {
             eq_seen += __popcll(be);
             keep = valid && (key[i] > T || (eq && rank < take_eq));
         } else {
-            keep = valid && sv[i] >= thr;
+            keep = valid && a.tau_mode != SA_TAU_TOPP && sv[i] >= thr;   // TOPP: n_c = 0
         }
         keep = valid && (keep || dense_row || (int64_t)J * a.block_k < a.n_prefix);
         const uint64_t bk = __ballot(keep);

@@ -13,9 +13,12 @@
  *     centroids as in the PARK page, section 4.1).  The compared quantity r_IJ
  *     is either the proxy probability relative to the row's largest one,
  *     exp(s_IJ - max_J' s_IJ') (SA_TAU_RELATIVE), or the proxy probability
- *     softmax_J(s_I.)_J itself (SA_TAU_ABSOLUTE).  A top-k budget caps the
- *     kept count at max_keep (rank by r descending, ties by J ascending); if
- *     fewer than min_keep clear tau, the min_keep best-ranked blocks are kept.
+ *     softmax_J(s_I.)_J itself (SA_TAU_ABSOLUTE).  SA_TAU_TOPP keeps instead
+ *     the shortest prefix of the ranking whose proxy probability mass reaches
+ *     1 - tau (cumulative-mass retention, the dynamic budget the Sol-Attn
+ *     abstract contrasts with fixed ones).  A top-k budget caps the kept count
+ *     at max_keep (rank by r descending, ties by J ascending); if fewer than
+ *     min_keep clear tau, the min_keep best-ranked blocks are kept.
  *     Key blocks that start before n_dense_prefix tokens are always kept, and
  *     a query block that starts before n_dense_prefix keeps every key block.
  *     The proxy map is never written to memory; only its per-row maximum and
@@ -77,8 +80,10 @@ typedef enum sa_status {
 typedef enum sa_dtype { SA_BF16 = 0, SA_F32 = 1 } sa_dtype;
 
 typedef enum sa_tau_mode {
-    SA_TAU_RELATIVE = 0,       /* r = exp(s_IJ - max_J' s_IJ')                       */
-    SA_TAU_ABSOLUTE = 1        /* r = softmax_J(s_I.)_J                              */
+    SA_TAU_RELATIVE = 0,       /* keep r >= tau, r = exp(s_IJ - max_J' s_IJ')        */
+    SA_TAU_ABSOLUTE = 1,       /* keep r >= tau, r = softmax_J(s_I.)_J               */
+    SA_TAU_TOPP = 2            /* keep ranking positions whose preceding proxy mass
+                                  is < 1 - tau                                       */
 } sa_tau_mode;
 
 enum {
@@ -89,7 +94,8 @@ enum {
 typedef struct sa_params {
     int32_t B, H, N, d;        /* N >= 1; d in {64, 128}                            */
     int32_t block_q, block_k;  /* each in {64, 128}; N need not be a multiple        */
-    float   tau;               /* >= 0; 0 keeps every block; > 1 keeps only floor    */
+    float   tau;               /* >= 0; 0 keeps every block; > 1 (TOPP: >= 1) keeps
+                                  only the floor and the prefix                      */
     int32_t tau_mode;          /* sa_tau_mode                                        */
     int32_t max_keep;          /* top-k cap on kept blocks per query block, 0 = none */
     int32_t min_keep;          /* floor when fewer clear tau (clamped to n_kb)       */

@@ -48,7 +48,14 @@ def brute_route(q, k, block_q, block_k, tau, tau_mode, max_keep, min_keep, n_pre
             z = math.fsum(math.exp(x - top) for x in s)
             r = [math.exp(x - top) / z for x in s]
         ranking = sorted(range(len(kr)), key=lambda J: (-r[J], J))
-        cands = [J for J in ranking if r[J] >= tau]
+        if tau_mode == 2:        # shortest ranking prefix with mass >= 1 - tau
+            cands = []
+            for J in ranking:
+                if math.fsum(r[x] for x in cands) >= 1.0 - tau:
+                    break
+                cands.append(J)
+        else:
+            cands = [J for J in ranking if r[J] >= tau]
         if max_keep > 0 and len(cands) > max_keep:
             chosen = set(cands[:max_keep])
         elif len(cands) < min_keep:

@@ -17,7 +17,13 @@ What it computes (per batch entry b and head h, tokens [N, d]):
            during online softmax).  Two readings:
              RELATIVE  r = P_IJ / max_J' P_IJ' = exp(s_IJ - max_J' s_IJ')
              ABSOLUTE  r = P_IJ
-           candidates C_I = {J : r_IJ >= tau}; a top-k budget caps |C_I| at
+             TOPP      r = P_IJ, and C_I is the shortest prefix of the ranking
+                       (r descending, J ascending) whose proxy mass reaches
+                       1 - tau: J is a candidate iff the mass ranked before it
+                       is < 1 - tau (cumulative-mass retention, the dynamic
+                       budget the Sol-Attn abstract contrasts with fixed ones)
+           candidates C_I = {J : r_IJ >= tau} (RELATIVE, ABSOLUTE); a top-k
+           budget caps |C_I| at
            max_keep (rank by r descending, then J ascending); if fewer than
            min_keep clear tau, the first min_keep of the ranking are kept; key
            blocks that start inside the dense prefix are always kept, and a
@@ -45,6 +51,7 @@ import numpy as np
 
 RELATIVE = 0
 ABSOLUTE = 1
+TOPP = 2
 EXEMPT_BAND = 1e-4      # |r - cut| below this: the keep decision is rounding-sensitive
 
 
@@ -94,10 +101,10 @@ def _logsumexp_rows(s: np.ndarray) -> np.ndarray:
 
 
 def compare_quantity(s: np.ndarray, tau_mode: int) -> np.ndarray:
-    """r[I, J] compared against tau: P/max P (RELATIVE) or P (ABSOLUTE)."""
+    """r[I, J]: P/max P (RELATIVE), else the proxy probability P."""
     if tau_mode == RELATIVE:
         return np.exp(s - s.max(axis=1, keepdims=True))
-    if tau_mode == ABSOLUTE:
+    if tau_mode in (ABSOLUTE, TOPP):
         return np.exp(s - _logsumexp_rows(s)[:, None])
     raise ValueError(f"unknown tau_mode {tau_mode}")
 
@@ -137,9 +144,17 @@ def select(r: np.ndarray, p: RouteParams, N: int) -> tuple:
     for I in range(n_qb):
         row = r[I]
         order = rank_order(row)
-        cand = row >= p.tau
+        if p.tau_mode == TOPP:
+            # keep rank i iff the mass ranked before it is below 1 - tau
+            target = 1.0 - p.tau
+            before = np.concatenate([[0.0], np.cumsum(row[order])[:-1]])
+            cand = np.zeros(n_kb, dtype=bool)
+            cand[order[before < target]] = True
+            exempt[I, order[np.abs(before - target) < EXEMPT_BAND]] = True
+        else:
+            cand = row >= p.tau
+            exempt[I] |= np.abs(row - p.tau) < EXEMPT_BAND
         n_c = int(cand.sum())
-        exempt[I] |= np.abs(row - p.tau) < EXEMPT_BAND
         if p.max_keep > 0 and n_c > p.max_keep:
             # candidates are a prefix of the ranking; keep its first max_keep
             keep = order[:p.max_keep]

@@ -59,7 +59,7 @@ def params(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(N=0), B.SA_ERR_INVALID_ARG), (dict(B=0), B.SA_ERR_INVALID_ARG), (dict(tau=-1.0), B.SA_ERR_INVALID_ARG),
-    (dict(tau=float("nan")), B.SA_ERR_INVALID_ARG), (dict(tau_mode=2), B.SA_ERR_INVALID_ARG),
+    (dict(tau=float("nan")), B.SA_ERR_INVALID_ARG), (dict(tau_mode=3), B.SA_ERR_INVALID_ARG), (dict(tau_mode=-1), B.SA_ERR_INVALID_ARG),
     (dict(max_keep=-1), B.SA_ERR_INVALID_ARG), (dict(n_dense_prefix=1001), B.SA_ERR_INVALID_ARG),
     (dict(dtype=5), B.SA_ERR_INVALID_ARG), (dict(flags=8), B.SA_ERR_INVALID_ARG),
     (dict(scale=-1.0), B.SA_ERR_INVALID_ARG), (dict(d=96), B.SA_ERR_UNSUPPORTED),

@@ -73,6 +73,11 @@ SMALL = [
     ("n63", (1, 7, 9), 64, 64, 64, "bf16", 0.05, R.RELATIVE, 0, 1, 0, False, 1, 1),
     ("n130", (1, 10, 13), 128, 128, 64, "bf16", 0.05, R.ABSOLUTE, 0, 1, 0, False, 1, 1),
     ("big_prefix", (2, 5, 20), 128, 128, 64, "bf16", 0.03, R.RELATIVE, 2, 1, 300, False, 1, 1),
+    ("topp", (4, 8, 32), 128, 128, 64, "bf16", 0.05, R.TOPP, 0, 1, 0, False, 1, 2),
+    ("topp_cap_prefix", (3, 8, 27), 128, 128, 128, "bf16", 0.02, R.TOPP, 3, 1, 100, True, 1, 2),
+    ("topp_f32_floor", (4, 8, 16), 64, 64, 64, "f32", 0.6, R.TOPP, 0, 2, 0, False, 1, 1),
+    ("topp_all", (2, 8, 20), 128, 128, 64, "bf16", 0.0, R.TOPP, 0, 1, 0, False, 1, 1),
+    ("topp_none", (2, 8, 20), 128, 128, 64, "bf16", 1.0, R.TOPP, 0, 0, 0, False, 1, 1),
 ]
 
 

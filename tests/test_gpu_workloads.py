@@ -42,10 +42,12 @@ def check_workload(w, cfgs, heads, blocks_per_head=6):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("mode", [R.RELATIVE, R.ABSOLUTE])
+@pytest.mark.parametrize("mode", [R.RELATIVE, R.ABSOLUTE, R.TOPP])
 def test_wan13b_full(mode):
     w = S.WORKLOADS["wan1.3b"]
-    check_workload(w, [cfg_for(w, mode=mode)], [(0, h) for h in range(w.H)], blocks_per_head=6)
+    # TOPP retains 1 - tau of the proxy mass: tau = 0.1 here (0.01 would keep ~95%)
+    cfg = cfg_for(w, mode=mode, tau=0.1 if mode == R.TOPP else None)
+    check_workload(w, [cfg], [(0, h) for h in range(w.H)], blocks_per_head=6)
 
 
 def test_wan14b_tau_sweep():

@@ -144,6 +144,9 @@ BRUTE = [  # N, d, bq, bk, prefix, tau, mode, max_keep, min_keep
     (9, 4, 2, 4, 0, 0.2, 0, 2, 1), (16, 4, 4, 4, 5, 0.6, 0, 0, 1), (23, 5, 4, 3, 0, 0.05, 1, 3, 2),
     (31, 3, 8, 4, 0, 1.5, 0, 0, 0), (31, 3, 8, 4, 0, 1.5, 1, 0, 2), (40, 6, 8, 8, 9, 0.02, 1, 2, 1), (40, 6, 8, 4, 16, 0.3, 0, 0, 1),
     (64, 4, 16, 8, 0, 0.01, 0, 4, 1), (64, 4, 8, 16, 0, 0.25, 1, 0, 1), (33, 2, 4, 4, 0, 0.7, 0, 5, 3),
+    # TOPP: shortest ranking prefix with proxy mass >= 1 - tau
+    (40, 6, 8, 4, 0, 0.1, 2, 0, 1), (64, 4, 8, 8, 0, 0.3, 2, 3, 1), (33, 5, 4, 4, 9, 0.05, 2, 0, 2),
+    (31, 3, 8, 4, 0, 1.0, 2, 0, 0), (23, 4, 4, 2, 0, 0.0, 2, 0, 1),
 ]
 
 
@@ -223,6 +226,38 @@ def test_absolute_keeps_at_most_inverse_tau(tau):
     # the bound is tight enough to matter: the flat rows would otherwise keep more
     p_rel = R.RouteParams(64, 32, tau, R.RELATIVE, min_keep=0)
     assert R.route_ref(q, k, p_rel).mask.sum(axis=1).max() > math.floor(1.0 / tau)
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("tau", [0.05, 0.3, 0.7])
+def test_topp_is_smallest_set_reaching_the_mass(seed, tau):
+    """TOPP keeps a minimum-cardinality set of key blocks whose proxy mass reaches
+    1 - tau (found by enumerating subsets), and of those the one of largest mass."""
+    N, d, bq, bk = 80, 8, 8, 8                       # n_kb = 10
+    q, k, v = rand_qkv(N, d, 700 + seed, qs=2.0)
+    p = R.RouteParams(bq, bk, tau, R.TOPP, min_keep=0)
+    rt = R.route_ref(q, k, p)
+    for I in range(rt.mask.shape[0]):
+        P = rt.r[I]
+        assert abs(P.sum() - 1.0) < 1e-12
+        kept = set(np.flatnonzero(rt.mask[I]).tolist())
+        size = next(n for n in range(len(P) + 1)
+                    if any(sum(P[j] for j in S) >= 1 - tau for S in itertools.combinations(range(len(P)), n)))
+        assert len(kept) == size
+        best = max(itertools.combinations(range(len(P)), size), key=lambda S: (sum(P[j] for j in S), [-j for j in S]))
+        assert kept == set(best)
+
+
+def test_topp_tau_zero_is_dense():
+    """TOPP with tau = 0 needs the whole proxy mass: every block is kept (no proxy
+    probability underflows at this scale) and the output is dense attention."""
+    q, k, v = rand_qkv(96, 8, 21, qs=1.0)
+    p = R.RouteParams(16, 8, 0.0, R.TOPP)
+    rt = R.route_ref(q, k, p)
+    assert rt.mask.all()
+    O, L = R.forward_ref(q, k, v, p)
+    Od, Ld = R.dense_ref(q, k, v)
+    assert np.abs(O - Od).max() < 1e-12 and np.abs(L - Ld).max() < 1e-12
 
 
 @pytest.mark.parametrize("tau", [1.0, 0.5, 0.01])
