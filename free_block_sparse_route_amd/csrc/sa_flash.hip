@@ -75,12 +75,16 @@ struct TileDesc {
 };
 
 // The tile sequence of one work item; every thread steps it identically and
-// every field is wave-uniform.  The kept-block index and the mask word are
-// fetched one step ahead, so their memory latency is hidden behind a tile
-// instead of delaying the next tile's loads.
+// every field is wave-uniform.  The kept list and the mask words are read
+// through the scalar cache (constant address space: the route wrote them before
+// this kernel started and nothing changes them during it), one entry ahead of
+// use, so that the read is in flight during a whole step and no step waits on
+// the vector-memory counter, which also counts the tile loads in flight.
+template <typename X> using kconst = __attribute__((address_space(4))) X;
+
 struct TileStream {
-    const int32_t *list;
-    const uint32_t *mask;
+    const kconst<int32_t> *list;
+    const kconst<uint32_t> *mask;
     int cnt, li, sub;
     int exact_rows, exact_kind;
     int dense_tiles, t;
@@ -89,10 +93,10 @@ struct TileStream {
     uint32_t w_cur, w_pf;     // mask words rt and rt + 1
 
     __device__ void prime() {
-        J_cur = cnt > 0 ? __builtin_amdgcn_readfirstlane(list[0]) : 0;
-        J_pf = cnt > 1 ? __builtin_amdgcn_readfirstlane(list[1]) : 0;
-        w_cur = n_rt > 0 ? (uint32_t)__builtin_amdgcn_readfirstlane(mask[0]) : 0u;
-        w_pf = n_rt > 1 ? (uint32_t)__builtin_amdgcn_readfirstlane(mask[1]) : 0u;
+        J_cur = cnt > 0 ? list[0] : 0;
+        J_pf = cnt > 1 ? list[1] : 0;
+        w_cur = n_rt > 0 ? mask[0] : 0u;
+        w_pf = n_rt > 1 ? mask[1] : 0u;
     }
 
     __device__ bool next(TileDesc &o, const FlashArgs &a) {
@@ -115,7 +119,7 @@ struct TileStream {
                 ++li;
                 sub = 0;
                 J_cur = J_pf;
-                J_pf = li + 1 < cnt ? __builtin_amdgcn_readfirstlane(list[li + 1]) : 0;
+                J_pf = list[min(li + 1, cnt - 1)];   // unconditional: the load lands in J_pf's register
             }
             if (tok0 < b1) {
                 o.kind = exact_kind;
@@ -128,7 +132,7 @@ struct TileStream {
             const int cur = rt++;
             const uint32_t bits = w_cur;
             w_cur = w_pf;
-            w_pf = rt + 1 < n_rt ? (uint32_t)__builtin_amdgcn_readfirstlane(mask[rt + 1]) : 0u;
+            w_pf = mask[min(rt + 1, n_rt - 1)];
             const int lim = a.n_kb - cur * 32;
             const uint32_t vmask = lim >= 32 ? ~0u : ((1u << lim) - 1u);
             if ((~bits & vmask) != 0) {
@@ -614,9 +618,9 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
     ts.dense_tiles = (a.N + ts.exact_rows - 1) / ts.exact_rows;
     const size_t row_id = (size_t)bh * a.n_qb + I;
     if constexpr (kSparse) {
-        ts.list = a.kv_idx + row_id * a.kv_idx_cap;
+        ts.list = (const kconst<int32_t> *)(a.kv_idx + row_id * a.kv_idx_cap);
         ts.cnt = __builtin_amdgcn_readfirstlane(a.kv_count[row_id]);
-        ts.mask = a.kv_mask + row_id * a.mask_words;
+        ts.mask = (const kconst<uint32_t> *)(a.kv_mask + row_id * a.mask_words);
         ts.n_rt = (a.residual && ts.cnt < a.n_kb) ? a.mask_words : 0;   // all kept: no residual
     } else {
         ts.list = nullptr;
