@@ -63,18 +63,45 @@ __device__ __forceinline__ uint32_t orderable(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Wave-wide reductions on the VALU, every lane receiving the result: DPP
+// swaps lanes within quads (xor 1, xor 2), mirrors within 8 and 16 lanes, and
+// v_permlane16/32_swap exchange rows and halves.  Each step combines two
+// values that every lane of the pair sees in the same order, so all lanes end
+// with bit-identical results.  Call from wave-uniform control flow only.
+__device__ __forceinline__ float dpp_f(float x, int ctrl) {
+    switch (ctrl) {   // the control must be a constant of the builtin
+        case 0xB1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+        case 0x4E: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+        case 0x141: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+        default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+    }
+}
+
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+    v = op(v, dpp_f(v, 0xB1));        // quad_perm [1,0,3,2]
+    v = op(v, dpp_f(v, 0x4E));        // quad_perm [2,3,0,1]
+    v = op(v, dpp_f(v, 0x141));       // row_half_mirror: the other quad of 8
+    v = op(v, dpp_f(v, 0x140));       // row_mirror: the other 8 of 16
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+    return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    return wave_reduce(v, [](float x, float y) { return x + y; });
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Constant address space: loads through it at a wave-uniform address go
+// through the scalar cache.  Only for memory that nothing writes while the
+// kernel runs (buffers a previous kernel wrote).
+template <typename X> using kconst = __attribute__((address_space(4))) X;
 
 }  // namespace sa

@@ -80,8 +80,6 @@ struct TileDesc {
 // this kernel started and nothing changes them during it), one entry ahead of
 // use, so that the read is in flight during a whole step and no step waits on
 // the vector-memory counter, which also counts the tile loads in flight.
-template <typename X> using kconst = __attribute__((address_space(4))) X;
-
 struct TileStream {
     const kconst<int32_t> *list;
     const kconst<uint32_t> *mask;

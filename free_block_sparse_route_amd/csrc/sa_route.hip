@@ -27,7 +27,8 @@ namespace sa {
 
 constexpr int kPoolThreads = 256;
 constexpr int kSelectThreads = 256;
-constexpr int kOrderThreads = 512;
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderTiles = 448;         // 32 x 448 counters: 56 KB of LDS
 constexpr int kBands = 32;               // floor(log2(cost)) of a non-negative int32
 
 // --------------------------------------------------------------------- pool
@@ -101,10 +102,18 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const T *__restrict_
 }
 
 // --------------------------------------------------------------------- select
+// e^x and ln x on the hardware base-2 exponential and logarithm (a few ulp;
+// the proxy decisions carry a 1e-4 exemption band)
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+__device__ __forceinline__ float fast_log(float x) { return __builtin_amdgcn_logf(x) * 0.693147180559945309f; }
+
 __device__ __forceinline__ uint64_t lanes_below() {
     const int l = lane_id();
     return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
+
+// Sum over the wave of small per-lane counts (exact: far below 2^24).
+__device__ __forceinline__ int wave_count(int c) { return (int)wave_sum((float)c); }
 
 // Number of row entries whose key is >= kmin (wave-uniform result).
 __device__ __forceinline__ int count_ge(const float *S, int n, uint32_t kmin) {
@@ -121,73 +130,18 @@ __device__ __forceinline__ int count_ge(const float *S, int n, uint32_t kmin) {
 __device__ __forceinline__ float mass_ge(const float *S, int n, uint32_t kmin, float lse) {
     float ms = 0.f;
     for (int J = lane_id(); J < n; J += kWave)
-        if (orderable(S[J]) >= kmin) ms += expf(S[J] - lse);
+        if (orderable(S[J]) >= kmin) ms += fast_exp(S[J] - lse);
     return wave_sum(ms);
 }
 
-// Rows longer than 20 * 64 key blocks: the same steps, reading the row from LDS.
-__device__ __forceinline__ void select_row_lds(const float *S, int bh, int I, const SelectArgs &a) {
+// Kept list, bit mask, count, statistics and cost of one proxy row read from
+// LDS.  With ksel > 0 the row keeps the keys above T and the first take_eq keys
+// equal to T in J order; otherwise the entries at or above thr (none for TOPP).
+// Blocks of the dense prefix are always kept.
+__device__ __forceinline__ void compact_row_lds(const float *S, int bh, int I, const SelectArgs &a, int ksel,
+                                                uint32_t T, int take_eq, float thr, float m, float lse) {
     const int lane = lane_id();
     const int n = a.n_kb;
-    float m = -INFINITY;
-    for (int J = lane; J < n; J += kWave) m = fmaxf(m, S[J]);
-    m = wave_max(m);
-    float z = 0.f;
-    for (int J = lane; J < n; J += kWave) z += expf(S[J] - m);
-    z = wave_sum(z);
-    const float lse = m + logf(z);
-    const float thr = (a.tau_mode == SA_TAU_ABSOLUTE ? lse : m) + a.ln_tau;
-
-    int n_c = 0;
-    if (a.tau_mode == SA_TAU_TOPP) {
-        // length of the ranking prefix whose preceding proxy mass stays below
-        // the target (see the register version below)
-        const float target = a.topp_target;
-        if (target > 0.f) {
-            uint32_t Ts = 0;
-            for (int bit = 31; bit >= 0; --bit) {
-                const uint32_t cand = Ts | (1u << bit);
-                if (mass_ge(S, n, cand, lse) >= target) Ts = cand;
-            }
-            if (Ts == 0u) {
-                n_c = n;
-            } else {
-                const float mgt = Ts == 0xffffffffu ? 0.f : mass_ge(S, n, Ts + 1, lse);
-                const int ngt = Ts == 0xffffffffu ? 0 : count_ge(S, n, Ts + 1);
-                const int neq = count_ge(S, n, Ts) - ngt;
-                float peq = 0.f;
-                for (int J = lane; J < n; J += kWave)
-                    if (orderable(S[J]) == Ts) peq = expf(S[J] - lse);
-                peq = wave_max(peq);
-                int teq = 1;
-                while (teq < neq && mgt + (float)teq * peq < target) ++teq;
-                n_c = ngt + teq;
-            }
-        }
-    } else {
-        for (int base = 0; base < n; base += kWave) {
-            const int J = base + lane;
-            n_c += __popcll(__ballot(J < n && S[J] >= thr));
-        }
-    }
-    int ksel = 0;
-    if (a.max_keep > 0 && n_c > a.max_keep) ksel = a.max_keep;
-    else if (n_c < a.min_keep) ksel = min(a.min_keep, n);
-    else if (a.tau_mode == SA_TAU_TOPP) ksel = n_c;         // a ranking prefix of n_c blocks
-
-    // ksel-th largest key T, built bit by bit from the top: the largest T with
-    // #{key >= T} >= ksel.  Equal keys beyond the budget are resolved by J.
-    uint32_t T = 0;
-    int take_eq = 0;
-    if (ksel > 0) {
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = T | (1u << bit);
-            if (count_ge(S, n, cand) >= ksel) T = cand;
-        }
-        const int n_gt = (T == 0xffffffffu) ? 0 : count_ge(S, n, T + 1);
-        take_eq = ksel - n_gt;
-    }
-
     const size_t row = (size_t)bh * a.n_qb + I;
     int32_t *idx = a.kv_idx + row * a.kv_idx_cap;
     uint32_t *mask = a.kv_mask + row * a.mask_words;
@@ -232,22 +186,95 @@ __device__ __forceinline__ void select_row_lds(const float *S, int bh, int I, co
     }
 }
 
+// Rows longer than 20 * 64 key blocks: the same steps, reading the row from LDS.
+__device__ __forceinline__ void select_row_lds(const float *S, int bh, int I, const SelectArgs &a) {
+    const int lane = lane_id();
+    const int n = a.n_kb;
+    float m = -INFINITY;
+    for (int J = lane; J < n; J += kWave) m = fmaxf(m, S[J]);
+    m = wave_max(m);
+    float z = 0.f;
+    for (int J = lane; J < n; J += kWave) z += fast_exp(S[J] - m);
+    z = wave_sum(z);
+    const float lse = m + fast_log(z);
+    const float thr = (a.tau_mode == SA_TAU_ABSOLUTE ? lse : m) + a.ln_tau;
+
+    int n_c = 0;
+    if (a.tau_mode == SA_TAU_TOPP) {
+        // length of the ranking prefix whose preceding proxy mass stays below
+        // the target (see the register version below)
+        const float target = a.topp_target;
+        if (target > 0.f) {
+            uint32_t Ts = 0;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t cand = Ts | (1u << bit);
+                if (mass_ge(S, n, cand, lse) >= target) Ts = cand;
+            }
+            if (Ts == 0u) {
+                n_c = n;
+            } else {
+                const float mgt = Ts == 0xffffffffu ? 0.f : mass_ge(S, n, Ts + 1, lse);
+                const int ngt = Ts == 0xffffffffu ? 0 : count_ge(S, n, Ts + 1);
+                const int neq = count_ge(S, n, Ts) - ngt;
+                float peq = 0.f;
+                for (int J = lane; J < n; J += kWave)
+                    if (orderable(S[J]) == Ts) peq = fast_exp(S[J] - lse);
+                peq = wave_max(peq);
+                int teq = 1;
+                while (teq < neq && mgt + (float)teq * peq < target) ++teq;
+                n_c = ngt + teq;
+            }
+        }
+    } else {
+        for (int base = 0; base < n; base += kWave) {
+            const int J = base + lane;
+            n_c += __popcll(__ballot(J < n && S[J] >= thr));
+        }
+    }
+    int ksel = 0;
+    if (a.max_keep > 0 && n_c > a.max_keep) ksel = a.max_keep;
+    else if (n_c < a.min_keep) ksel = min(a.min_keep, n);
+    else if (a.tau_mode == SA_TAU_TOPP) ksel = n_c;         // a ranking prefix of n_c blocks
+
+    // ksel-th largest key T, built bit by bit from the top: the largest T with
+    // #{key >= T} >= ksel.  Equal keys beyond the budget are resolved by J.
+    uint32_t T = 0;
+    int take_eq = 0;
+    if (ksel > 0) {
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = T | (1u << bit);
+            if (count_ge(S, n, cand) >= ksel) T = cand;
+        }
+        const int n_gt = (T == 0xffffffffu) ? 0 : count_ge(S, n, T + 1);
+        take_eq = ksel - n_gt;
+    }
+
+    compact_row_lds(S, bh, I, a, ksel, T, take_eq, thr, m, lse);
+}
+
 // One proxy row: statistics, the tau test, the cap or floor, the kept list,
 // bit mask and cost.  The lane holds scores J = lane + 64 i, i < R, in registers
 // (R * 64 >= n_kb): every pass over the row, in particular the 32 counting
 // passes of the cap's k-th-largest search, runs on registers.
 template <int R>
 __device__ __forceinline__ void select_row(const float *S, int bh, int I, const SelectArgs &a) {
-    const int lane = lane_id();
-    const int n = a.n_kb;
-    // absent entries (J >= n) hold -inf and key 0, below every real key
+    // Per-row copies the compiler cannot hoist out of the caller's loop over
+    // rows: per-chunk conditions derived from them would otherwise stay live
+    // across rows (as 64-bit lane masks) and spill.
+    int lane = lane_id(), n = a.n_kb;
+    asm volatile("" : "+v"(lane));
+    asm volatile("" : "+s"(n));
+    // Absent entries (J >= n) hold -inf: weight 0, and a key below every
+    // finite score's, so no count or budget search that ends at a real key
+    // includes them.  No per-entry validity mask is kept: held for every
+    // chunk, such masks fill the scalar registers.
     float sv[R];
     uint32_t key[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         const int J = i * kWave + lane;
         sv[i] = J < n ? S[J] : -INFINITY;
-        key[i] = J < n ? orderable(sv[i]) : 0u;
+        key[i] = orderable(sv[i]);
     }
     float m = -INFINITY;
 #pragma unroll
@@ -256,10 +283,12 @@ __device__ __forceinline__ void select_row(const float *S, int bh, int I, const 
     float z = 0.f;
 #pragma unroll
     for (int i = 0; i < R; ++i)
-        if (key[i] != 0u) z += expf(sv[i] - m);
+        z += fast_exp(sv[i] - m);
     z = wave_sum(z);
-    const float lse = m + logf(z);
-    const float thr = (a.tau_mode == SA_TAU_ABSOLUTE ? lse : m) + a.ln_tau;
+    const float lse = m + fast_log(z);
+    // tau = 0 gives thr = -inf; clamped to the lowest finite value it keeps
+    // every real entry and no absent one
+    const float thr = fmaxf((a.tau_mode == SA_TAU_ABSOLUTE ? lse : m) + a.ln_tau, -3.40282347e38f);   // lowest finite float
 
     int n_c = 0;
     uint32_t T = 0;
@@ -273,7 +302,7 @@ __device__ __forceinline__ void select_row(const float *S, int bh, int I, const 
         const float target = a.topp_target;
         float pv[R];
 #pragma unroll
-        for (int i = 0; i < R; ++i) pv[i] = key[i] != 0u ? expf(sv[i] - lse) : 0.f;
+        for (int i = 0; i < R; ++i) pv[i] = fast_exp(sv[i] - lse);
         if (target > 0.f) {
             uint32_t Ts = 0;
             for (int bit = 31; bit >= 0; --bit) {
@@ -292,10 +321,12 @@ __device__ __forceinline__ void select_row(const float *S, int bh, int I, const 
                 for (int i = 0; i < R; ++i) {
                     mgt += key[i] > Ts ? pv[i] : 0.f;
                     peq = key[i] == Ts ? pv[i] : peq;
-                    ngt += __popcll(__ballot(key[i] > Ts));
-                    neq += __popcll(__ballot(key[i] == Ts));
+                    ngt += key[i] > Ts;
+                    neq += key[i] == Ts;
                 }
                 mgt = wave_sum(mgt);
+                ngt = wave_count(ngt);
+                neq = wave_count(neq);
                 peq = wave_max(peq);
                 int teq = 1;
                 while (teq < neq && mgt + (float)teq * peq < target) ++teq;
@@ -307,7 +338,8 @@ __device__ __forceinline__ void select_row(const float *S, int bh, int I, const 
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < R; ++i) n_c += __popcll(__ballot(key[i] != 0u && sv[i] >= thr));
+        for (int i = 0; i < R; ++i) n_c += sv[i] >= thr;
+        n_c = wave_count(n_c);
     }
     int ksel = 0;
     if (a.max_keep > 0 && n_c > a.max_keep) ksel = a.max_keep;
@@ -324,49 +356,57 @@ __device__ __forceinline__ void select_row(const float *S, int bh, int I, const 
             const uint32_t cand = T | (1u << bit);
             int cnt = 0;
 #pragma unroll
-            for (int i = 0; i < R; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-            if (cnt >= ksel) T = cand;
+            for (int i = 0; i < R; ++i) cnt += key[i] >= cand;
+            if (wave_count(cnt) >= ksel) T = cand;
         }
         int n_gt = 0;
         if (T != 0xffffffffu)
 #pragma unroll
-            for (int i = 0; i < R; ++i) n_gt += __popcll(__ballot(key[i] > T));
-        take_eq = ksel - n_gt;
+            for (int i = 0; i < R; ++i) n_gt += key[i] > T;
+        take_eq = ksel - wave_count(n_gt);
     }
 
+    // Equal keys at T split by the budget (rare): rank them in J order on the
+    // LDS copy of the row.  Otherwise the kept set is every key >= T.
+    if (ksel > 0) {
+        int n_eq = 0;
+#pragma unroll
+        for (int i = 0; i < R; ++i) n_eq += key[i] == T;
+        if (take_eq < wave_count(n_eq)) {
+            compact_row_lds(S, bh, I, a, ksel, T, take_eq, thr, m, lse);
+            return;
+        }
+    }
     const size_t row = (size_t)bh * a.n_qb + I;
     int32_t *idx = a.kv_idx + row * a.kv_idx_cap;
     uint32_t *mask = a.kv_mask + row * a.mask_words;
-    const bool dense_row = (int64_t)I * a.block_q < a.n_prefix;
-    const int last_cnt = a.N - (n - 1) * a.block_k;
-    int kept = 0, eq_seen = 0, tiles = 0;
+    int lv = lane, n_prefix = a.n_prefix, block_k = a.block_k;   // per-row copies, as above
+    asm volatile("" : "+s"(n_prefix), "+s"(block_k));
+    const bool dense_row = (int64_t)I * a.block_q < n_prefix;
+    const int rows = a.exact_tile_rows;
+    const int t_full = (block_k + rows - 1) / rows;
+    const int t_last = (a.N - (n - 1) * block_k + rows - 1) / rows;
+    int kept = 0, tiles = 0;
+    uint32_t word = 0u;                 // lane w ends with mask word w
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-        const int J = i * kWave + lane;
-        const bool valid = key[i] != 0u;
-        bool keep;
-        if (ksel > 0) {
-            const bool eq = valid && key[i] == T;
-            const uint64_t be = __ballot(eq);
-            const int rank = eq_seen + __popcll(be & lanes_below());
-            eq_seen += __popcll(be);
-            keep = valid && (key[i] > T || (eq && rank < take_eq));
-        } else {
-            keep = valid && a.tau_mode != SA_TAU_TOPP && sv[i] >= thr;   // TOPP: n_c = 0
-        }
-        keep = valid && (keep || dense_row || (int64_t)J * a.block_k < a.n_prefix);
+        const int J = i * kWave + lv;
+        // ksel > 0: T is a real entry's key, above every absent one
+        bool keep = ksel > 0 ? key[i] >= T : a.tau_mode != SA_TAU_TOPP && sv[i] >= thr;   // TOPP: n_c = 0
+        keep = keep || (dense_row && sv[i] > -INFINITY) || (int64_t)J * block_k < n_prefix;
         const uint64_t bk = __ballot(keep);
         if (keep) idx[kept + __popcll(bk & lanes_below())] = J;
         kept += __popcll(bk);
-        const int w = 2 * i;
-        if (lane == 0 && w < a.mask_words) mask[w] = (uint32_t)bk;
-        if (lane == 1 && w + 1 < a.mask_words) mask[w + 1] = (uint32_t)(bk >> 32);
-        // cost: exact tiles of kept blocks, plus one residual tile per 32 pooled
-        // blocks (one mask word) that holds a dropped block
-        const int nj = (J == n - 1) ? last_cnt : a.block_k;
-        tiles += keep ? (nj + a.exact_tile_rows - 1) / a.exact_tile_rows : 0;
-        const uint64_t bd = __ballot(valid && !keep);
-        if (lane == 0) tiles += ((uint32_t)bd != 0) + ((uint32_t)(bd >> 32) != 0);
+        word = lv == 2 * i ? (uint32_t)bk : lv == 2 * i + 1 ? (uint32_t)(bk >> 32) : word;
+        // cost: exact tiles of the kept blocks
+        tiles += keep ? (J == n - 1 ? t_last : t_full) : 0;
+    }
+    // plus one residual tile per mask word that holds a dropped block
+    if (lv < a.mask_words) {
+        mask[lv] = word;
+        const int lim = n - 32 * lv;
+        const uint32_t vmask = lim >= 32 ? ~0u : ((1u << lim) - 1u);
+        tiles += (~word & vmask) != 0u;
     }
     tiles = (int)wave_sum((float)tiles);
     if (lane == 0) {
@@ -377,7 +417,17 @@ __device__ __forceinline__ void select_row(const float *S, int bh, int I, const 
     }
 }
 
-template <int D, int G>
+__device__ __forceinline__ void launder(SelectArgs &a) {
+    asm volatile("" : "+s"(a.N), "+s"(a.block_q), "+s"(a.block_k), "+s"(a.n_qb), "+s"(a.n_kb), "+s"(a.mask_words));
+    asm volatile("" : "+s"(a.kv_idx_cap), "+s"(a.exact_tile_rows), "+s"(a.tau_mode), "+s"(a.max_keep),
+                 "+s"(a.min_keep), "+s"(a.n_prefix));
+    asm volatile("" : "+s"(a.scale), "+s"(a.ln_tau), "+s"(a.topp_target));
+    asm volatile("" : "+s"(a.kv_count), "+s"(a.kv_idx), "+s"(a.cost), "+s"(a.kv_mask), "+s"(a.row_stats));
+}
+
+// R: proxy row chunks of 64 held in registers (R * 64 >= n_kb), 0: longer rows
+// are read from LDS.
+template <int D, int G, int R>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     extern __shared__ __attribute__((aligned(16))) float smem[];
     const int bh = blockIdx.y;
@@ -385,84 +435,153 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     const int g_cnt = min(G, a.n_qb - I0);
     const int n = a.n_kb;
     float *S = smem;                                      // [G][n]
-    float *QB = smem + ((G * n + 3) & ~3);                // [G][D]
-    for (int i = threadIdx.x; i < G * D; i += kSelectThreads)
-        QB[i] = (i / D) < g_cnt ? a.q_mean[((size_t)bh * a.n_qb + I0) * D + i] : 0.f;
-    __syncthreads();
-    const float *kb = a.k_mean + (size_t)bh * n * D;
-    for (int J = threadIdx.x; J < n; J += kSelectThreads) {
-        float acc[G];
+    {
+        // Proxy rows on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, fp32
+        // products and sums): a wave takes 16 key blocks at a time and forms
+        // their scores against the group's (up to 16) query blocks.  Lane
+        // (i16, kg) supplies key block i16 and query block i16 at features
+        // kg * KS + s in MFMA step s (s even and odd on two accumulators);
+        // result register r is key block 4 kg + r against query block i16.
+        const int lane = lane_id();
+        const int wave0 = threadIdx.x / kWave;
+        const int i16 = lane & 15, kg = lane >> 4;
+        constexpr int KS = D / 4;
+        float qv[KS];
+        {
+            const bool ok = i16 < g_cnt;
+            const float *src = a.q_mean + ((size_t)bh * a.n_qb + I0 + (ok ? i16 : 0)) * D + kg * KS;
 #pragma unroll
-        for (int g = 0; g < G; ++g) acc[g] = 0.f;
-        const float *kr = kb + (size_t)J * D;
-#pragma unroll 4
-        for (int c = 0; c < D; c += 4) {
-            const f32x4 kv = *reinterpret_cast<const f32x4 *>(kr + c);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const f32x4 qv = *reinterpret_cast<const f32x4 *>(QB + g * D + c);
-                acc[g] = fmaf(qv[0], kv[0], acc[g]);
-                acc[g] = fmaf(qv[1], kv[1], acc[g]);
-                acc[g] = fmaf(qv[2], kv[2], acc[g]);
-                acc[g] = fmaf(qv[3], kv[3], acc[g]);
+            for (int e = 0; e < KS; e += 4) {
+                const f32x4 x = ok ? *reinterpret_cast<const f32x4 *>(src + e) : f32x4{};
+                qv[e] = x[0];
+                qv[e + 1] = x[1];
+                qv[e + 2] = x[2];
+                qv[e + 3] = x[3];
             }
         }
+        const float *kb = a.k_mean + (size_t)bh * n * D;
+        const int n_sl = (n + 15) / 16;
+        constexpr int kStride = kSelectThreads / kWave;
+        auto load_slice = [&](int sl, float (&kv)[KS]) {
+            const int J = sl * 16 + i16;
+            const float *src = kb + (size_t)(J < n ? J : 0) * D + kg * KS;
 #pragma unroll
-        for (int g = 0; g < G; ++g) S[g * n + J] = acc[g] * a.scale;
+            for (int e = 0; e < KS; e += 4) {
+                const f32x4 x = J < n ? *reinterpret_cast<const f32x4 *>(src + e) : f32x4{};
+                kv[e] = x[0];
+                kv[e + 1] = x[1];
+                kv[e + 2] = x[2];
+                kv[e + 3] = x[3];
+            }
+        };
+        float kv[KS], kn[KS];
+        if (wave0 < n_sl) load_slice(wave0, kv);
+        for (int sl = wave0; sl < n_sl; sl += kStride) {
+            if (sl + kStride < n_sl) load_slice(sl + kStride, kn);     // the next slice's keys in flight
+            f32x4 acc0 = {}, acc1 = {};
+#pragma unroll
+            for (int e = 0; e < KS; e += 2) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[e], qv[e], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[e + 1], qv[e + 1], acc1, 0, 0, 0);
+            }
+            if (i16 < g_cnt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int Jr = sl * 16 + 4 * kg + r;
+                    if (Jr < n) S[i16 * n + Jr] = (acc0[r] + acc1[r]) * a.scale;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < KS; ++e) kv[e] = kn[e];
+        }
     }
     __syncthreads();
     const int wave = threadIdx.x / kWave;
-    const int chunks = (n + kWave - 1) / kWave;        // uniform over the launch
     for (int g = wave; g < g_cnt; g += kSelectThreads / kWave) {
+        // A copy of the arguments the compiler must re-read every row, so that
+        // nothing derived from them is hoisted out of this loop and held in
+        // scalar registers across rows (it would spill).
+        SelectArgs ar = a;
+        launder(ar);
         const float *row = S + g * n;
-        if (chunks <= 2) select_row<2>(row, bh, I0 + g, a);
-        else if (chunks <= 4) select_row<4>(row, bh, I0 + g, a);
-        else if (chunks <= 8) select_row<8>(row, bh, I0 + g, a);
-        else if (chunks <= 16) select_row<16>(row, bh, I0 + g, a);
-        else if (chunks <= 20) select_row<20>(row, bh, I0 + g, a);
-        else select_row_lds(row, bh, I0 + g, a);
+        if constexpr (R > 0) select_row<R>(row, bh, I0 + g, ar);
+        else select_row_lds(row, bh, I0 + g, ar);
     }
 }
 
 // --------------------------------------------------------------------- order
 __device__ __forceinline__ int cost_band(int32_t c) { return c > 1 ? 31 - __clz(c) : 0; }
 
-// One workgroup.  Thread t owns the items of one contiguous chunk; cnt[r][t]
-// counts its items in row r = kBands-1-band (row 0: highest band).  The
-// exclusive prefix over cnt in (row, thread) order is then where thread t
-// writes its first item of row r, which makes the sort stable.
+// One workgroup of 16 waves.  The items are cut into at most kOrderTiles
+// tiles of consecutive items (64 * m each); a wave owns whole tiles and reads
+// them 64 items at a time (coalesced).  Pass 1 counts each tile's items per
+// band row r = kBands-1-band (row 0: highest band); the exclusive prefix over
+// the counts in (row, tile) order is where a tile's first item of row r goes;
+// pass 2 places the items, ranking equal rows within 64 items by lane.  The
+// order is therefore by row, then by item: a stable sort.
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *cost, int32_t *work_order, int W) {
-    __shared__ int32_t cnt[kBands * kOrderThreads];
-    __shared__ int32_t part[kOrderThreads];
-    const int t = threadIdx.x;
-    const int chunk = (W + kOrderThreads - 1) / kOrderThreads;
-    const int i0 = min(W, t * chunk), i1 = min(W, i0 + chunk);
-    for (int r = 0; r < kBands; ++r) cnt[r * kOrderThreads + t] = 0;
-    for (int i = i0; i < i1; ++i) ++cnt[(kBands - 1 - cost_band(cost[i])) * kOrderThreads + t];
+    constexpr int NW = kOrderThreads / kWave;
+    constexpr int kCells = kBands * kOrderTiles;
+    constexpr int kPer = kCells / kOrderThreads;
+    static_assert(kCells % kOrderThreads == 0, "scan split");
+    __shared__ int32_t cnt[kCells];                       // [row][tile]
+    __shared__ int32_t part[NW];
+    if (W <= 0) return;
+    const int t = threadIdx.x, lane = lane_id(), wave = t / kWave;
+    const int m = (W + kWave * kOrderTiles - 1) / (kWave * kOrderTiles);   // 64-item chunks per tile
+    const int span = kWave * m;
+    const int n_tiles = (W + span - 1) / span;
+    for (int e = t; e < kCells; e += kOrderThreads) cnt[e] = 0;
     __syncthreads();
-    // thread t scans the kBands consecutive entries [t*kBands, (t+1)*kBands) of cnt
-    constexpr int kPer = kBands;   // kBands * kOrderThreads entries / kOrderThreads threads
+    for (int tile = wave; tile < n_tiles; tile += NW) {
+        for (int c = 0; c < m; ++c) {
+            const int i = tile * span + c * kWave + lane;
+            const int row = i < W ? kBands - 1 - cost_band(cost[i]) : -1;
+            uint64_t left = __ballot(row >= 0);
+            while (left) {
+                const int r = __builtin_amdgcn_readlane(row, __builtin_ctzll(left));
+                const uint64_t mr = __ballot(row == r);
+                if (lane == 0) cnt[r * kOrderTiles + tile] += __popcll(mr);
+                left &= ~mr;
+            }
+        }
+    }
+    __syncthreads();
+    // exclusive scan of cnt: thread t takes kPer consecutive cells
     int32_t *mine = cnt + t * kPer;
     int sum = 0;
     for (int e = 0; e < kPer; ++e) sum += mine[e];
-    part[t] = sum;
-    __syncthreads();
-    for (int off = 1; off < kOrderThreads; off <<= 1) {       // inclusive scan of part
-        const int v = t >= off ? part[t - off] : 0;
-        __syncthreads();
-        part[t] += v;
-        __syncthreads();
+    int incl = sum;                                        // inclusive scan within the wave
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
     }
-    int run = t > 0 ? part[t - 1] : 0;
+    if (lane == kWave - 1) part[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += part[w];
+    int run = before + incl - sum;
     for (int e = 0; e < kPer; ++e) {
         const int c = mine[e];
         mine[e] = run;
         run += c;
     }
     __syncthreads();
-    for (int i = i0; i < i1; ++i) {
-        const int slot = (kBands - 1 - cost_band(cost[i])) * kOrderThreads + t;
-        work_order[cnt[slot]++] = i;
+    for (int tile = wave; tile < n_tiles; tile += NW) {
+        for (int c = 0; c < m; ++c) {
+            const int i = tile * span + c * kWave + lane;
+            const int row = i < W ? kBands - 1 - cost_band(cost[i]) : -1;
+            uint64_t left = __ballot(row >= 0);
+            while (left) {
+                const int r = __builtin_amdgcn_readlane(row, __builtin_ctzll(left));
+                const uint64_t mr = __ballot(row == r);
+                const int base = cnt[r * kOrderTiles + tile];
+                if (row == r) work_order[base + __popcll(mr & lanes_below())] = i;
+                if (lane == 0) cnt[r * kOrderTiles + tile] = base + __popcll(mr);
+                left &= ~mr;
+            }
+        }
     }
 }
 
@@ -484,32 +603,48 @@ hipError_t launch_pool(int dtype, int D, const void *q, const void *k, const voi
                    : launch_pool_t<float, 128>(q, k, v, a, BH, st);
 }
 
+// Query blocks per select workgroup: as many proxy rows as the LDS budget
+// holds (each workgroup reads all mean keys of its head once), at most 16.
 int select_group(int n_kb, int D, int n_qb) {
-    int G = 8;
-    while (G > 1 && ((size_t)G * n_kb + 4 + (size_t)G * D) * 4 > kSelectLdsBudget) G /= 2;
-    while (G > 1 && G / 2 >= n_qb) G /= 2;
-    return G;
+    (void)D;
+    static const int kG[] = {16, 12, 8, 4, 1};
+    int i = 0;
+    while (kG[i] > 1 && select_lds_bytes(kG[i], n_kb, D) > kSelectLdsBudget) ++i;
+    while (kG[i] > 1 && kG[i + 1] >= n_qb) ++i;
+    return kG[i];
 }
 
 size_t select_lds_bytes(int G, int n_kb, int D) {
-    return (((size_t)G * n_kb + 3) / 4 * 4 + (size_t)G * D) * sizeof(float);
+    (void)D;
+    return ((size_t)G * n_kb + 3) / 4 * 4 * sizeof(float);
 }
 
-template <int D, int G>
+template <int D, int G, int R>
 static hipError_t launch_select_t(const SelectArgs &a, int BH, hipStream_t st) {
     const size_t lds = select_lds_bytes(G, a.n_kb, D);
     dim3 grid((a.n_qb + G - 1) / G, BH);
-    hipLaunchKernelGGL((select_kernel<D, G>), grid, dim3(kSelectThreads), lds, st, a);
+    hipLaunchKernelGGL((select_kernel<D, G, R>), grid, dim3(kSelectThreads), lds, st, a);
     return hipGetLastError();
+}
+
+template <int D, int G>
+static hipError_t launch_select_g(const SelectArgs &a, int BH, hipStream_t st) {
+    const int chunks = (a.n_kb + kWave - 1) / kWave;
+    if (chunks <= 4) return launch_select_t<D, G, 4>(a, BH, st);
+    if (chunks <= 8) return launch_select_t<D, G, 8>(a, BH, st);
+    if (chunks <= 16) return launch_select_t<D, G, 16>(a, BH, st);
+    if (chunks <= 20) return launch_select_t<D, G, 20>(a, BH, st);
+    return launch_select_t<D, G, 0>(a, BH, st);
 }
 
 template <int D>
 static hipError_t launch_select_d(const SelectArgs &a, int G, int BH, hipStream_t st) {
     switch (G) {
-        case 8: return launch_select_t<D, 8>(a, BH, st);
-        case 4: return launch_select_t<D, 4>(a, BH, st);
-        case 2: return launch_select_t<D, 2>(a, BH, st);
-        default: return launch_select_t<D, 1>(a, BH, st);
+        case 16: return launch_select_g<D, 16>(a, BH, st);
+        case 12: return launch_select_g<D, 12>(a, BH, st);
+        case 8: return launch_select_g<D, 8>(a, BH, st);
+        case 4: return launch_select_g<D, 4>(a, BH, st);
+        default: return launch_select_g<D, 1>(a, BH, st);
     }
 }
 
