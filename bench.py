@@ -50,6 +50,8 @@ def parse():
                          "collections of two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of this "
                          "script with --with-copy, then exit")
     ap.add_argument("--pmc-command", default="", help="the command the counter runs used (recorded)")
+    ap.add_argument("--cold-calls", type=int, default=20,
+                    help="calls timed one by one after flushing the caches with a 512 MiB write (0: skip)")
     return ap.parse_args()
 
 
@@ -200,6 +202,97 @@ def cpu_baseline(w, cfg, Qc, Kc, Vc, budget_s: float = 12.0):
             "ms_per_step_extrapolated": t_total * 1e3, "host_cores_visible": cores}
 
 
+def median(xs):
+    xs = sorted(xs)
+    k = len(xs)
+    return 0.5 * (xs[(k - 1) // 2] + xs[k // 2])
+
+
+FLUSH_BYTES = 512 << 20
+
+
+def cold_timing(sa, Q, K, V, rt, O, cfg, calls):
+    """Median route and forward times with cold caches: before each call a 512 MiB
+    buffer is written, which evicts the inputs from the L2s and the 256 MB
+    Infinity Cache.  The write is outside the timed events."""
+    import torch
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    r_ms, f_ms = [], []
+    for i in range(calls):
+        flush.fill_(float(i))
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        sa.route(Q, K, V, cfg, out=rt)
+        e[1].record()
+        flush.fill_(float(i) + 0.5)            # the forward, too, starts cold
+        e2 = torch.cuda.Event(enable_timing=True)
+        e2.record()
+        sa.forward(Q, K, V, rt, cfg, out=O)
+        e[2].record()
+        torch.cuda.synchronize()
+        r_ms.append(e[0].elapsed_time(e[1]))
+        f_ms.append(e2.elapsed_time(e[2]))
+    del flush
+    return {"route_ms_median": median(r_ms), "forward_ms_median": median(f_ms), "calls": calls,
+            "flush_bytes": FLUSH_BYTES}
+
+
+def permute_timing(sa, X, w, reps=10):
+    """Token reordering of one [B, H, N, d] tensor into the workload's Hilbert
+    order (gather) and back (scatter): median ms and GB/s, counting every row
+    read once and written once."""
+    import torch
+    perm = sa.hilbert_order(*w.grid).cuda()
+    Y = torch.empty_like(X)
+    Z = torch.empty_like(X)
+    res = {}
+    for name, src, dst, inv in (("gather", X, Y, False), ("scatter", Y, Z, True)):
+        sa.permute_tokens(src, perm, w.n_text, inverse=inv, out=dst)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            sa.permute_tokens(src, perm, w.n_text, inverse=inv, out=dst)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = median(ts)
+        gbs = 2.0 * X.numel() * X.element_size() / (ms * 1e-3) / 1e9
+        res[name] = {"ms_median": ms, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+    torch.cuda.synchronize()
+    assert torch.equal(Z, X), "permutation round trip"
+    return res
+
+
+def issued_mfma_flops(w, rt, mask, cfg):
+    """Matrix-core flops the forward kernel issues per launch, counting padded
+    rows: every query block runs block_q rows (the last one padded), every kept
+    key block ceil(n_J / rows) exact tiles of `rows` keys (padded), and every
+    group of 32 pooled blocks with a dropped one a residual tile.  Per wave
+    (32 query rows) a tile takes, in 32x32x16 bf16 MFMAs of 32768 flops:
+    bf16 exact d/4; bf16 residual 3d/16 (the value remainders are not read);
+    fp32 exact or residual 5d/16 (split products)."""
+    import torch
+    d = w.d
+    rows = 64 if w.dtype == "bf16" else 32
+    n_j = torch.tensor([min(w.block_k, w.N - J * w.block_k) for J in range(rt.n_kb)], device=mask.device,
+                       dtype=torch.int64)
+    tiles_j = (n_j + rows - 1) // rows
+    exact_tiles = int((mask.long() * tiles_j).sum())
+    words = -(-rt.n_kb // 32)
+    pad = words * 32 - rt.n_kb
+    dropped = ~mask
+    if pad:
+        dropped = torch.nn.functional.pad(dropped, (0, pad), value=False)
+    resid_tiles = int(dropped.view(*dropped.shape[:-1], words, 32).any(-1).sum())
+    if cfg.no_residual:
+        resid_tiles = 0
+    per_exact = d // 4 if w.dtype == "bf16" else 5 * d // 16
+    per_resid = 3 * d // 16 if w.dtype == "bf16" else 5 * d // 16
+    waves = w.block_q // 32
+    return float((exact_tiles * per_exact + resid_tiles * per_resid) * waves * 32768)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -247,6 +340,9 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     route_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     fwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    warm = {"route_ms_median": median([e[0].elapsed_time(e[1]) for e in ev]),
+            "forward_ms_median": median([e[1].elapsed_time(e[2]) for e in ev])}
+    cold = cold_timing(sa, Q, K, V, rt, O, cfg, args.cold_calls) if args.cold_calls > 0 else None
 
     # algorithmic work of one forward launch, from the route it consumed
     mask = rt.mask()
@@ -260,6 +356,7 @@ def main():
     resid_flops = float(4.0 * w.d * (m_i * dropped).sum())
     dense_flops = 4.0 * w.B * w.H * w.N * w.N * w.d
     kept_frac = exact_flops / dense_flops
+    issued = issued_mfma_flops(w, rt, mask, cfg)
     fwd_tflops = (exact_flops + resid_flops) / (fwd_ms * 1e-3) / 1e12
 
     es = 2 if w.dtype == "bf16" else 4
@@ -307,6 +404,11 @@ def main():
         "dense_ms": dense_ms,
         "speedup_vs_dense": (dense_ms / (route_ms + fwd_ms)) if dense_ms else None,
         "inverse_kept_fraction": 1.0 / kept_frac,
+        "issued_mfma_flops_per_forward": issued,
+        "issued_mfma_frac": issued / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "timing_warm": warm,
+        "timing_cold": cold,
+        "permute": permute_timing(sa, Q, w) if w.hilbert else None,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

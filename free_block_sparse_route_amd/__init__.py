@@ -8,7 +8,12 @@ hand-written HIP for AMD Instinct MI355X (gfx950).
     o_dense = sa.dense_ref_gpu(q, k, v)  # same kernels, every block kept, no residual
 
 q, k, v: device tensors [B, H, N, d], bf16 or fp32, d in {64, 128}.
+
+Hilbert token order (video grid T x Hh x W after an n0-token prefix):
+    perm = sa.hilbert_order(T, Hh, W).cuda()
+    qh = sa.permute_tokens(q, perm, n0)                 # and k, v
+    o = sa.permute_tokens(o_h, perm, n0, inverse=True)  # back to raster order
 """
 from .binding import (ABSOLUTE, FLAG_NO_RESIDUAL, RELATIVE, TOPP, Config, Route, SaParams, SaRoute,  # noqa: F401
-                      SparseAttnError, dense_flops, dense_ref_gpu, forward, kv_idx_cap, last_error,
-                      make_params, route, route_sizes, status_string)
+                      SparseAttnError, dense_flops, dense_ref_gpu, forward, hilbert_order, kv_idx_cap,
+                      last_error, make_params, permute_tokens, route, route_sizes, status_string)

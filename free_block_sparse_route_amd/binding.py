@@ -1,7 +1,7 @@
 """ctypes binding of libsparse_attn.so (argument marshalling only).
 
 Same names as the C ABI in include/sparse_attn.h: route, forward,
-dense_ref_gpu, route_sizes, kv_idx_cap.  Torch tensors supply device memory
+dense_ref_gpu, route_sizes, kv_idx_cap, hilbert_order, permute_tokens.  Torch tensors supply device memory
 and the current HIP stream; every step of the computation runs in the
 library's HIP kernels.  If the library has not been built the import fails.
 """
@@ -59,6 +59,11 @@ def _load():
     lib.sparse_attn_forward.restype = ctypes.c_int
     lib.sparse_attn_dense_ref_gpu.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.sparse_attn_dense_ref_gpu.restype = ctypes.c_int
+    i32 = ctypes.c_int32
+    lib.sparse_attn_hilbert_order.argtypes = [i32, i32, i32, ctypes.POINTER(i32)]
+    lib.sparse_attn_hilbert_order.restype = ctypes.c_int
+    lib.sparse_attn_permute_tokens.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp, vp]
+    lib.sparse_attn_permute_tokens.restype = ctypes.c_int
     lib.sparse_attn_status_string.argtypes = [ctypes.c_int]
     lib.sparse_attn_status_string.restype = ctypes.c_char_p
     lib.sparse_attn_last_error.argtypes = []
@@ -193,6 +198,34 @@ def dense_ref_gpu(q, k, v, block_q: int = 128, scale: float = 0.0, out: torch.Te
     _check(lib.sparse_attn_dense_ref_gpu(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                          L.data_ptr() if lse else None, _stream(q.device)))
     return (o, L) if lse else o
+
+
+def hilbert_order(T: int, Hh: int, W: int) -> torch.Tensor:
+    """sparse_attn_hilbert_order: int32 [T*Hh*W] (CPU), raster index of the token at
+    each Hilbert curve position."""
+    perm = torch.empty(T * Hh * W, dtype=torch.int32)
+    _check(lib.sparse_attn_hilbert_order(T, Hh, W, ctypes.cast(perm.data_ptr(), ctypes.POINTER(ctypes.c_int32))))
+    return perm
+
+
+def permute_tokens(x: torch.Tensor, perm: torch.Tensor, n0: int = 0, inverse: bool = False,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """sparse_attn_permute_tokens: rows [n0, n0 + len(perm)) of x [B, H, N, d] gathered
+    by perm (inverse=False) or scattered by it (inverse=True); other rows copied."""
+    if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, H, N, d] device tensor")
+    dt = {torch.bfloat16: SA_BF16, torch.float32: SA_F32}.get(x.dtype)
+    if dt is None:
+        raise TypeError(f"unsupported dtype {x.dtype} (bf16 or fp32)")
+    if perm.dtype != torch.int32 or perm.device != x.device or not perm.is_contiguous():
+        raise ValueError("perm must be a contiguous int32 tensor on x's device")
+    o = out if out is not None else torch.empty_like(x)
+    if o.shape != x.shape or o.dtype != x.dtype or not o.is_contiguous():
+        raise ValueError("out must match x")
+    B, H, N, d = x.shape
+    _check(lib.sparse_attn_permute_tokens(B, H, N, d, dt, n0, perm.numel(), perm.data_ptr() if perm.numel() else None,
+                                          int(inverse), x.data_ptr(), o.data_ptr(), _stream(x.device)))
+    return o
 
 
 def status_string(s: int) -> str:

@@ -213,6 +213,44 @@ sa_status sparse_attn_dense_ref_gpu(const sa_params *p, const void *q, const voi
     return run_flash(p, q, k, v, nullptr, o, lse, stream, "dense: launch");
 }
 
+sa_status sparse_attn_hilbert_order(int32_t T, int32_t Hh, int32_t W, int32_t *perm) {
+    if (!perm) return fail(SA_ERR_INVALID_ARG, "perm is NULL");
+    if (T < 1 || Hh < 1 || W < 1) return fail(SA_ERR_INVALID_ARG, "grid %d x %d x %d: sides must be >= 1", T, Hh, W);
+    int b = 1;
+    const int side = T > Hh ? (T > W ? T : W) : (Hh > W ? Hh : W);
+    while ((1 << b) < side) ++b;
+    if (b > SA_HILBERT_MAX_BITS)
+        return fail(SA_ERR_UNSUPPORTED, "grid side %d exceeds %d", side, 1 << SA_HILBERT_MAX_BITS);
+    const int64_t n = sa::hilbert_fill(T, Hh, W, b, perm);
+    if (n != (int64_t)T * Hh * W) return fail(SA_ERR_INVALID_ARG, "internal: %lld points", (long long)n);
+    return SA_OK;
+}
+
+sa_status sparse_attn_permute_tokens(int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype, int32_t n0,
+                                     int32_t n_perm, const int32_t *perm, int32_t inverse, const void *in,
+                                     void *out, void *stream) {
+    if (B < 1 || H < 1 || N < 1) return fail(SA_ERR_INVALID_ARG, "B, H, N must be >= 1 (got %d, %d, %d)", B, H, N);
+    if (dtype != SA_BF16 && dtype != SA_F32) return fail(SA_ERR_INVALID_ARG, "dtype %d is not an sa_dtype", dtype);
+    if (d != 64 && d != 128) return fail(SA_ERR_UNSUPPORTED, "d = %d (supported: 64, 128)", d);
+    if (n0 < 0 || n_perm < 0 || (int64_t)n0 + n_perm > N)
+        return fail(SA_ERR_INVALID_ARG, "rows [%d, %d + %d) outside [0, %d)", n0, n0, n_perm, N);
+    if (inverse != 0 && inverse != 1) return fail(SA_ERR_INVALID_ARG, "inverse must be 0 or 1");
+    if (!in || !out) return fail(SA_ERR_INVALID_ARG, "in or out is NULL");
+    if (in == out) return fail(SA_ERR_INVALID_ARG, "in and out must not be the same buffer");
+    if (n_perm > 0 && !perm) return fail(SA_ERR_INVALID_ARG, "perm is NULL");
+    if ((int64_t)B * H * N * d > ((int64_t)1 << 40)) return fail(SA_ERR_INVALID_ARG, "tensor too large");
+    if ((int64_t)B * H > 65535) return fail(SA_ERR_UNSUPPORTED, "B * H = %lld exceeds 65535", (long long)B * H);
+    sa::PermuteArgs a;
+    a.N = N;
+    a.units = d * (dtype == SA_BF16 ? 2 : 4) / 16;
+    a.n0 = n0;
+    a.n_perm = n_perm;
+    a.inverse = inverse;
+    hipError_t e = sa::launch_permute(in, out, perm, a, B * H, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "permute: launch");
+    return SA_OK;
+}
+
 const char *sparse_attn_status_string(sa_status s) {
     switch (s) {
         case SA_OK: return "ok";

@@ -40,6 +40,13 @@ struct FlashArgs {
     float *lse;                          // nullable
 };
 
+struct PermuteArgs {
+    int N;                               // rows per (b, h)
+    int units;                           // 16-byte units per row
+    int n0, n_perm;                      // permuted rows [n0, n0 + n_perm)
+    int inverse;                         // 0: gather, 1: scatter
+};
+
 hipError_t launch_pool(int dtype, int D, const void *q, const void *k, const void *v,
                        const PoolArgs &a, int BH, hipStream_t st);
 hipError_t launch_select(int D, const SelectArgs &a, int BH, hipStream_t st);
@@ -49,5 +56,12 @@ size_t select_lds_bytes(int G, int n_kb, int D);
 // Sparse forward when a.kv_idx != nullptr, dense otherwise.
 hipError_t launch_flash(int dtype, int D, int BQ, const void *q, const void *k, const void *v,
                         void *o, const FlashArgs &a, int BH, hipStream_t st);
+
+// Token permutation on the GPU; host Hilbert order of a T x Hh x W grid on the
+// 2^b cube (returns the number of points written to perm).
+hipError_t launch_permute(const void *in, void *out, const int32_t *perm, const PermuteArgs &a, int BH,
+                          hipStream_t st);
+void hilbert_point(uint64_t h, int b, uint32_t X[3]);
+int64_t hilbert_fill(int T, int Hh, int W, int b, int32_t *perm);
 
 }  // namespace sa

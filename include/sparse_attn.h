@@ -175,6 +175,37 @@ sa_status sparse_attn_forward(const sa_params *p, const void *q, const void *k, 
 sa_status sparse_attn_dense_ref_gpu(const sa_params *p, const void *q, const void *k,
                                     const void *v, void *o, float *lse, void *stream);
 
+/* Token reordering (DFSAttn abstract: tokens reordered along a 3D Hilbert curve
+ * before blocking, so that a block of consecutive tokens is compact in space
+ * and time).  The library orders a T x Hh x W video token grid and permutes
+ * token rows of [B, H, N, d] tensors; a caller reorders Q, K and V, runs route
+ * and forward, and restores the output order with the inverse permutation. */
+
+#define SA_HILBERT_MAX_BITS 9       /* grid sides up to 512 */
+
+/* Hilbert order of the grid: perm[i] = raster index t*Hh*W + y*W + x of the
+ * token at curve position i.  The curve is J. Skilling's (AIP Conf. Proc. 707,
+ * 2004) on the enclosing 2^b cube, b = ceil(log2(max side)) (at least 1), with
+ * the index formed from the bit planes of (t, y, x), most significant first;
+ * the grid's tokens keep the order of their positions on it.  perm: host
+ * memory of T*Hh*W int32, owned by the caller.  Host only; no HIP calls.
+ * Errors: SA_ERR_INVALID_ARG (NULL perm, a side < 1), SA_ERR_UNSUPPORTED (a
+ * side above 2^SA_HILBERT_MAX_BITS). */
+sa_status sparse_attn_hilbert_order(int32_t T, int32_t Hh, int32_t W, int32_t *perm);
+
+/* Row permutation of a [B, H, N, d] tensor (d in {64, 128}, dtype an sa_dtype)
+ * on rows [n0, n0 + n_perm) of every (b, h); other rows are copied unchanged.
+ *   inverse = 0 (gather):  out[b,h,n0+i,:] = in[b,h,n0+perm[i],:]
+ *   inverse = 1 (scatter): out[b,h,n0+perm[i],:] = in[b,h,n0+i,:]
+ * so a scatter with perm undoes a gather with it.  in, out: device memory, not
+ * the same buffer; perm: device memory of n_perm int32 holding a permutation
+ * of [0, n_perm) (an entry outside that range skips its row, leaving that
+ * output row as it was).  Enqueued on `stream`; reads and writes every row
+ * once. */
+sa_status sparse_attn_permute_tokens(int32_t B, int32_t H, int32_t N, int32_t d, int32_t dtype, int32_t n0,
+                                     int32_t n_perm, const int32_t *perm, int32_t inverse, const void *in,
+                                     void *out, void *stream);
+
 /* Static description of a status code. */
 const char *sparse_attn_status_string(sa_status s);
 
