@@ -31,22 +31,43 @@ def _mean_rows(X, lo, hi):
     return [math.fsum(X[t][c] for t in range(lo, hi)) / n for c in range(d)]
 
 
-def brute_route(q, k, block_q, block_k, tau, tau_mode, max_keep, min_keep, n_prefix, scale):
-    """Keep mask as a list of lists of bools [n_qb][n_kb]."""
+def brute_pama(q, kbar, qlo, qhi, scale):
+    """Importance of every key block for the query block [qlo, qhi): each query's
+    softmax over the key-block means, averaged over the block's queries."""
+    nk = len(kbar)
+    acc = [[] for _ in range(nk)]
+    for i in range(qlo, qhi):
+        lg = [scale * _dot(q[i], kbar[J]) for J in range(nk)]
+        top = max(lg)
+        e = [math.exp(x - top) for x in lg]
+        z = math.fsum(e)
+        for J in range(nk):
+            acc[J].append(e[J] / z)
+    return [math.fsum(a) / (qhi - qlo) for a in acc]
+
+
+def brute_route(q, k, block_q, block_k, tau, tau_mode, max_keep, min_keep, n_prefix, scale, pama=False):
+    """Keep mask as a list of lists of bools [n_qb][n_kb].  pama: the proxy is the
+    per-query block attention averaged in the query block."""
     N = len(q)
     qr = _block_ranges(N, block_q)
     kr = _block_ranges(N, block_k)
     qbar = [_mean_rows(q, lo, hi) for lo, hi in qr]
     kbar = [_mean_rows(k, lo, hi) for lo, hi in kr]
     mask = []
-    for I, (qlo, _) in enumerate(qr):
-        s = [scale * _dot(qbar[I], kbar[J]) for J in range(len(kr))]
-        top = max(s)
-        if tau_mode == 0:        # relative to the row's largest proxy probability
-            r = [math.exp(x - top) for x in s]
-        else:                    # the proxy probability itself
-            z = math.fsum(math.exp(x - top) for x in s)
-            r = [math.exp(x - top) / z for x in s]
+    for I, (qlo, qhi) in enumerate(qr):
+        if pama:
+            P = brute_pama(q, kbar, qlo, qhi, scale)
+            top = max(P)
+            r = [x / top for x in P] if tau_mode == 0 else P
+        else:
+            s = [scale * _dot(qbar[I], kbar[J]) for J in range(len(kr))]
+            top = max(s)
+            if tau_mode == 0:        # relative to the row's largest proxy probability
+                r = [math.exp(x - top) for x in s]
+            else:                    # the proxy probability itself
+                z = math.fsum(math.exp(x - top) for x in s)
+                r = [math.exp(x - top) / z for x in s]
         ranking = sorted(range(len(kr)), key=lambda J: (-r[J], J))
         if tau_mode == 2:        # shortest ranking prefix with mass >= 1 - tau
             cands = []

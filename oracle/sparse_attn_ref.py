@@ -52,6 +52,8 @@ import numpy as np
 RELATIVE = 0
 ABSOLUTE = 1
 TOPP = 2
+CENTROID = 0            # proxy: softmax over key blocks of the query block mean's scores
+PAMA = 1                # proxy: per-query softmax over key blocks, averaged in the query block
 EXEMPT_BAND = 1e-4      # |r - cut| below this: the keep decision is rounding-sensitive
 
 
@@ -65,6 +67,7 @@ class RouteParams:
     min_keep: int = 1
     n_prefix: int = 0          # dense-attended leading tokens
     scale: float = 0.0         # 0 => 1/sqrt(d)
+    proxy: int = CENTROID      # CENTROID or PAMA
 
     def sigma(self, d: int) -> float:
         return self.scale if self.scale > 0 else 1.0 / math.sqrt(d)
@@ -93,6 +96,24 @@ def pool(X: np.ndarray, bs: int) -> np.ndarray:
 def proxy_scores(qbar: np.ndarray, kbar: np.ndarray, sigma: float) -> np.ndarray:
     """s[I, J] = sigma * qbar_I . kbar_J."""
     return sigma * (qbar @ kbar.T)
+
+
+def pama_importance(q: np.ndarray, kbar: np.ndarray, bq: int, sigma: float) -> np.ndarray:
+    """A[I, J] = mean over the queries i of query block I of softmax_J(sigma q_i . kbar_J).
+
+    Per-query attention-mass aggregation (PARK page, section 5.1): every
+    original query normalises its attention over the key-block centroids on its
+    own, and the distributions are averaged within the query block (instead of
+    averaging the queries first).  Rows sum to 1.  Reading: the softmax runs over
+    the centroids with equal weight, like the centroid proxy (no block-size
+    weight for a short last key block)."""
+    q = np.asarray(q, dtype=np.float64)
+    logits = sigma * (q @ kbar.T)                        # [N, n_kb]
+    logits -= logits.max(axis=1, keepdims=True)
+    P = np.exp(logits)
+    P /= P.sum(axis=1, keepdims=True)
+    N = q.shape[0]
+    return np.stack([P[I * bq:min((I + 1) * bq, N)].mean(axis=0) for I in range(n_blocks(N, bq))])
 
 
 def _logsumexp_rows(s: np.ndarray) -> np.ndarray:
@@ -181,7 +202,12 @@ def route_ref(q: np.ndarray, k: np.ndarray, p: RouteParams) -> RouteResult:
     N, d = q.shape
     qbar = pool(q, p.block_q)
     kbar = pool(k, p.block_k)
-    s = proxy_scores(qbar, kbar, p.sigma(d))
+    if p.proxy == PAMA:
+        # scores whose softmax is the importance A (rows of A sum to 1): s = ln A
+        with np.errstate(divide="ignore"):
+            s = np.log(pama_importance(q, kbar, p.block_q, p.sigma(d)))
+    else:
+        s = proxy_scores(qbar, kbar, p.sigma(d))
     r = compare_quantity(s, p.tau_mode)
     mask, exempt = select(r, p, N)
     return RouteResult(mask=mask, s=s, r=r, row_max=s.max(axis=1), row_lse=_logsumexp_rows(s),

@@ -381,3 +381,69 @@ def test_recall_is_one_when_all_kept():
     p = R.RouteParams(32, 32, 0.0)
     rt = R.route_ref(q, k, p)
     assert abs(R.attention_recall(q, k, rt.mask, p) - 1.0) < 1e-12
+
+
+# ----------------------------------------------------------------------------- PAMA proxy
+# Per-query attention-mass aggregation (PARK page, section 5.1): each query's
+# softmax over the key-block means, averaged within its query block.
+PAMA_BRUTE = [  # N, d, bq, bk, prefix, tau, mode, max_keep, min_keep
+    (40, 6, 8, 4, 0, 0.1, 0, 0, 1), (40, 6, 8, 4, 0, 0.05, 1, 0, 1), (40, 6, 8, 4, 0, 0.1, 2, 0, 1),
+    (33, 5, 4, 4, 9, 0.2, 0, 3, 2), (31, 3, 8, 4, 0, 0.3, 2, 2, 1), (23, 4, 4, 2, 0, 0.0, 1, 0, 1),
+]
+
+
+@pytest.mark.parametrize("N,d,bq,bk,prefix,tau,mode,mk,mn", PAMA_BRUTE)
+def test_pama_brute_force_agrees(N, d, bq, bk, prefix, tau, mode, mk, mn):
+    q, k, v = rand_qkv(N, d, 7 * N + d, qs=2.5)
+    sig = 1.0 / math.sqrt(d)
+    p = R.RouteParams(bq, bk, tau, mode, max_keep=mk, min_keep=mn, n_prefix=prefix, proxy=R.PAMA)
+    rt = R.route_ref(q, k, p)
+    bm = BR.brute_route(q.tolist(), k.tolist(), bq, bk, tau, mode, mk, mn, prefix, sig, pama=True)
+    assert np.array_equal(rt.mask, np.array(bm, dtype=bool))
+    kbar = R.pool(k, bk)
+    for I in range(R.n_blocks(N, bq)):
+        want = BR.brute_pama(q.tolist(), kbar.tolist(), I * bq, min((I + 1) * bq, N), sig)
+        np.testing.assert_allclose(np.exp(rt.s[I]), want, rtol=0, atol=1e-13)
+
+
+def test_pama_rows_are_distributions():
+    q, k, _ = rand_qkv(100, 8, 5, qs=3.0)
+    A = R.pama_importance(q, R.pool(k, 16), 32, 1 / math.sqrt(8))
+    assert A.shape == (4, 7) and (A > 0).all()
+    np.testing.assert_allclose(A.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("mode", [R.RELATIVE, R.ABSOLUTE, R.TOPP])
+def test_pama_equals_centroid_proxy_for_identical_queries(mode):
+    """When every query of a block is the same vector, averaging after the
+    softmax equals the softmax of the mean query: PAMA reduces to the centroid
+    proxy, decisions and scores alike."""
+    rng = np.random.default_rng(11)
+    bq, N, d = 8, 48, 6
+    q = np.repeat(rng.standard_normal((N // bq, d)) * 3, bq, axis=0)
+    k = rng.standard_normal((N, d))
+    pc = R.RouteParams(bq, 4, 0.05, mode)
+    pp = R.RouteParams(bq, 4, 0.05, mode, proxy=R.PAMA)
+    rc, rp = R.route_ref(q, k, pc), R.route_ref(q, k, pp)
+    np.testing.assert_allclose(rp.r, rc.r, rtol=0, atol=1e-13)
+    assert np.array_equal(rp.mask, rc.mask)
+
+
+def test_pama_keeps_what_query_averaging_erases():
+    """Two opposite queries in one block and key-block means +e, -e, 0: the mean
+    query is 0, so the centroid proxy is uniform, while each query's own softmax
+    peaks on one of the first two blocks.  Closed form with a = sigma c:
+    A = (cosh a, cosh a, 1) / (2 cosh a + 1)."""
+    d, c = 4, 6.0
+    e = np.zeros(d); e[0] = 1.0
+    q = np.stack([c * e, -c * e])
+    k = np.stack([e, e, -e, -e, 0 * e, 0 * e])             # block size 2: means +e, -e, 0
+    sig = 1 / math.sqrt(d)
+    a = sig * c
+    want = np.array([math.cosh(a), math.cosh(a), 1.0]) / (2 * math.cosh(a) + 1)
+    A = R.pama_importance(q, R.pool(k, 2), 2, sig)
+    np.testing.assert_allclose(A[0], want, rtol=1e-14)
+    pp = R.RouteParams(2, 2, 0.5, R.RELATIVE, proxy=R.PAMA)
+    pc = R.RouteParams(2, 2, 0.5, R.RELATIVE)
+    assert R.route_ref(q, k, pp).mask[0].tolist() == [True, True, False]
+    assert R.route_ref(q, k, pc).mask[0].tolist() == [True, True, True]
