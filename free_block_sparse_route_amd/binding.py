@@ -21,6 +21,8 @@ SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_CAPACITY, SA_ERR_HIP = 0, 
 SA_BF16, SA_F32 = 0, 1
 RELATIVE, ABSOLUTE, TOPP = 0, 1, 2
 FLAG_NO_RESIDUAL = 1
+FLAG_PAMA = 2
+CENTROID, PAMA = 0, 1          # routing proxy
 BUFFERS = ("kv_count", "kv_idx", "kv_mask", "q_mean", "k_mean", "v_mean", "kv_split", "row_stats", "cost",
            "work_order")
 
@@ -91,6 +93,7 @@ class Config:
     n_dense_prefix: int = 0
     scale: float = 0.0
     no_residual: bool = False
+    proxy: int = CENTROID      # CENTROID (block means) or PAMA (per-query, averaged)
 
 
 def make_params(q: torch.Tensor, cfg: Config) -> SaParams:
@@ -99,7 +102,8 @@ def make_params(q: torch.Tensor, cfg: Config) -> SaParams:
     if dt is None:
         raise TypeError(f"unsupported dtype {q.dtype} (bf16 or fp32)")
     return SaParams(B, H, N, d, cfg.block_q, cfg.block_k, cfg.tau, cfg.tau_mode, cfg.max_keep, cfg.min_keep,
-                    cfg.n_dense_prefix, cfg.scale, dt, FLAG_NO_RESIDUAL if cfg.no_residual else 0)
+                    cfg.n_dense_prefix, cfg.scale, dt,
+                    (FLAG_NO_RESIDUAL if cfg.no_residual else 0) | (FLAG_PAMA if cfg.proxy == PAMA else 0))
 
 
 def _stream(dev) -> int:

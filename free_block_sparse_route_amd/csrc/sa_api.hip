@@ -52,7 +52,8 @@ sa_status check_params(const sa_params *p, bool routing) {
         return fail(SA_ERR_INVALID_ARG, "dtype %d is not an sa_dtype", p->dtype);
     if (!(p->scale >= 0.f) || isinf(p->scale))
         return fail(SA_ERR_INVALID_ARG, "scale must be finite and >= 0");
-    if (p->flags & ~SA_FLAG_NO_RESIDUAL) return fail(SA_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
+    if (p->flags & ~(SA_FLAG_NO_RESIDUAL | SA_FLAG_PAMA))
+        return fail(SA_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
     const int64_t elems = (int64_t)p->B * p->H * p->N * p->d;
     if (elems > ((int64_t)1 << 40)) return fail(SA_ERR_INVALID_ARG, "tensor too large");
     if (routing) {
@@ -71,6 +72,8 @@ sa_status check_params(const sa_params *p, bool routing) {
     const Dims d = dims_of(p);
     if (routing && d.n_kb > sa::kMaxKeyBlocks)
         return fail(SA_ERR_UNSUPPORTED, "n_kb = %d exceeds %d", d.n_kb, sa::kMaxKeyBlocks);
+    if (routing && (p->flags & SA_FLAG_PAMA) && sa::pama_lds_bytes(d.n_kb, p->block_q) > sa::kPamaLdsBudget)
+        return fail(SA_ERR_UNSUPPORTED, "PAMA proxy: n_kb = %d too large for block_q = %d", d.n_kb, p->block_q);
     if (d.BH * d.n_qb > INT32_MAX / 2) return fail(SA_ERR_UNSUPPORTED, "too many work items");
     return SA_OK;
 }
@@ -159,7 +162,7 @@ sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, co
     sa_.kv_count = r->kv_count; sa_.kv_idx = r->kv_idx; sa_.cost = r->cost;
     sa_.work_order = r->work_order; sa_.kv_mask = r->kv_mask;
     sa_.row_stats = r->row_stats;
-    e = sa::launch_select(p->d, sa_, (int)d.BH, st);
+    e = sa::launch_select(p->d, sa_, (int)d.BH, st, p->dtype, (p->flags & SA_FLAG_PAMA) ? q : nullptr);
     if (e != hipSuccess) return hip_fail(e, "route: select launch");
     return SA_OK;
 }

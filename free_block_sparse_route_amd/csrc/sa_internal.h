@@ -49,7 +49,12 @@ struct PermuteArgs {
 
 hipError_t launch_pool(int dtype, int D, const void *q, const void *k, const void *v,
                        const PoolArgs &a, int BH, hipStream_t st);
-hipError_t launch_select(int D, const SelectArgs &a, int BH, hipStream_t st);
+// Proxy, selection and work order.  q == nullptr: centroid proxy (block means);
+// otherwise the PAMA proxy from the queries q (dtype an sa_dtype).
+hipError_t launch_select(int D, const SelectArgs &a, int BH, hipStream_t st, int dtype = 0,
+                         const void *q = nullptr);
+size_t pama_lds_bytes(int n_kb, int BQ);
+constexpr size_t kPamaLdsBudget = 64 * 1024;
 int select_group(int n_kb, int D, int n_qb);
 size_t select_lds_bytes(int G, int n_kb, int D);
 

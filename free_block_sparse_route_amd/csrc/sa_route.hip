@@ -20,6 +20,8 @@
 //         scheduling, which matters where a row may keep most key blocks),
 //         while within a band the blocks stay in ascending order: neighbouring
 //         query blocks keep mostly the same key blocks and meet in the L2.
+#include <type_traits>
+
 #include "sa_device.h"
 #include "sa_internal.h"
 
@@ -509,6 +511,249 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     }
 }
 
+// --------------------------------------------------------------------- PAMA
+// Per-query attention-mass aggregation (PARK page, section 5.1): the importance
+// of key block J for query block I is the mean over the block's queries i of
+// softmax_J(scale q_i . kbar_J); the selection then runs on s_IJ = ln A_IJ,
+// whose softmax is A itself.  One workgroup per query block, a wave per 32
+// queries; the logits of 32 key blocks at a time come from bf16 matrix cores
+// with fp32 sums, every operand split into bf16 parts (the key means into
+// three, fp32 queries into three; bf16 queries are exact) and every product of
+// parts whose orders add up to at most 2 summed: the logits carry fp32-level
+// error, which the decisions need.  Two passes over the key blocks: the first
+// takes each query's maximum and normaliser (S^T = kbar q^T: a lane holds one
+// query), the second recomputes the logits as S = q kbar^T (a lane holds one
+// key block) and sums the normalised weights over the wave's queries.  The
+// operand registers serve both products unchanged: the A and B operands of a
+// 32x32x16 MFMA have the same lane layout.
+
+template <typename T> struct QSplit { static constexpr int N = 1; };
+template <> struct QSplit<float> { static constexpr int N = 3; };
+
+// bf16 parts of 8 fp32 values: x = p[0] + p[1] + p[2] up to 2^-24 |x|
+template <int NP>
+__device__ __forceinline__ void split8(const float *x, bf16x8 (&p)[NP]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float r = x[e];
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const bf16 b = (bf16)r;
+            p[k][e] = b;
+            r -= (float)b;
+        }
+    }
+}
+
+// Staging of one tile of 32 key-block means, split into three bf16 parts, in
+// LDS: part p, row r at p * 32 * RS + r * RS bytes, RS = 2 D + 16 (the pad puts
+// the 16 rows read by one ds_read_b128 quarter on distinct banks).  Every
+// thread loads, splits and writes FPT consecutive features of one row; the
+// waves then read their MFMA operands from the one staged copy.
+template <int D, int BQ>
+struct PamaStage {
+    static constexpr int THREADS = BQ * 2;
+    static constexpr int FPT = 32 * D / THREADS;        // features per thread
+    static constexpr int TPR = D / FPT;                 // threads per row
+    static constexpr int RS = 2 * D + 16;
+    static constexpr int BYTES = 3 * 32 * RS;
+    float x[FPT];
+
+    __device__ __forceinline__ void load(const float *kb, int n_kb, int jt) {
+        const int r = threadIdx.x / TPR, f = (threadIdx.x % TPR) * FPT;
+        const int J = jt * 32 + r;
+        const float *src = kb + (size_t)(J < n_kb ? J : 0) * D + f;
+#pragma unroll
+        for (int e = 0; e < FPT; e += 4) {
+            const f32x4 v = J < n_kb ? *reinterpret_cast<const f32x4 *>(src + e) : f32x4{};
+            x[e] = v[0];
+            x[e + 1] = v[1];
+            x[e + 2] = v[2];
+            x[e + 3] = v[3];
+        }
+    }
+
+    __device__ __forceinline__ void store(unsigned char *lds) const {
+        const int r = threadIdx.x / TPR, f = (threadIdx.x % TPR) * FPT;
+#pragma unroll
+        for (int e = 0; e < FPT; e += 8) {
+            bf16x8 p[3];
+            split8<3>(x + e, p);
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+                *reinterpret_cast<bf16x8 *>(lds + k * 32 * RS + r * RS + (f + e) * 2) = p[k];
+        }
+    }
+
+    // operand of lane (h, l32) for step c, part k: row l32, features 16c + 8h..
+    static __device__ __forceinline__ bf16x8 frag(const unsigned char *lds, int c, int k, int h, int l32) {
+        return *reinterpret_cast<const bf16x8 *>(lds + k * 32 * RS + l32 * RS + (16 * c + 8 * h) * 2);
+    }
+};
+
+template <typename T, int D, int BQ, int R>
+__global__ __launch_bounds__(BQ * 2) void pama_kernel(const T *__restrict__ q, SelectArgs a) {
+    constexpr int WAVES = BQ / 32;
+    constexpr int NQ = QSplit<T>::N;
+    constexpr int NS = D / 16;
+    using St = PamaStage<D, BQ>;
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    const int n = a.n_kb;
+    unsigned char *tile = reinterpret_cast<unsigned char *>(smem);
+    float *part = smem + St::BYTES / 4;          // [WAVES][n]
+    float *row = part + WAVES * n;               // [n]: ln A
+    float *cq = row + n;                         // [BQ]: per-query log2 normaliser
+    const int bh = blockIdx.y, I = blockIdx.x;
+    const int lane = lane_id(), h = lane >> 5, l32 = lane & 31;
+    const int wave = threadIdx.x / kWave;
+    const int q0 = I * a.block_q;
+    const int m_I = min(a.block_q, a.N - q0);
+    const int qrow = q0 + wave * 32 + l32;
+    const bool row_ok = wave * 32 + l32 < m_I;
+    const float c2 = a.scale * 1.44269504088896341f;          // logits in log2 units
+
+    bf16x8 qf[NS][NQ];           // lane (h, l32): query l32 of the wave, features 16c + 8h..
+    {
+        const T *src = q + ((size_t)bh * a.N + (row_ok ? qrow : q0)) * D + 8 * h;
+#pragma unroll
+        for (int c = 0; c < NS; ++c) {
+            float x[8];
+            Ld8<T>::load_f32(src + 16 * c, x);
+            if (!row_ok)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = 0.f;
+            split8<NQ>(x, qf[c]);
+        }
+    }
+    const float *kb = a.k_mean + (size_t)bh * n * D;
+    const int n_jt = (n + 31) / 32;
+
+    // One pass over the key-block tiles.  kSwap = false: S^T (lane: query l32,
+    // key blocks 8(r/4) + 4h + r%4); true: S (lane: key block l32, queries
+    // 8(r/4) + 4h + r%4).  Products of parts with orders a + b <= 2, smallest
+    // first.  The next tile's means are loaded while this one is multiplied.
+    auto pass = [&](auto swap, auto &&post) {
+        constexpr bool kSwap = decltype(swap)::value;
+        St st;
+        st.load(kb, n, 0);
+        for (int jt = 0; jt < n_jt; ++jt) {
+            st.store(tile);
+            __syncthreads();
+            if (jt + 1 < n_jt) st.load(kb, n, jt + 1);
+            f32x16 acc = {};
+#pragma unroll
+            for (int c = 0; c < NS; ++c) {
+                bf16x8 kp[3];
+#pragma unroll
+                for (int k = 0; k < 3; ++k) kp[k] = St::frag(tile, c, k, h, l32);
+#pragma unroll
+                for (int ord = 2; ord >= 0; --ord) {
+#pragma unroll
+                    for (int qa = 0; qa < NQ; ++qa) {
+                        const int kb_ = ord - qa;
+                        if (kb_ < 0 || kb_ > 2) continue;
+                        if constexpr (kSwap)
+                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[c][qa], kp[kb_], acc, 0, 0, 0);
+                        else
+                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kp[kb_], qf[c][qa], acc, 0, 0, 0);
+                    }
+                }
+            }
+            __syncthreads();                      // the tile is read; the next store may overwrite it
+            post(jt, acc);
+        }
+    };
+
+    // pass 1: per lane, running max and sum of 2^logit over its key blocks, for query l32
+    float m = -INFINITY, z = 0.f;
+    pass(std::false_type{}, [&](int jt, const f32x16 &st) {
+        float x[16];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int J = jt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            x[r] = J < n ? st[r] * c2 : -INFINITY;
+            mt = fmaxf(mt, x[r]);
+        }
+        if (mt > -INFINITY) {
+            const float mn = fmaxf(m, mt);
+            float zt = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) zt += __builtin_amdgcn_exp2f(x[r] - mn);
+            z = z * __builtin_amdgcn_exp2f(m - mn) + zt;       // m = -inf: z = 0
+            m = mn;
+        }
+    });
+    {
+        // combine the two lanes of each query: c = log2 of its normaliser
+        const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        const auto pz = __builtin_amdgcn_permlane32_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+        const float m0 = __uint_as_float(pm[0]), m1 = __uint_as_float(pm[1]);
+        const float z0 = __uint_as_float(pz[0]), z1 = __uint_as_float(pz[1]);
+        const float M = fmaxf(m0, m1);
+        const float Z = (m0 > -INFINITY ? z0 * __builtin_amdgcn_exp2f(m0 - M) : 0.f) +
+                        (m1 > -INFINITY ? z1 * __builtin_amdgcn_exp2f(m1 - M) : 0.f);
+        if (h == 0) cq[wave * 32 + l32] = row_ok ? M + __builtin_amdgcn_logf(Z) : INFINITY;
+    }
+    __syncthreads();
+    // pass 2: normalised weights of each key block summed over the wave's queries
+    float cr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cr[r] = cq[wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
+    pass(std::true_type{}, [&](int jt, const f32x16 &st) {
+        float w = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) w += __builtin_amdgcn_exp2f(st[r] * c2 - cr[r]);   // invalid rows: 0
+        const auto pw = __builtin_amdgcn_permlane32_swap(__float_as_uint(w), __float_as_uint(w), false, false);
+        const float ws = __uint_as_float(pw[0]) + __uint_as_float(pw[1]);
+        const int J = jt * 32 + l32;
+        if (h == 0 && J < n) part[wave * n + J] = ws;
+    });
+    __syncthreads();
+    const float inv_m = 1.f / (float)m_I;
+    for (int J = threadIdx.x; J < n; J += BQ * 2) {
+        float A = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) A += part[w * n + J];
+        A *= inv_m;
+        row[J] = A > 0.f ? fast_log(A) : -1e30f;     // an underflowed importance stays a real, finite score
+    }
+    __syncthreads();
+    if (wave == 0) {
+        if constexpr (R > 0) select_row<R>(row, bh, I, a);
+        else select_row_lds(row, bh, I, a);
+    }
+}
+
+size_t pama_lds_bytes(int n_kb, int BQ) {
+    const size_t stage = BQ == 128 ? PamaStage<128, 128>::BYTES : PamaStage<128, 64>::BYTES;   // d = 128 bound
+    return stage + ((size_t)(BQ / 32 + 1) * n_kb + BQ) * sizeof(float);
+}
+
+template <typename T, int D, int BQ, int R>
+static hipError_t launch_pama_t(const void *q, const SelectArgs &a, int BH, hipStream_t st) {
+    hipLaunchKernelGGL((pama_kernel<T, D, BQ, R>), dim3(a.n_qb, BH), dim3(BQ * 2), pama_lds_bytes(a.n_kb, BQ), st,
+                       (const T *)q, a);
+    return hipGetLastError();
+}
+
+template <typename T, int D, int BQ>
+static hipError_t launch_pama_b(const void *q, const SelectArgs &a, int BH, hipStream_t st) {
+    const int chunks = (a.n_kb + kWave - 1) / kWave;
+    if (chunks <= 4) return launch_pama_t<T, D, BQ, 4>(q, a, BH, st);
+    if (chunks <= 8) return launch_pama_t<T, D, BQ, 8>(q, a, BH, st);
+    if (chunks <= 16) return launch_pama_t<T, D, BQ, 16>(q, a, BH, st);
+    if (chunks <= 20) return launch_pama_t<T, D, BQ, 20>(q, a, BH, st);
+    return launch_pama_t<T, D, BQ, 0>(q, a, BH, st);
+}
+
+template <typename T>
+static hipError_t launch_pama_dt(int D, const void *q, const SelectArgs &a, int BH, hipStream_t st) {
+    if (D == 128) return a.block_q == 128 ? launch_pama_b<T, 128, 128>(q, a, BH, st)
+                                          : launch_pama_b<T, 128, 64>(q, a, BH, st);
+    return a.block_q == 128 ? launch_pama_b<T, 64, 128>(q, a, BH, st) : launch_pama_b<T, 64, 64>(q, a, BH, st);
+}
+
 // --------------------------------------------------------------------- order
 __device__ __forceinline__ int cost_band(int32_t c) { return c > 1 ? 31 - __clz(c) : 0; }
 
@@ -648,10 +893,14 @@ static hipError_t launch_select_d(const SelectArgs &a, int G, int BH, hipStream_
     }
 }
 
-hipError_t launch_select(int D, const SelectArgs &a, int BH, hipStream_t st) {
-    const int G = select_group(a.n_kb, D, a.n_qb);
+hipError_t launch_select(int D, const SelectArgs &a, int BH, hipStream_t st, int dtype, const void *q) {
     hipError_t e = hipSuccess;
-    e = D == 64 ? launch_select_d<64>(a, G, BH, st) : launch_select_d<128>(a, G, BH, st);
+    if (q) {
+        e = dtype == SA_BF16 ? launch_pama_dt<bf16>(D, q, a, BH, st) : launch_pama_dt<float>(D, q, a, BH, st);
+    } else {
+        const int G = select_group(a.n_kb, D, a.n_qb);
+        e = D == 64 ? launch_select_d<64>(a, G, BH, st) : launch_select_d<128>(a, G, BH, st);
+    }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, st, (const int32_t *)a.cost, a.work_order,
                        BH * a.n_qb);

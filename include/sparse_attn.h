@@ -23,6 +23,14 @@
  *     a query block that starts before n_dense_prefix keeps every key block.
  *     The proxy map is never written to memory; only its per-row maximum and
  *     log-sum-exp are.
+ *     With SA_FLAG_PAMA the proxy is per-query attention-mass aggregation
+ *     (PARK page, section 5.1): A_IJ = mean over the queries i of block I of
+ *     softmax_J(scale * q_i . kbar_J), each original query normalised over
+ *     the key-block means on its own before the average; the scores compared
+ *     are then s_IJ = ln A_IJ (so the softmax of a row is A itself, and
+ *     SA_TAU_TOPP retains PARK's cumulative importance).  Its logits carry
+ *     fp32-level error (split bf16 products).  Supported while
+ *     (block_q / 32 + 1) * n_kb + block_q floats fit in 64 KB.
  *
  *  2. Exact pass.  One online-softmax pass over the kept key blocks:
  *     logits scale * q_i . k_t for every token t of a kept block (Sol-Attn
@@ -87,7 +95,8 @@ typedef enum sa_tau_mode {
 } sa_tau_mode;
 
 enum {
-    SA_FLAG_NO_RESIDUAL = 1    /* forward: dropped blocks contribute nothing         */
+    SA_FLAG_NO_RESIDUAL = 1,   /* forward: dropped blocks contribute nothing         */
+    SA_FLAG_PAMA = 2           /* route: PAMA proxy instead of the centroid proxy    */
 };
 
 /* Problem statement: B, H, N, d, block sizes, tau and budget. */

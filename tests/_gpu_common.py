@@ -24,16 +24,17 @@ def sa():
     return m
 
 
-def cfg_for(w: S.Workload, tau=None, mode=R.RELATIVE, max_keep=None, min_keep=1, prefix=None, no_residual=False):
+def cfg_for(w: S.Workload, tau=None, mode=R.RELATIVE, max_keep=None, min_keep=1, prefix=None, no_residual=False,
+            proxy=R.CENTROID):
     m = sa()
     return m.Config(block_q=w.block_q, block_k=w.block_k, tau=w.tau if tau is None else tau, tau_mode=mode,
                     max_keep=w.max_keep if max_keep is None else max_keep, min_keep=min_keep,
-                    n_dense_prefix=w.n_text if prefix is None else prefix, no_residual=no_residual)
+                    n_dense_prefix=w.n_text if prefix is None else prefix, no_residual=no_residual, proxy=proxy)
 
 
 def oracle_params(cfg) -> R.RouteParams:
     return R.RouteParams(cfg.block_q, cfg.block_k, float(np.float32(cfg.tau)), cfg.tau_mode, cfg.max_keep,
-                         cfg.min_keep, cfg.n_dense_prefix, cfg.scale)
+                         cfg.min_keep, cfg.n_dense_prefix, cfg.scale, proxy=cfg.proxy)
 
 
 def run_gpu(Q, K, V, cfg):

@@ -89,6 +89,29 @@ def test_small_parity(case):
     full_check(w, cfg, label="small")
 
 
+# PAMA proxy (PARK page, section 5.1): per-query block attention averaged in the
+# query block; the same selection rules on s = ln A
+PAMA_SMALL = [
+    # name, grid, d, bq, bk, dtype, tau, mode, max_keep, min_keep, n_text, hilbert, B, H
+    ("pama_rel", (4, 8, 32), 128, 128, 128, "bf16", 0.05, R.RELATIVE, 0, 1, 0, False, 1, 2),
+    ("pama_topp_cap", (5, 8, 25), 128, 128, 64, "bf16", 0.1, R.TOPP, 6, 1, 0, False, 1, 2),
+    ("pama_abs_d64_q64", (3, 9, 21), 64, 64, 128, "bf16", 0.02, R.ABSOLUTE, 0, 2, 0, False, 2, 1),
+    ("pama_prefix_hilbert", (4, 8, 30), 128, 128, 128, "bf16", 0.1, R.TOPP, 0, 1, 100, True, 1, 2),
+    ("pama_f32", (4, 8, 16), 64, 64, 64, "f32", 0.1, R.TOPP, 0, 1, 0, False, 1, 2),
+    ("pama_f32_d128_q128", (3, 7, 19), 128, 128, 64, "f32", 0.02, R.RELATIVE, 3, 1, 0, False, 1, 1),
+    ("pama_n130", (1, 10, 13), 128, 128, 64, "bf16", 0.05, R.RELATIVE, 0, 1, 0, False, 1, 1),
+    ("pama_n1", (1, 1, 1), 128, 128, 128, "bf16", 0.01, R.TOPP, 0, 1, 0, False, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", PAMA_SMALL, ids=[c[0] for c in PAMA_SMALL])
+def test_pama_parity(case):
+    name, grid, d, bq, bk, dt, tau, mode, mk, mn, n_text, hil, B, H = case
+    w = S.small(name, B, H, d, grid, bq, bk, tau, dtype=dt, qscale=6.0, n_text=n_text, hilbert=hil)
+    cfg = cfg_for(w, mode=mode, max_keep=mk, min_keep=mn, proxy=R.PAMA)
+    full_check(w, cfg, label="pama")
+
+
 @pytest.mark.parametrize("mode", [R.RELATIVE, R.ABSOLUTE])
 def test_tiny_workload(mode):
     w = S.WORKLOADS["tiny"]

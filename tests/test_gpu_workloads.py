@@ -50,6 +50,15 @@ def test_wan13b_full(mode):
     check_workload(w, [cfg], [(0, h) for h in range(w.H)], blocks_per_head=6)
 
 
+@pytest.mark.parametrize("mode", [R.RELATIVE, R.TOPP])
+def test_wan13b_full_pama(mode):
+    """PAMA proxy on the full Wan-1.3B shape (PARK retrieves by cumulative
+    importance: TOPP at tau 0.1; RELATIVE at the workload's tau)."""
+    w = S.WORKLOADS["wan1.3b"]
+    cfg = cfg_for(w, mode=mode, tau=0.1 if mode == R.TOPP else None, proxy=R.PAMA)
+    check_workload(w, [cfg], heads=[(0, h) for h in range(w.H)])
+
+
 def test_wan14b_tau_sweep():
     w = S.WORKLOADS["wan14b"]
     cfgs = [cfg_for(w, tau=t) for t in S.WAN14B_TAU_SWEEP] + [cfg_for(w, tau=0.003, mode=R.ABSOLUTE)]
