@@ -399,6 +399,7 @@ __device__ __forceinline__ float row_pair_sum(float x) {
 // far from overflow.  Numerator and normaliser share the reference, so the
 // softmax is unchanged.
 constexpr float kLazy = 32.f;
+constexpr float kLazyWeight = 4294967296.f;     // 2^kLazy
 
 // Online-softmax state of the wave's 32 rows (per lane: its row, log2 units).
 template <int D>
@@ -407,6 +408,14 @@ struct SoftState {
     float m_ref, l_run;
 
     __device__ __forceinline__ float m_use() const { return m_ref == -INFINITY ? 0.f : m_ref; }
+
+    // After weights were formed against m_use(): the reference must move if
+    // one of them may exceed 2^kLazy (their sum shows it, as do an overflow
+    // and a NaN) or if there is no reference yet.  Rare: the first tile of a
+    // row, and a rise of the logits by more than kLazy.
+    __device__ __forceinline__ bool needs_move(float psum) const {
+        return !(psum <= kLazyWeight) || m_ref == -INFINITY;
+    }
 
     // New reference from this tile's row maxima (row_max: both lanes of a row
     // agree); rescales the normaliser and returns the factor for the accumulator.
@@ -467,8 +476,10 @@ __device__ __forceinline__ void drop_absent(f32x16 &s, int lim) {
 // An exact tile in four scheduling regions: S^T of key rows 0..31; S^T of rows
 // 32..63 while the weights of rows 0..31 are formed; P V of keys 0..31 while
 // the weights of keys 32..63 are formed; P V of keys 32..63.  The MFMAs of one
-// half run while the exponentials of the other are computed.  Before the
-// weights of a half, a row that passes the reference moves it (rare).  Rows at
+// half run while the exponentials of the other are computed.  The weights of a
+// half are formed against the current reference without a row maximum; when
+// one may pass 2^kLazy (seen in their sum) the reference moves to the half's
+// row maximum and they are formed again (rare).  Rows at
 // or past `valid` (a partial last tile) are dropped.  wait_v() runs before the
 // first read of Vs.  Accumulator register r of lane (h, l32) holds key row
 // 8(r/4) + 4h + r%4 of its 32-row block.
@@ -479,8 +490,6 @@ __device__ __forceinline__ void tile_exact(const unsigned char *Ks, const unsign
     constexpr int NS = D / 16, NB = D / 32;
     f32x16 s0 = qk_half<D, BQ>(Ks, 0, ln, qf);
     if (valid < kTile) drop_absent(s0, valid - 4 * h);
-    const float mx_a = half_max(s0, c);
-    if (__ballot(mx_a > sm.m_ref + kLazy) != 0) sm.move_ref(row_pair_max(mx_a));
     bf16x8 p0, p1, p2, p3;
     float ps_a, ps_b;
     f32x16 s1 = qk_half<D, BQ>(Ks, 1, ln, qf);
@@ -497,14 +506,16 @@ __device__ __forceinline__ void tile_exact(const unsigned char *Ks, const unsign
     pin(p0);
     pin(p1);
     pin(ps_a);
+    if (__ballot(sm.needs_move(ps_a)) != 0) {
+        // rare path: the logits are formed again from the keys still in LDS,
+        // so that none stays live across the scheduled region above
+        f32x16 r0 = qk_half<D, BQ>(Ks, 0, ln, qf);
+        if (valid < kTile) drop_absent(r0, valid - 4 * h);
+        sm.move_ref(row_pair_max(half_max(r0, c)));
+        weights_half(r0, c, sm.m_use(), p0, p1, ps_a);
+    }
     sm.l_run += ps_a;
     if (valid < kTile) drop_absent(s1, valid - 32 - 4 * h);
-    const float mx_b = half_max(s1, c);
-    // the weights of keys 0..31 are relative to the old reference: the
-    // accumulator is rescaled only after their P V has been added
-    const bool move_b = __ballot(mx_b > sm.m_ref + kLazy) != 0;
-    float alpha_b = 1.f;
-    if (move_b) alpha_b = sm.move_ref_l(row_pair_max(mx_b));
     wait_v();                           // this tile's values are in LDS from here on
     pv_half<D, BQ>(Vs, 0, ln, p0, p1, sm.acc);
     weights_half(s1, c, sm.m_use(), p2, p3, ps_b);
@@ -518,7 +529,14 @@ __device__ __forceinline__ void tile_exact(const unsigned char *Ks, const unsign
     pin(p2);
     pin(p3);
     pin(ps_b);
-    if (move_b) sm.scale_acc(alpha_b);
+    if (__ballot(sm.needs_move(ps_b)) != 0) {
+        // the weights of keys 0..31 were formed against the old reference: the
+        // accumulator is rescaled after their P V has been added
+        f32x16 r1 = qk_half<D, BQ>(Ks, 1, ln, qf);
+        if (valid < kTile) drop_absent(r1, valid - 32 - 4 * h);
+        sm.scale_acc(sm.move_ref_l(row_pair_max(half_max(r1, c))));
+        weights_half(r1, c, sm.m_use(), p2, p3, ps_b);
+    }
     sm.l_run += ps_b;
     pv_half<D, BQ>(Vs, 1, ln, p2, p3, sm.acc);
 }
