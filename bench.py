@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--workload", default="wan1.3b")
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--tau-mode", choices=("relative", "absolute", "topp"), default="relative")
+    ap.add_argument("--fused", action="store_true",
+                    help="fused routing: the route pre-pass writes row statistics only and the forward "
+                         "takes the keep decisions itself")
     ap.add_argument("--proxy", choices=("centroid", "pama"), default="centroid",
                     help="routing proxy: block means (default) or per-query block attention averaged per block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -123,7 +126,7 @@ def pmc_summary(args):
     rd = f_kib * 1024.0 * scale_f
     wr = w_kib * 1024.0 * scale_w
     rec = {"kernel": "flash_kernel (sparse forward with residual)", "workload": args.workload,
-           "tau_mode": args.tau_mode, "proxy": args.proxy, "flash_source_sha256_16": source_hash(),
+           "tau_mode": args.tau_mode, "proxy": args.proxy, "fused": args.fused, "flash_source_sha256_16": source_hash(),
            "bytes_per_launch": rd + wr, "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
            "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
            "copy_fetch_kib": copy_f, "copy_write_kib": copy_w, "fetch_scale": scale_f, "write_scale": scale_w,
@@ -316,7 +319,7 @@ def main():
     mode = {"relative": sa.RELATIVE, "absolute": sa.ABSOLUTE, "topp": sa.TOPP}[args.tau_mode]
     cfg = sa.Config(block_q=w.block_q, block_k=w.block_k, tau=w.tau if args.tau is None else args.tau,
                     tau_mode=mode, max_keep=w.max_keep, min_keep=1, n_dense_prefix=w.n_text,
-                    proxy=sa.PAMA if args.proxy == "pama" else sa.CENTROID)
+                    proxy=sa.PAMA if args.proxy == "pama" else sa.CENTROID, fused=args.fused)
     print(f"[bench] generating {w.name} B{w.B} H{w.H} N{w.N} d{w.d}", file=sys.stderr, flush=True)
     Qc, Kc, Vc = S.make_qkv(w)
     Q, K, V = Qc.cuda(), Kc.cuda(), Vc.cuda()
@@ -394,7 +397,7 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32 in, bf16 products",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "block_q": w.block_q, "block_k": w.block_k, "tau": cfg.tau, "tau_mode": args.tau_mode, "proxy": args.proxy,
+                   "block_q": w.block_q, "block_k": w.block_k, "tau": cfg.tau, "tau_mode": args.tau_mode, "proxy": args.proxy, "fused": args.fused,
                    "max_keep": cfg.max_keep, "n_dense_prefix": cfg.n_dense_prefix,
                    "kept_fraction": kept_frac},
         "roofline": {"bound": "mfma", "achieved": fwd_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -14,6 +14,6 @@ Hilbert token order (video grid T x Hh x W after an n0-token prefix):
     qh = sa.permute_tokens(q, perm, n0)                 # and k, v
     o = sa.permute_tokens(o_h, perm, n0, inverse=True)  # back to raster order
 """
-from .binding import (ABSOLUTE, CENTROID, FLAG_NO_RESIDUAL, FLAG_PAMA, PAMA, RELATIVE, TOPP, Config, Route, SaParams, SaRoute,  # noqa: F401
+from .binding import (ABSOLUTE, CENTROID, FLAG_FUSED, FLAG_NO_RESIDUAL, FLAG_PAMA, PAMA, RELATIVE, TOPP, Config, Route, SaParams, SaRoute,  # noqa: F401
                       SparseAttnError, dense_flops, dense_ref_gpu, forward, hilbert_order, kv_idx_cap,
                       last_error, make_params, permute_tokens, route, route_sizes, status_string)

@@ -22,6 +22,7 @@ SA_BF16, SA_F32 = 0, 1
 RELATIVE, ABSOLUTE, TOPP = 0, 1, 2
 FLAG_NO_RESIDUAL = 1
 FLAG_PAMA = 2
+FLAG_FUSED = 4
 CENTROID, PAMA = 0, 1          # routing proxy
 BUFFERS = ("kv_count", "kv_idx", "kv_mask", "q_mean", "k_mean", "v_mean", "kv_split", "row_stats", "cost",
            "work_order")
@@ -94,6 +95,7 @@ class Config:
     scale: float = 0.0
     no_residual: bool = False
     proxy: int = CENTROID      # CENTROID (block means) or PAMA (per-query, averaged)
+    fused: bool = False        # routing decisions taken inside the forward pass
 
 
 def make_params(q: torch.Tensor, cfg: Config) -> SaParams:
@@ -103,7 +105,8 @@ def make_params(q: torch.Tensor, cfg: Config) -> SaParams:
         raise TypeError(f"unsupported dtype {q.dtype} (bf16 or fp32)")
     return SaParams(B, H, N, d, cfg.block_q, cfg.block_k, cfg.tau, cfg.tau_mode, cfg.max_keep, cfg.min_keep,
                     cfg.n_dense_prefix, cfg.scale, dt,
-                    (FLAG_NO_RESIDUAL if cfg.no_residual else 0) | (FLAG_PAMA if cfg.proxy == PAMA else 0))
+                    (FLAG_NO_RESIDUAL if cfg.no_residual else 0) | (FLAG_PAMA if cfg.proxy == PAMA else 0) |
+                    (FLAG_FUSED if cfg.fused else 0))
 
 
 def _stream(dev) -> int:

@@ -52,7 +52,7 @@ sa_status check_params(const sa_params *p, bool routing) {
         return fail(SA_ERR_INVALID_ARG, "dtype %d is not an sa_dtype", p->dtype);
     if (!(p->scale >= 0.f) || isinf(p->scale))
         return fail(SA_ERR_INVALID_ARG, "scale must be finite and >= 0");
-    if (p->flags & ~(SA_FLAG_NO_RESIDUAL | SA_FLAG_PAMA))
+    if (p->flags & ~(SA_FLAG_NO_RESIDUAL | SA_FLAG_PAMA | SA_FLAG_FUSED))
         return fail(SA_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
     const int64_t elems = (int64_t)p->B * p->H * p->N * p->d;
     if (elems > ((int64_t)1 << 40)) return fail(SA_ERR_INVALID_ARG, "tensor too large");
@@ -72,6 +72,16 @@ sa_status check_params(const sa_params *p, bool routing) {
     const Dims d = dims_of(p);
     if (routing && d.n_kb > sa::kMaxKeyBlocks)
         return fail(SA_ERR_UNSUPPORTED, "n_kb = %d exceeds %d", d.n_kb, sa::kMaxKeyBlocks);
+    if (routing && (p->flags & SA_FLAG_FUSED)) {
+        // the decision of a block depends only on its own proxy and the row's
+        // statistics: no cap, no ranking-based mode, no floor that can bind
+        if (p->flags & SA_FLAG_PAMA) return fail(SA_ERR_UNSUPPORTED, "fused routing with the PAMA proxy");
+        if (p->tau_mode == SA_TAU_TOPP) return fail(SA_ERR_UNSUPPORTED, "fused routing with SA_TAU_TOPP");
+        if (p->max_keep != 0) return fail(SA_ERR_UNSUPPORTED, "fused routing with max_keep");
+        const bool floor_free = p->min_keep == 0 || (p->min_keep == 1 && p->tau_mode == SA_TAU_RELATIVE && p->tau <= 1.f);
+        if (!floor_free) return fail(SA_ERR_UNSUPPORTED, "fused routing with a min_keep floor that can bind");
+        if (d.words > sa::kFusedMaxWords) return fail(SA_ERR_UNSUPPORTED, "fused routing: n_kb = %d too large", d.n_kb);
+    }
     if (routing && (p->flags & SA_FLAG_PAMA) && sa::pama_lds_bytes(d.n_kb, p->block_q) > sa::kPamaLdsBudget)
         return fail(SA_ERR_UNSUPPORTED, "PAMA proxy: n_kb = %d too large for block_q = %d", d.n_kb, p->block_q);
     if (d.BH * d.n_qb > INT32_MAX / 2) return fail(SA_ERR_UNSUPPORTED, "too many work items");
@@ -158,6 +168,7 @@ sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, co
     sa_.scale = p->scale > 0.f ? p->scale : (float)(1.0 / sqrt((double)p->d));
     sa_.ln_tau = p->tau > 0.f ? (float)log((double)p->tau) : -INFINITY;
     sa_.topp_target = 1.f - p->tau;
+    sa_.stats_only = (p->flags & SA_FLAG_FUSED) ? 1 : 0;
     sa_.q_mean = r->q_mean; sa_.k_mean = r->k_mean;
     sa_.kv_count = r->kv_count; sa_.kv_idx = r->kv_idx; sa_.cost = r->cost;
     sa_.work_order = r->work_order; sa_.kv_mask = r->kv_mask;
@@ -182,6 +193,18 @@ static sa_status run_flash(const sa_params *p, const void *q, const void *k, con
         fa.residual = (p->flags & SA_FLAG_NO_RESIDUAL) ? 0 : 1;
         fa.kv_count = r->kv_count; fa.kv_idx = r->kv_idx; fa.work_order = r->work_order;
         fa.kv_mask = r->kv_mask; fa.kv_split = (const sa::bf16 *)r->kv_split;
+        if (p->flags & SA_FLAG_FUSED) {
+            fa.kv_idx = nullptr;
+            fa.kv_mask_out = r->kv_mask;
+            fa.kv_count_out = r->kv_count;
+            fa.q_mean = r->q_mean;
+            fa.k_mean = r->k_mean;
+            fa.row_stats = r->row_stats;
+            fa.tau_mode = p->tau_mode;
+            fa.n_prefix = p->n_dense_prefix;
+            fa.scale = (float)scale;
+            fa.ln_tau = p->tau > 0.f ? (float)log((double)p->tau) : -INFINITY;
+        }
     }
     hipError_t e = sa::launch_flash(p->dtype, p->d, p->block_q, q, k, v, o, fa, (int)d.BH,
                                     (hipStream_t)stream);
@@ -200,6 +223,10 @@ sa_status sparse_attn_forward(const sa_params *p, const void *q, const void *k, 
         (s = check_ptr(r->kv_mask, "route.kv_mask")) ||
         (s = check_ptr(r->kv_split, "route.kv_split")) ||
         (s = check_ptr(r->work_order, "route.work_order")))
+        return s;
+    if ((p->flags & SA_FLAG_FUSED) &&
+        ((s = check_ptr(r->q_mean, "route.q_mean")) || (s = check_ptr(r->k_mean, "route.k_mean")) ||
+         (s = check_ptr(r->row_stats, "route.row_stats"))))
         return s;
     if (r->kv_idx_cap < min_cap(p))
         return fail(SA_ERR_CAPACITY, "route.kv_idx_cap %d < required %d", r->kv_idx_cap, min_cap(p));

@@ -27,6 +27,8 @@
 // reading one feature chunk of 16 rows hit distinct banks, for V so that the
 // transposing reads (ds_read_b64_tr_b16) that build V^T operands spread over
 // all banks.
+#include <type_traits>
+
 #include "sa_device.h"
 #include "sa_internal.h"
 
@@ -144,6 +146,119 @@ struct TileStream {
         return false;
     }
 };
+
+// Fused routing: the kept blocks come from this work item's decision words in
+// LDS (bit J % 32 of word J / 32), in ascending J, then one residual tile per
+// word that holds a dropped block: the same tile order as a route's lists.
+struct BitStream {
+    const uint32_t *lw;       // decision words in LDS
+    int words, wi, sub, rt, n_rt;
+    int exact_rows, exact_kind;
+    uint32_t bits;            // kept bits of word wi not yet visited
+
+    __device__ uint32_t word(int w) const { return (uint32_t)__builtin_amdgcn_readfirstlane((int)lw[w]); }
+
+    __device__ void prime() {
+        wi = 0;
+        sub = 0;
+        rt = 0;
+        bits = words > 0 ? word(0) : 0u;
+    }
+
+    __device__ bool next(TileDesc &o, const FlashArgs &a) {
+        while (wi < words) {
+            if (bits == 0u) {
+                if (++wi < words) bits = word(wi);
+                continue;
+            }
+            const int J = wi * 32 + __builtin_ctz(bits);
+            const int b0 = J * a.block_k;
+            const int b1 = min(b0 + a.block_k, a.N);
+            const int tok0 = b0 + sub * exact_rows;
+            ++sub;
+            if (b0 + sub * exact_rows >= b1) {
+                bits &= bits - 1u;
+                sub = 0;
+            }
+            if (tok0 < b1) {
+                o.kind = exact_kind;
+                o.row0 = tok0;
+                o.valid = min(exact_rows, b1 - tok0);
+                return true;
+            }
+        }
+        while (rt < n_rt) {
+            const int cur = rt++;
+            const uint32_t kept = word(cur);
+            const int lim = a.n_kb - cur * 32;
+            const uint32_t vmask = lim >= 32 ? ~0u : ((1u << lim) - 1u);
+            if ((~kept & vmask) != 0) {
+                o.kind = kResidual;
+                o.row0 = cur * 32;
+                o.valid = kTile;
+                o.kept = kept | ~vmask;
+                return true;
+            }
+        }
+        return false;
+    }
+};
+
+// Decision words of one query block under fused routing, taken at the start of
+// its work item (Sol-Attn abstract: blocks are selected against the threshold
+// inside the attention pass; the pre-pass supplies only the proxy row's maximum
+// and log-sum-exp).  Every thread scores key blocks J = t, t + THREADS, ...:
+// s = scale * qbar_I . kbar_J in fp32 (the query mean through the scalar cache),
+// kept when s clears the threshold the route's row statistics give, or when
+// the dense prefix covers it.  Writes the words to LDS and to the route's mask,
+// the count to the route; returns the count (uniform).
+constexpr int kFusedWords = 512;           // n_kb <= 16368
+template <int D, int BQ>
+__device__ __forceinline__ int fused_route(int bh, int I, const FlashArgs &a, uint32_t *fw) {
+    using C = FC<D, BQ>;
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int n = a.n_kb, words = a.mask_words;
+    const size_t row = (size_t)bh * a.n_qb + I;
+    const float thr = (a.tau_mode == SA_TAU_ABSOLUTE ? a.row_stats[row * 2 + 1] : a.row_stats[row * 2]) + a.ln_tau;
+    const bool dense_row = (int64_t)I * a.block_q < a.n_prefix;
+    const kconst<float> *qb = (const kconst<float> *)(a.q_mean + row * D);
+    const float *kb = a.k_mean + (size_t)bh * n * D;
+    for (int base = 0; base < n; base += C::THREADS) {
+        const int J = base + (int)threadIdx.x;
+        bool keep = false;
+        if (J < n) {
+            const float *kr = kb + (size_t)J * D;
+            float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < D; c += 4) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(kr + c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s4[e] = fmaf(qb[c + e], x[e], s4[e]);
+            }
+            const float sc = ((s4[0] + s4[1]) + (s4[2] + s4[3])) * a.scale;
+            keep = sc >= thr || dense_row || (int64_t)J * a.block_k < a.n_prefix;
+        }
+        const uint64_t b = __ballot(keep);
+        const int w = (base + wave * kWave) / 32;
+        if (lane == 0 && w < words) fw[w] = (uint32_t)b;
+        if (lane == 1 && w + 1 < words) fw[w + 1] = (uint32_t)(b >> 32);
+    }
+    __syncthreads();
+    int cnt = 0;
+    for (int w = threadIdx.x; w < words; w += C::THREADS) {
+        const uint32_t x = fw[w];
+        a.kv_mask_out[row * words + w] = x;
+        cnt += __popc(x);
+    }
+    cnt = (int)wave_sum((float)cnt);
+    if (lane == 0) fw[kFusedWords + wave] = (uint32_t)cnt;
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < C::WAVES; ++w) total += (int)fw[kFusedWords + w];
+    if (threadIdx.x == 0) a.kv_count_out[row] = total;
+    return __builtin_amdgcn_readfirstlane(total);
+}
 
 // Buffer resource over `bytes` bytes at `base`: loads past the end return zero
 // (also when they go straight to LDS).
@@ -583,10 +698,11 @@ __device__ __forceinline__ void weights_split(f32x16 &s0, const f32x16 &s1, cons
 // One work item: the query block I of head bh = item / n_qb, from its first
 // tile to its output rows.  kSparse: kept-list and residual tiles from a route;
 // otherwise every key tile (dense).  LDS: K0/V0 and K1/V1, one tile each.
-template <typename T, int D, int BQ, bool kSparse>
+template <typename T, int D, int BQ, bool kSparse, bool kFused>
 __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, const T *__restrict__ k,
                                          const T *__restrict__ v, T *__restrict__ o, const FlashArgs &a,
-                                         unsigned char *K0, unsigned char *V0, unsigned char *K1, unsigned char *V1) {
+                                         unsigned char *K0, unsigned char *V0, unsigned char *K1, unsigned char *V1,
+                                         uint32_t *fw) {
     using C = FC<D, BQ>;
     constexpr bool kF32 = sizeof(T) == 4;
     const int bh = item / a.n_qb;
@@ -627,22 +743,30 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
         }
     }
 
-    TileStream ts;
-    ts.t = 0; ts.li = 0; ts.sub = 0; ts.rt = 0;
+    using Stream = std::conditional_t<kFused, BitStream, TileStream>;
+    Stream ts;
     ts.exact_rows = kF32 ? 32 : 64;
     ts.exact_kind = kF32 ? kExactSplit : kExact;
-    ts.dense_tiles = (a.N + ts.exact_rows - 1) / ts.exact_rows;
     const size_t row_id = (size_t)bh * a.n_qb + I;
-    if constexpr (kSparse) {
-        ts.list = (const kconst<int32_t> *)(a.kv_idx + row_id * a.kv_idx_cap);
-        ts.cnt = __builtin_amdgcn_readfirstlane(a.kv_count[row_id]);
-        ts.mask = (const kconst<uint32_t> *)(a.kv_mask + row_id * a.mask_words);
-        ts.n_rt = (a.residual && ts.cnt < a.n_kb) ? a.mask_words : 0;   // all kept: no residual
+    if constexpr (kFused) {
+        const int cnt = fused_route<D, BQ>(bh, I, a, fw);
+        ts.lw = fw;
+        ts.words = a.mask_words;
+        ts.n_rt = (a.residual && cnt < a.n_kb) ? a.mask_words : 0;   // all kept: no residual
     } else {
-        ts.list = nullptr;
-        ts.mask = nullptr;
-        ts.cnt = 0;
-        ts.n_rt = 0;
+        ts.t = 0; ts.li = 0; ts.sub = 0; ts.rt = 0;
+        ts.dense_tiles = (a.N + ts.exact_rows - 1) / ts.exact_rows;
+        if constexpr (kSparse) {
+            ts.list = (const kconst<int32_t> *)(a.kv_idx + row_id * a.kv_idx_cap);
+            ts.cnt = __builtin_amdgcn_readfirstlane(a.kv_count[row_id]);
+            ts.mask = (const kconst<uint32_t> *)(a.kv_mask + row_id * a.mask_words);
+            ts.n_rt = (a.residual && ts.cnt < a.n_kb) ? a.mask_words : 0;   // all kept: no residual
+        } else {
+            ts.list = nullptr;
+            ts.mask = nullptr;
+            ts.cnt = 0;
+            ts.n_rt = 0;
+        }
     }
     ts.prime();
     HeadSrc<T> hs;
@@ -790,29 +914,35 @@ __device__ __forceinline__ int grid_position(int i, int W) {
 
 // One workgroup per work item (query block); kSparse takes the item from the
 // route's work order, the dense path in plain order.
-template <typename T, int D, int BQ, bool kSparse>
+template <typename T, int D, int BQ, bool kSparse, bool kFused>
 __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<T, BQ>, kWavesPerEU<T, BQ>))) void flash_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
     FlashArgs a) {
     using C = FC<D, BQ>;
     const int p = grid_position(blockIdx.x, a.n_items);
-    const int item = kSparse ? __builtin_amdgcn_readfirstlane(a.work_order[p]) : p;
+    // fused routing has no work order (no costs before the pass): plain order
+    const int item = kSparse && !kFused ? __builtin_amdgcn_readfirstlane(a.work_order[p]) : p;
     __shared__ __attribute__((aligned(1024))) unsigned char K0[C::TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char K1[C::TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char V0[C::TILE];
+    uint32_t *fw = nullptr;
+    if constexpr (kFused) {
+        __shared__ uint32_t FW[kFusedWords + C::WAVES];
+        fw = FW;
+    }
     if constexpr (sizeof(T) == 2) {
-        run_item<T, D, BQ, kSparse>(item, q, k, v, o, a, K0, V0, K1, V0);
+        run_item<T, D, BQ, kSparse, kFused>(item, q, k, v, o, a, K0, V0, K1, V0, fw);
     } else {
         __shared__ __attribute__((aligned(1024))) unsigned char V1[C::TILE];
-        run_item<T, D, BQ, kSparse>(item, q, k, v, o, a, K0, V0, K1, V1);
+        run_item<T, D, BQ, kSparse, kFused>(item, q, k, v, o, a, K0, V0, K1, V1, fw);
     }
 }
 
-template <typename T, int D, int BQ, bool kSparse>
+template <typename T, int D, int BQ, bool kSparse, bool kFused>
 static hipError_t launch_flash_t(const void *q, const void *k, const void *v, void *o,
                                  const FlashArgs &a, int BH, hipStream_t st) {
     using C = FC<D, BQ>;
-    auto kern = flash_kernel<T, D, BQ, kSparse>;
+    auto kern = flash_kernel<T, D, BQ, kSparse, kFused>;
     FlashArgs args = a;
     args.n_items = BH * a.n_qb;
     hipLaunchKernelGGL(kern, dim3(args.n_items), dim3(C::THREADS), 0, st, (const T *)q, (const T *)k,
@@ -823,8 +953,9 @@ static hipError_t launch_flash_t(const void *q, const void *k, const void *v, vo
 template <typename T, int D, int BQ>
 static hipError_t launch_flash_s(const void *q, const void *k, const void *v, void *o, const FlashArgs &a,
                                  int BH, hipStream_t st) {
-    return a.kv_idx ? launch_flash_t<T, D, BQ, true>(q, k, v, o, a, BH, st)
-                    : launch_flash_t<T, D, BQ, false>(q, k, v, o, a, BH, st);
+    if (a.kv_mask_out) return launch_flash_t<T, D, BQ, true, true>(q, k, v, o, a, BH, st);
+    return a.kv_idx ? launch_flash_t<T, D, BQ, true, false>(q, k, v, o, a, BH, st)
+                    : launch_flash_t<T, D, BQ, false, false>(q, k, v, o, a, BH, st);
 }
 
 template <typename T>

@@ -21,6 +21,7 @@ struct SelectArgs {
     int N, block_q, block_k, n_qb, n_kb, mask_words, kv_idx_cap;
     int exact_tile_rows;                 // key rows per exact attention tile (cost model)
     int tau_mode, max_keep, min_keep, n_prefix;
+    int stats_only;                      // fused routing pre-pass: row statistics only
     float scale, ln_tau;                 // ln_tau = -inf when tau == 0
     float topp_target;                   // 1 - tau: proxy mass the TOPP mode retains
     const float *q_mean, *k_mean;
@@ -38,6 +39,13 @@ struct FlashArgs {
     const uint32_t *kv_mask;
     const bf16 *kv_split;                // [BH][2][words][64][D] hi/lo residual tiles
     float *lse;                          // nullable
+    // fused routing (kv_idx unused): the decisions are taken in the kernel
+    // from the block means and the pre-pass row statistics, and written out
+    const float *q_mean, *k_mean, *row_stats;
+    uint32_t *kv_mask_out;
+    int32_t *kv_count_out;
+    int tau_mode, n_prefix;
+    float scale, ln_tau;
 };
 
 struct PermuteArgs {
@@ -55,6 +63,7 @@ hipError_t launch_select(int D, const SelectArgs &a, int BH, hipStream_t st, int
                          const void *q = nullptr);
 size_t pama_lds_bytes(int n_kb, int BQ);
 constexpr size_t kPamaLdsBudget = 64 * 1024;
+constexpr int kFusedMaxWords = 512;              // decision words a fused work item holds in LDS
 int select_group(int n_kb, int D, int n_qb);
 size_t select_lds_bytes(int G, int n_kb, int D);
 

@@ -419,10 +419,26 @@ __device__ __forceinline__ void select_row(const float *S, int bh, int I, const 
     }
 }
 
+// Pre-pass of fused routing: the row's maximum and log-sum-exp only.
+__device__ __forceinline__ void row_stats_only(const float *S, int bh, int I, const SelectArgs &a) {
+    const int lane = lane_id(), n = a.n_kb;
+    float m = -INFINITY;
+    for (int J = lane; J < n; J += kWave) m = fmaxf(m, S[J]);
+    m = wave_max(m);
+    float z = 0.f;
+    for (int J = lane; J < n; J += kWave) z += fast_exp(S[J] - m);
+    z = wave_sum(z);
+    if (lane == 0) {
+        const size_t row = (size_t)bh * a.n_qb + I;
+        a.row_stats[row * 2 + 0] = m;
+        a.row_stats[row * 2 + 1] = m + fast_log(z);
+    }
+}
+
 __device__ __forceinline__ void launder(SelectArgs &a) {
     asm volatile("" : "+s"(a.N), "+s"(a.block_q), "+s"(a.block_k), "+s"(a.n_qb), "+s"(a.n_kb), "+s"(a.mask_words));
     asm volatile("" : "+s"(a.kv_idx_cap), "+s"(a.exact_tile_rows), "+s"(a.tau_mode), "+s"(a.max_keep),
-                 "+s"(a.min_keep), "+s"(a.n_prefix));
+                 "+s"(a.min_keep), "+s"(a.n_prefix), "+s"(a.stats_only));
     asm volatile("" : "+s"(a.scale), "+s"(a.ln_tau), "+s"(a.topp_target));
     asm volatile("" : "+s"(a.kv_count), "+s"(a.kv_idx), "+s"(a.cost), "+s"(a.kv_mask), "+s"(a.row_stats));
 }
@@ -506,7 +522,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
         SelectArgs ar = a;
         launder(ar);
         const float *row = S + g * n;
-        if constexpr (R > 0) select_row<R>(row, bh, I0 + g, ar);
+        if (ar.stats_only) row_stats_only(row, bh, I0 + g, ar);
+        else if constexpr (R > 0) select_row<R>(row, bh, I0 + g, ar);
         else select_row_lds(row, bh, I0 + g, ar);
     }
 }
@@ -902,6 +919,7 @@ hipError_t launch_select(int D, const SelectArgs &a, int BH, hipStream_t st, int
         e = D == 64 ? launch_select_d<64>(a, G, BH, st) : launch_select_d<128>(a, G, BH, st);
     }
     if (e != hipSuccess) return e;
+    if (a.stats_only) return hipSuccess;            // fused routing: no lists, no work order
     hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, st, (const int32_t *)a.cost, a.work_order,
                        BH * a.n_qb);
     return hipGetLastError();

@@ -31,6 +31,15 @@
  *     SA_TAU_TOPP retains PARK's cumulative importance).  Its logits carry
  *     fp32-level error (split bf16 products).  Supported while
  *     (block_q / 32 + 1) * n_kb + block_q floats fit in 64 KB.
+ *     With SA_FLAG_FUSED (pass it to both calls) routing is fused into the
+ *     attention pass, the Sol-Attn abstract's single pass: sparse_attn_route
+ *     only pools and writes the proxy rows' maximum and log-sum-exp (no lists,
+ *     no work order), and sparse_attn_forward takes each query block's
+ *     decisions at the start of its work item from s_IJ and those statistics,
+ *     writes them to kv_mask and kv_count, and attends in plain order.  The
+ *     decisions are the τ test of RELATIVE or ABSOLUTE; max_keep must be 0,
+ *     min_keep 0 (or 1 for RELATIVE with tau <= 1, where the argmax clears τ),
+ *     no PAMA, n_kb <= 16384.  The dense prefix applies as above.
  *
  *  2. Exact pass.  One online-softmax pass over the kept key blocks:
  *     logits scale * q_i . k_t for every token t of a kept block (Sol-Attn
@@ -96,7 +105,8 @@ typedef enum sa_tau_mode {
 
 enum {
     SA_FLAG_NO_RESIDUAL = 1,   /* forward: dropped blocks contribute nothing         */
-    SA_FLAG_PAMA = 2           /* route: PAMA proxy instead of the centroid proxy    */
+    SA_FLAG_PAMA = 2,          /* route: PAMA proxy instead of the centroid proxy    */
+    SA_FLAG_FUSED = 4          /* fused routing: decisions taken inside the forward  */
 };
 
 /* Problem statement: B, H, N, d, block sizes, tau and budget. */

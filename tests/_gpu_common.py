@@ -25,11 +25,12 @@ def sa():
 
 
 def cfg_for(w: S.Workload, tau=None, mode=R.RELATIVE, max_keep=None, min_keep=1, prefix=None, no_residual=False,
-            proxy=R.CENTROID):
+            proxy=R.CENTROID, fused=False):
     m = sa()
     return m.Config(block_q=w.block_q, block_k=w.block_k, tau=w.tau if tau is None else tau, tau_mode=mode,
                     max_keep=w.max_keep if max_keep is None else max_keep, min_keep=min_keep,
-                    n_dense_prefix=w.n_text if prefix is None else prefix, no_residual=no_residual, proxy=proxy)
+                    n_dense_prefix=w.n_text if prefix is None else prefix, no_residual=no_residual, proxy=proxy,
+                    fused=fused)
 
 
 def oracle_params(cfg) -> R.RouteParams:
@@ -49,14 +50,15 @@ def head_np(T: torch.Tensor, b: int, h: int) -> np.ndarray:
     return T[b, h].double().cpu().numpy()
 
 
-def check_lists(rt) -> np.ndarray:
-    """kv_count, kv_idx and the bit mask agree; returns the mask as numpy bool."""
+def check_lists(rt, lists: bool = True) -> np.ndarray:
+    """kv_count, kv_idx (unless fused routing, which writes no lists) and the bit
+    mask agree; returns the mask as numpy bool."""
     mask = rt.mask().cpu().numpy()
     cnt = rt.kv_count.cpu().numpy()
     idx = rt.kv_idx.cpu().numpy()
     assert np.array_equal(cnt, mask.sum(axis=-1)), "kv_count != popcount(mask)"
     B, H, n_qb, n_kb = mask.shape
-    for b in range(B):
+    for b in range(B if lists else 0):
         for h in range(H):
             for I in range(n_qb):
                 c = cnt[b, h, I]

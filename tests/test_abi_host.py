@@ -65,6 +65,10 @@ def params(**kw):
     (dict(scale=-1.0), B.SA_ERR_INVALID_ARG), (dict(d=96), B.SA_ERR_UNSUPPORTED),
     (dict(block_q=32), B.SA_ERR_UNSUPPORTED), (dict(block_k=256), B.SA_ERR_UNSUPPORTED),
     (dict(N=2_000_000, block_k=64), B.SA_ERR_UNSUPPORTED),
+    # fused routing decides each block alone: no cap, no top-p, no PAMA, no binding floor
+    (dict(flags=4, max_keep=3), B.SA_ERR_UNSUPPORTED), (dict(flags=4, tau_mode=2), B.SA_ERR_UNSUPPORTED),
+    (dict(flags=6), B.SA_ERR_UNSUPPORTED), (dict(flags=4, tau_mode=1, min_keep=1), B.SA_ERR_UNSUPPORTED),
+    (dict(flags=4, tau=1.5), B.SA_ERR_UNSUPPORTED),
 ])
 def test_invalid_params_rejected(kw, status):
     p = params(**kw)
@@ -72,6 +76,12 @@ def test_invalid_params_rejected(kw, status):
     arr = (ctypes.c_size_t * len(B.BUFFERS))()
     assert B.lib.sparse_attn_route_sizes(ctypes.byref(p), 1 << 20, arr) == status
     assert B.lib.sparse_attn_last_error().decode() != ""
+
+
+def test_fused_floor_free_configurations_accepted():
+    for kw in (dict(flags=4), dict(flags=4, tau_mode=1, min_keep=0), dict(flags=4, tau=1.0),
+               dict(flags=5, min_keep=0, tau=3.0)):
+        assert B.lib.sparse_attn_kv_idx_cap(ctypes.byref(params(**kw))) > 0, kw
 
 
 def test_kv_idx_cap_rules():

@@ -30,7 +30,7 @@ def full_check(w, cfg, blocks_per_head=None, heads=None, label=""):
         f"tau={cfg.tau} mode={cfg.tau_mode} cap={cfg.max_keep} floor={cfg.min_keep} prefix={cfg.n_dense_prefix}")
     Qc, Kc, Vc, Q, K, V = make(w)
     rt, O, L = run_gpu(Q, K, V, cfg)
-    mask = check_lists(rt)
+    mask = check_lists(rt, lists=not cfg.fused)
     stats = rt.row_stats.cpu().numpy()
     Oc = O.float().cpu().numpy()
     Lc = L.cpu().numpy()
@@ -110,6 +110,52 @@ def test_pama_parity(case):
     w = S.small(name, B, H, d, grid, bq, bk, tau, dtype=dt, qscale=6.0, n_text=n_text, hilbert=hil)
     cfg = cfg_for(w, mode=mode, max_keep=mk, min_keep=mn, proxy=R.PAMA)
     full_check(w, cfg, label="pama")
+
+
+# Fused routing (Sol-Attn abstract: selection inside the attention pass, after a
+# pre-pass of the proxy row statistics): the same decisions as the two-kernel
+# route, taken per work item inside the forward kernel
+FUSED_SMALL = [
+    # name, grid, d, bq, bk, dtype, tau, mode, min_keep, n_text, hilbert, B, H
+    ("fused_rel", (4, 8, 32), 128, 128, 128, "bf16", 0.01, R.RELATIVE, 1, 0, False, 1, 2),
+    ("fused_abs_k64", (5, 8, 25), 128, 128, 64, "bf16", 0.01, R.ABSOLUTE, 0, 0, False, 1, 2),
+    ("fused_prefix_hilbert", (4, 8, 30), 128, 128, 128, "bf16", 0.01, R.RELATIVE, 1, 100, True, 1, 2),
+    ("fused_d64_q64", (3, 9, 21), 64, 64, 128, "bf16", 0.02, R.RELATIVE, 0, 0, False, 2, 1),
+    ("fused_f32", (4, 8, 16), 64, 64, 64, "f32", 0.02, R.RELATIVE, 1, 0, False, 1, 2),
+    ("fused_all_dropped", (3, 8, 27), 128, 128, 128, "bf16", 2.0, R.RELATIVE, 0, 0, False, 1, 1),
+    ("fused_n130", (1, 10, 13), 128, 128, 64, "bf16", 0.05, R.ABSOLUTE, 0, 0, False, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_SMALL, ids=[c[0] for c in FUSED_SMALL])
+def test_fused_parity(case):
+    name, grid, d, bq, bk, dt, tau, mode, mn, n_text, hil, B, H = case
+    w = S.small(name, B, H, d, grid, bq, bk, tau, dtype=dt, qscale=6.0, n_text=n_text, hilbert=hil)
+    cfg = cfg_for(w, mode=mode, max_keep=0, min_keep=mn, fused=True)
+    rt, O, L, mask = full_check(w, cfg, label="fused")
+    # the two-kernel route on the same inputs: the same decisions outside the
+    # band, and then the same tiles in the same order, so the same bits
+    Qc, Kc, Vc, Q, K, V = make(w)
+    cfg2 = cfg_for(w, mode=mode, max_keep=0, min_keep=mn)
+    rt2, O2, L2 = run_gpu(Q, K, V, cfg2)
+    mask2 = rt2.mask().cpu().numpy()
+    same = (mask == mask2).all(axis=-1)                  # [B, H, n_qb]: rows with identical decisions
+    say(f"  rows with identical decisions {int(same.sum())} / {same.size}")
+    rows = torch.from_numpy(np.repeat(same, w.block_q, axis=-1)[..., :w.N])
+    assert torch.equal(O.cpu()[rows], O2.cpu()[rows]) and torch.equal(L.cpu()[rows], L2.cpu()[rows])
+
+
+def test_fused_rejects_what_it_cannot_decide_alone():
+    m = sa()
+    w = S.small("fr", 1, 1, 128, (2, 8, 16), 128, 128, 0.01)
+    Qc, Kc, Vc, Q, K, V = make(w)
+    for kw in (dict(max_keep=3), dict(tau_mode=R.TOPP), dict(tau_mode=R.ABSOLUTE, min_keep=1),
+               dict(proxy=R.PAMA), dict(tau=1.5, min_keep=1)):
+        base = dict(block_q=128, block_k=128, tau=0.01, fused=True, min_keep=0)
+        base.update(kw)
+        with pytest.raises(m.SparseAttnError) as ei:
+            m.route(Q, K, V, m.Config(**base))
+        assert ei.value.status == m.binding.SA_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("mode", [R.RELATIVE, R.ABSOLUTE])

@@ -16,14 +16,14 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
-def check_workload(w, cfgs, heads, blocks_per_head=6):
+def check_workload(w, cfgs, heads, blocks_per_head=6, lists=True):
     say(f"[case] {w.name}: generating B{w.B} H{w.H} N{w.N}")
     Qc, Kc, Vc = S.make_qkv(w)
     Q, K, V = Qc.cuda(), Kc.cuda(), Vc.cuda()
     for cfg in cfgs:
         say(f"[case] {w.name} tau={cfg.tau} mode={cfg.tau_mode} cap={cfg.max_keep} prefix={cfg.n_dense_prefix}")
         rt, O, L = run_gpu(Q, K, V, cfg)
-        mask = check_lists(rt)
+        mask = check_lists(rt, lists=lists)
         stats = rt.row_stats.cpu().numpy()
         assert torch.isfinite(O).all().item() and torch.isfinite(L).all().item()
         nd_tot = 0
@@ -57,6 +57,13 @@ def test_wan13b_full_pama(mode):
     w = S.WORKLOADS["wan1.3b"]
     cfg = cfg_for(w, mode=mode, tau=0.1 if mode == R.TOPP else None, proxy=R.PAMA)
     check_workload(w, [cfg], heads=[(0, h) for h in range(w.H)])
+
+
+def test_wan13b_full_fused():
+    """Fused routing (decisions inside the forward) on the full Wan-1.3B shape."""
+    w = S.WORKLOADS["wan1.3b"]
+    cfg = cfg_for(w, fused=True)
+    check_workload(w, [cfg], heads=[(0, h) for h in range(w.H)], lists=False)
 
 
 def test_wan14b_tau_sweep():
