@@ -109,7 +109,7 @@ def pmc_summary(args):
     the plain 1 GiB copy in the same run."""
     fetch_rows = _pmc_rows(args.pmc_summary[0], "FETCH_SIZE")
     write_rows = _pmc_rows(args.pmc_summary[1], "WRITE_SIZE")
-    is_flash = lambda r: "flash_kernel" in r["Kernel_Name"] and "Lb1E" in r["Kernel_Name"]
+    is_flash = lambda r: "flash_kernel" in r["Kernel_Name"] and "Lb1ELb0E" in r["Kernel_Name"]
     # the copy: the dispatch of a kernel named for copying whose counter is the largest
     def copy_kib(rows):
         cands = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
