@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--workload", default="wan1.3b")
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--tau-mode", choices=("relative", "absolute", "topp"), default="relative")
+    ap.add_argument("--sparsepr", type=int, default=0, metavar="P",
+                    help="also time the probe-fitted residual correction with P probes per query block and "
+                         "compare its error against dense attention with the block residual's")
     ap.add_argument("--fused", action="store_true",
                     help="fused routing: the route pre-pass writes row statistics only and the forward "
                          "takes the keep decisions itself")
@@ -269,6 +272,30 @@ def permute_timing(sa, X, w, reps=10):
     return res
 
 
+def sparsepr_compare(sa, Q, K, V, rt, cfg, O, P, rank=8, ridge=1e-3, reps=5):
+    """Median time of the probe-fitted correction (P probes per query block) and the
+    relative Frobenius error against the library's dense path of: the forward
+    with the block residual, the probe-fitted output, the kept tokens alone."""
+    import dataclasses
+    import torch
+    ws = torch.empty(sa.sparsepr_workspace_size(Q, cfg, P), dtype=torch.uint8, device=Q.device)
+    Opr = torch.empty_like(O)
+    ts = []
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        sa.forward_sparsepr(Q, K, V, rt, cfg, probes_per_block=P, rank=rank, ridge=ridge, out=Opr, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    Okept = sa.forward(Q, K, V, rt, dataclasses.replace(cfg, no_residual=True))
+    Od = sa.dense_ref_gpu(Q, K, V, block_q=cfg.block_q)
+    torch.cuda.synchronize()
+    err = lambda A: float(torch.linalg.norm((A.float() - Od.float()).flatten()) / torch.linalg.norm(Od.float().flatten()))
+    return {"probes_per_block": P, "rank": rank, "ridge": ridge, "ms_median": median(ts[1:]),
+            "rel_fro_vs_dense": {"block_residual": err(O), "probe_fitted": err(Opr), "kept_tokens_only": err(Okept)}}
+
+
 def issued_mfma_flops(w, rt, mask, cfg):
     """Matrix-core flops the forward kernel issues per launch, counting padded
     rows: every query block runs block_q rows (the last one padded), every kept
@@ -415,6 +442,7 @@ def main():
         "timing_warm": warm,
         "timing_cold": cold,
         "permute": permute_timing(sa, Q, w) if w.hilbert else None,
+        "sparsepr": sparsepr_compare(sa, Q, K, V, rt, cfg, O, args.sparsepr) if args.sparsepr else None,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

@@ -15,5 +15,6 @@ Hilbert token order (video grid T x Hh x W after an n0-token prefix):
     o = sa.permute_tokens(o_h, perm, n0, inverse=True)  # back to raster order
 """
 from .binding import (ABSOLUTE, CENTROID, FLAG_FUSED, FLAG_NO_RESIDUAL, FLAG_PAMA, PAMA, RELATIVE, TOPP, Config, Route, SaParams, SaRoute,  # noqa: F401
-                      SparseAttnError, dense_flops, dense_ref_gpu, forward, hilbert_order, kv_idx_cap,
-                      last_error, make_params, permute_tokens, route, route_sizes, status_string)
+                      SparseAttnError, dense_flops, dense_ref_gpu, forward, forward_sparsepr, hilbert_order,
+                      kv_idx_cap, last_error, make_params, permute_tokens, route, route_sizes,
+                      sparsepr_workspace_size, status_string)

@@ -1,7 +1,8 @@
 """ctypes binding of libsparse_attn.so (argument marshalling only).
 
 Same names as the C ABI in include/sparse_attn.h: route, forward,
-dense_ref_gpu, route_sizes, kv_idx_cap, hilbert_order, permute_tokens.  Torch tensors supply device memory
+dense_ref_gpu, route_sizes, kv_idx_cap, hilbert_order, permute_tokens,
+forward_sparsepr, sparsepr_workspace_size.  Torch tensors supply device memory
 and the current HIP stream; every step of the computation runs in the
 library's HIP kernels.  If the library has not been built the import fails.
 """
@@ -67,6 +68,11 @@ def _load():
     lib.sparse_attn_hilbert_order.restype = ctypes.c_int
     lib.sparse_attn_permute_tokens.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, i32, vp, vp, vp]
     lib.sparse_attn_permute_tokens.restype = ctypes.c_int
+    lib.sparse_attn_sparsepr_workspace_size.argtypes = [P, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.sparse_attn_sparsepr_workspace_size.restype = ctypes.c_int
+    lib.sparse_attn_forward_sparsepr.argtypes = [P, vp, vp, vp, R, i32, i32, ctypes.c_float, vp, ctypes.c_size_t,
+                                                 vp, vp]
+    lib.sparse_attn_forward_sparsepr.restype = ctypes.c_int
     lib.sparse_attn_status_string.argtypes = [ctypes.c_int]
     lib.sparse_attn_status_string.restype = ctypes.c_char_p
     lib.sparse_attn_last_error.argtypes = []
@@ -205,6 +211,30 @@ def dense_ref_gpu(q, k, v, block_q: int = 128, scale: float = 0.0, out: torch.Te
     _check(lib.sparse_attn_dense_ref_gpu(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                          L.data_ptr() if lse else None, _stream(q.device)))
     return (o, L) if lse else o
+
+
+def sparsepr_workspace_size(q, cfg: Config, probes_per_block: int) -> int:
+    """sparse_attn_sparsepr_workspace_size: bytes of the probe-fitted residual's workspace."""
+    p = make_params(q, cfg)
+    n = ctypes.c_size_t()
+    _check(lib.sparse_attn_sparsepr_workspace_size(ctypes.byref(p), probes_per_block, ctypes.byref(n)))
+    return n.value
+
+
+def forward_sparsepr(q, k, v, rt: Route, cfg: Config, probes_per_block: int = 2, rank: int = 8,
+                     ridge: float = 1e-3, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """sparse_attn_forward_sparsepr: attention over the kept tokens, corrected by an
+    affine map fitted on exact probe rows (in place of the block residual)."""
+    _check_qkv(q, k, v)
+    p = make_params(q, cfg)
+    n = sparsepr_workspace_size(q, cfg, probes_per_block)
+    ws = workspace if workspace is not None else torch.empty(n, dtype=torch.uint8, device=q.device)
+    o = out if out is not None else torch.empty_like(q)
+    _check(lib.sparse_attn_forward_sparsepr(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                            ctypes.byref(rt.c), probes_per_block, rank, ridge, ws.data_ptr(),
+                                            ws.numel(), o.data_ptr(), _stream(q.device)))
+    return o
 
 
 def hilbert_order(T: int, Hh: int, W: int) -> torch.Tensor:

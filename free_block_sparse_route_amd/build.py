@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparse_attn.so")
-SOURCES = ("sa_api.hip", "sa_route.hip", "sa_flash.hip", "sa_permute.hip")
+SOURCES = ("sa_api.hip", "sa_route.hip", "sa_flash.hip", "sa_permute.hip", "sa_sparsepr.hip")
 ARCH = "gfx950"
 
 FLAGS = [

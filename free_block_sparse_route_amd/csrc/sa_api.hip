@@ -179,18 +179,20 @@ sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, co
 }
 
 static sa_status run_flash(const sa_params *p, const void *q, const void *k, const void *v,
-                           const sa_route *r, void *o, float *lse, void *stream, const char *who) {
+                           const sa_route *r, void *o, float *lse, void *stream, const char *who,
+                           float *o32 = nullptr, bool no_residual = false) {
     const Dims d = dims_of(p);
     sa::FlashArgs fa;
     memset(&fa, 0, sizeof fa);
-    fa.N = p->N; fa.block_q = p->block_q; fa.block_k = p->block_k;
+    fa.N = p->N; fa.Nq = p->N; fa.block_q = p->block_q; fa.block_k = p->block_k;
     fa.n_qb = d.n_qb; fa.n_kb = d.n_kb; fa.mask_words = d.words;
     const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->d);
     fa.scale_log2 = (float)(scale * 1.4426950408889634);
     fa.lse = lse;
+    fa.o32 = o32;
     if (r) {
         fa.kv_idx_cap = r->kv_idx_cap;
-        fa.residual = (p->flags & SA_FLAG_NO_RESIDUAL) ? 0 : 1;
+        fa.residual = ((p->flags & SA_FLAG_NO_RESIDUAL) || no_residual) ? 0 : 1;
         fa.kv_count = r->kv_count; fa.kv_idx = r->kv_idx; fa.work_order = r->work_order;
         fa.kv_mask = r->kv_mask; fa.kv_split = (const sa::bf16 *)r->kv_split;
         if (p->flags & SA_FLAG_FUSED) {
@@ -278,6 +280,104 @@ sa_status sparse_attn_permute_tokens(int32_t B, int32_t H, int32_t N, int32_t d,
     a.inverse = inverse;
     hipError_t e = sa::launch_permute(in, out, perm, a, B * H, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "permute: launch");
+    return SA_OK;
+}
+
+// Probe-fitted residual: workspace pieces, each 256-byte aligned.
+namespace {
+struct PrLayout {
+    size_t qp, od32, o32, scratch, cb_mat, cb_vec, total;
+    int M;
+};
+PrLayout pr_layout(const sa_params *p, int per_block) {
+    const Dims d = dims_of(p);
+    const size_t es = p->dtype == SA_BF16 ? 2 : 4;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    PrLayout L;
+    L.M = d.n_qb * per_block;
+    const size_t BH = (size_t)d.BH, D = (size_t)p->d;
+    size_t off = 0;
+    L.qp = off; off += up(BH * L.M * D * es);
+    L.od32 = off; off += up(BH * L.M * D * 4);
+    L.o32 = off; off += up(BH * (size_t)p->N * D * 4);
+    L.scratch = off; off += up(BH * 3 * D * D * 4);
+    L.cb_mat = off; off += up(BH * D * D * 4);
+    L.cb_vec = off; off += up(BH * D * 4);
+    L.total = off;
+    return L;
+}
+
+sa_status check_pr(const sa_params *p, int32_t per_block, int32_t rank, float ridge) {
+    if (per_block < 1 || per_block > sa::kPrMaxPerBlock)
+        return fail(SA_ERR_INVALID_ARG, "probes_per_block %d outside [1, %d]", per_block, sa::kPrMaxPerBlock);
+    const int rmax = sa::kPrMaxRank < p->d ? sa::kPrMaxRank : p->d;
+    if (rank < 1 || rank > rmax) return fail(SA_ERR_INVALID_ARG, "rank %d outside [1, %d]", rank, rmax);
+    if (!(ridge >= 0.f) || isinf(ridge)) return fail(SA_ERR_INVALID_ARG, "ridge must be finite and >= 0");
+    if (p->flags & SA_FLAG_FUSED) return fail(SA_ERR_UNSUPPORTED, "probe-fitted residual after fused routing");
+    if (dims_of(p).n_qb * per_block < 2) return fail(SA_ERR_INVALID_ARG, "fewer than 2 probe rows");
+    return SA_OK;
+}
+}  // namespace
+
+sa_status sparse_attn_sparsepr_workspace_size(const sa_params *p, int32_t probes_per_block, size_t *bytes) {
+    sa_status s = check_params(p, true);
+    if (s != SA_OK) return s;
+    if (!bytes) return fail(SA_ERR_INVALID_ARG, "bytes is NULL");
+    if (probes_per_block < 1 || probes_per_block > sa::kPrMaxPerBlock)
+        return fail(SA_ERR_INVALID_ARG, "probes_per_block %d outside [1, %d]", probes_per_block, sa::kPrMaxPerBlock);
+    *bytes = pr_layout(p, probes_per_block).total;
+    return SA_OK;
+}
+
+sa_status sparse_attn_forward_sparsepr(const sa_params *p, const void *q, const void *k, const void *v,
+                                       const sa_route *r, int32_t probes_per_block, int32_t rank, float ridge,
+                                       void *workspace, size_t workspace_bytes, void *o, void *stream) {
+    sa_status s = check_params(p, true);
+    if (s != SA_OK) return s;
+    if ((s = check_pr(p, probes_per_block, rank, ridge)) != SA_OK) return s;
+    if ((s = check_ptr(q, "q")) || (s = check_ptr(k, "k")) || (s = check_ptr(v, "v")) ||
+        (s = check_ptr(o, "o")) || (s = check_ptr(r, "route")) || (s = check_ptr(workspace, "workspace")))
+        return s;
+    if ((s = check_ptr(r->kv_count, "route.kv_count")) || (s = check_ptr(r->kv_idx, "route.kv_idx")) ||
+        (s = check_ptr(r->kv_mask, "route.kv_mask")) || (s = check_ptr(r->kv_split, "route.kv_split")) ||
+        (s = check_ptr(r->work_order, "route.work_order")))
+        return s;
+    if (r->kv_idx_cap < min_cap(p))
+        return fail(SA_ERR_CAPACITY, "route.kv_idx_cap %d < required %d", r->kv_idx_cap, min_cap(p));
+    const PrLayout L = pr_layout(p, probes_per_block);
+    if (workspace_bytes < L.total)
+        return fail(SA_ERR_CAPACITY, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
+    const Dims d = dims_of(p);
+    hipStream_t st = (hipStream_t)stream;
+    unsigned char *ws = (unsigned char *)workspace;
+    sa::PrArgs a;
+    a.N = p->N; a.M = L.M; a.per_block = probes_per_block; a.block_q = p->block_q; a.rank = rank; a.ridge = ridge;
+    a.O32 = (const float *)(ws + L.o32);
+    a.Od32 = (const float *)(ws + L.od32);
+    a.scratch = (float *)(ws + L.scratch);
+    a.CB = (float *)(ws + L.cb_mat);
+    a.Cb = (float *)(ws + L.cb_vec);
+    // 1. sparse output over the kept tokens only, fp32
+    if ((s = run_flash(p, q, k, v, r, nullptr, nullptr, stream, "sparsepr: sparse pass", (float *)(ws + L.o32),
+                       true)) != SA_OK)
+        return s;
+    // 2. probe queries, gathered, attended densely in fp32
+    hipError_t e = sa::launch_sparsepr_step(0, p->dtype, p->d, q, ws + L.qp, nullptr, a, (int)d.BH, st);
+    if (e != hipSuccess) return hip_fail(e, "sparsepr: gather launch");
+    sa::FlashArgs fa;
+    memset(&fa, 0, sizeof fa);
+    fa.N = p->N; fa.Nq = L.M; fa.block_q = p->block_q; fa.block_k = p->block_k;
+    fa.n_qb = (L.M + p->block_q - 1) / p->block_q; fa.n_kb = d.n_kb; fa.mask_words = d.words;
+    const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->d);
+    fa.scale_log2 = (float)(scale * 1.4426950408889634);
+    fa.o32 = (float *)(ws + L.od32);
+    e = sa::launch_flash(p->dtype, p->d, p->block_q, ws + L.qp, k, v, nullptr, fa, (int)d.BH, st);
+    if (e != hipSuccess) return hip_fail(e, "sparsepr: probe pass launch");
+    // 3. fit, 4. apply
+    e = sa::launch_sparsepr_step(1, p->dtype, p->d, nullptr, nullptr, nullptr, a, (int)d.BH, st);
+    if (e != hipSuccess) return hip_fail(e, "sparsepr: fit launch");
+    e = sa::launch_sparsepr_step(2, p->dtype, p->d, nullptr, nullptr, o, a, (int)d.BH, st);
+    if (e != hipSuccess) return hip_fail(e, "sparsepr: apply launch");
     return SA_OK;
 }
 

@@ -710,9 +710,10 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
     const int lane = lane_id();
     const int h = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const size_t head = (size_t)bh * a.N * D;
+    const size_t head = (size_t)bh * a.N * D;            // keys and values
+    const size_t qhead = (size_t)bh * a.Nq * D;          // queries and outputs
     const int qrow = I * a.block_q + wave * 32 + l32;
-    const bool row_ok = qrow < a.N;
+    const bool row_ok = qrow < a.Nq;
 
     Lanes<D, BQ> ln;
     ln.init(wave, lane);
@@ -725,7 +726,7 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
         const bf16x8 zero = {};
 #pragma unroll
         for (int c2 = 0; c2 < D / 16; ++c2) {
-            const size_t off = head + (size_t)qrow * D + 16 * c2 + 8 * h;
+            const size_t off = qhead + (size_t)qrow * D + 16 * c2 + 8 * h;
             if constexpr (kF32) {
                 float x[8];
                 if (row_ok) Ld8<float>::load_f32(reinterpret_cast<const float *>(q) + off, x);
@@ -884,15 +885,27 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
     const float lt = row_pair_sum(sm.l_run);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (row_ok) {
-        T *orow = o + head + (size_t)qrow * D;
+        if (a.o32) {                     // fp32 output (an intermediate of a later step)
+            float *orow = a.o32 + qhead + (size_t)qrow * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                Store4<T>::st(orow + 32 * db + 8 * g + 4 * h, sm.acc[db][4 * g] * inv, sm.acc[db][4 * g + 1] * inv,
-                              sm.acc[db][4 * g + 2] * inv, sm.acc[db][4 * g + 3] * inv);
+                for (int g = 0; g < 4; ++g)
+                    Store4<float>::st(orow + 32 * db + 8 * g + 4 * h, sm.acc[db][4 * g] * inv,
+                                      sm.acc[db][4 * g + 1] * inv, sm.acc[db][4 * g + 2] * inv,
+                                      sm.acc[db][4 * g + 3] * inv);
+        } else {
+            T *orow = o + qhead + (size_t)qrow * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    Store4<T>::st(orow + 32 * db + 8 * g + 4 * h, sm.acc[db][4 * g] * inv,
+                                  sm.acc[db][4 * g + 1] * inv, sm.acc[db][4 * g + 2] * inv,
+                                  sm.acc[db][4 * g + 3] * inv);
+        }
         if (a.lse && h == 0)
-            a.lse[(size_t)bh * a.N + qrow] = lt > 0.f ? (sm.m_ref + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+            a.lse[(size_t)bh * a.Nq + qrow] = lt > 0.f ? (sm.m_ref + log2f(lt)) * 0.69314718055994531f : -INFINITY;
     }
 }
 

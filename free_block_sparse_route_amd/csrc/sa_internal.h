@@ -32,6 +32,8 @@ struct SelectArgs {
 
 struct FlashArgs {
     int N, block_q, block_k, n_qb, n_kb, mask_words, kv_idx_cap;
+    int Nq;                              // query rows per (b, h): N, or the probe count of a probe pass
+    float *o32;                          // when set, O is written here in fp32 (o unused)
     float scale_log2;                    // logit scale times log2(e)
     int residual;                        // fold dropped blocks (route present)
     const int32_t *kv_count, *kv_idx, *work_order;
@@ -70,6 +72,22 @@ size_t select_lds_bytes(int G, int n_kb, int D);
 // Sparse forward when a.kv_idx != nullptr, dense otherwise.
 hipError_t launch_flash(int dtype, int D, int BQ, const void *q, const void *k, const void *v,
                         void *o, const FlashArgs &a, int BH, hipStream_t st);
+
+// Probe-fitted residual correction.
+constexpr int kPrMaxRank = 16;
+constexpr int kPrMaxPerBlock = 16;
+struct PrArgs {
+    int N, M, per_block, block_q, rank;  // M = n_qb * per_block probes per (b, h)
+    float ridge;
+    const float *O32;                    // [BH, N, D] sparse output (kept tokens only), fp32
+    const float *Od32;                   // [BH, M, D] dense output at the probes, fp32
+    float *scratch;                      // [BH, 3, D, D] Gram matrices
+    float *CB;                           // [BH, D, D] B, then B Pk
+    float *Cb;                           // [BH, D] b, then b Pk
+};
+// step 0: gather the probe queries of q into qp; 1: fit; 2: apply to o
+hipError_t launch_sparsepr_step(int step, int dtype, int D, const void *q, void *qp, void *o, const PrArgs &a,
+                                int BH, hipStream_t st);
 
 // Token permutation on the GPU; host Hilbert order of a T x Hh x W grid on the
 // 2^b cube (returns the number of points written to perm).

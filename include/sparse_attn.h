@@ -194,6 +194,28 @@ sa_status sparse_attn_forward(const sa_params *p, const void *q, const void *k, 
 sa_status sparse_attn_dense_ref_gpu(const sa_params *p, const void *q, const void *k,
                                     const void *v, void *o, float *lse, void *stream);
 
+/* Probe-fitted residual correction (SparsePR summary, section B), a second way
+ * to correct the sparse output under the same route, in place of the block
+ * residual:
+ *   1. O_s: attention over the kept tokens only;
+ *   2. probes: probes_per_block rows per query block, evenly spread (row
+ *      I*block_q + floor((j + 1/2) m_I / probes_per_block)), attended densely;
+ *   3. per (b, h), R = O_dense - O_s at the probes is fitted as R ~ b + x B,
+ *      x = O_s (ridge regression with an unpenalised intercept, ridge
+ *      lam = ridge * trace(Xc^T Xc) / d on the centred probe outputs Xc), and
+ *      the map is projected on the `rank` leading right singular vectors of R;
+ *   4. o = O_s + (b + O_s B) Pk on every row that is not a probe, O_dense on
+ *      probe rows.
+ * All intermediates are fp32 in the caller's workspace, of the size
+ * sparse_attn_sparsepr_workspace_size() gives (host only, no HIP calls).
+ * probes_per_block in [1, 16], rank in [1, min(16, d)], ridge >= 0; the route
+ * must not be fused.  o has the layout and dtype of q.  The workspace must not
+ * be shared by concurrent calls. */
+sa_status sparse_attn_sparsepr_workspace_size(const sa_params *p, int32_t probes_per_block, size_t *bytes);
+sa_status sparse_attn_forward_sparsepr(const sa_params *p, const void *q, const void *k, const void *v,
+                                       const sa_route *r, int32_t probes_per_block, int32_t rank, float ridge,
+                                       void *workspace, size_t workspace_bytes, void *o, void *stream);
+
 /* Token reordering (DFSAttn abstract: tokens reordered along a 3D Hilbert curve
  * before blocking, so that a block of consecutive tokens is compact in space
  * and time).  The library orders a T x Hh x W video token grid and permutes

@@ -23,7 +23,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     lib = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -82,6 +82,35 @@ def test_fused_floor_free_configurations_accepted():
     for kw in (dict(flags=4), dict(flags=4, tau_mode=1, min_keep=0), dict(flags=4, tau=1.0),
                dict(flags=5, min_keep=0, tau=3.0)):
         assert B.lib.sparse_attn_kv_idx_cap(ctypes.byref(params(**kw))) > 0, kw
+
+
+@pytest.mark.parametrize("per,rank,ridge,flags,status", [
+    (0, 4, 1e-3, 0, B.SA_ERR_INVALID_ARG), (17, 4, 1e-3, 0, B.SA_ERR_INVALID_ARG),
+    (2, 0, 1e-3, 0, B.SA_ERR_INVALID_ARG), (2, 17, 1e-3, 0, B.SA_ERR_INVALID_ARG),
+    (2, 4, -1.0, 0, B.SA_ERR_INVALID_ARG), (2, 4, float("inf"), 0, B.SA_ERR_INVALID_ARG),
+    (2, 4, 1e-3, 4, B.SA_ERR_UNSUPPORTED),
+])
+def test_sparsepr_rejects_bad_arguments_before_launch(per, rank, ridge, flags, status):
+    p = params(flags=flags)
+    r = B.SaRoute(*([0x1000] * len(B.BUFFERS)), 1 << 10)
+    st = B.lib.sparse_attn_forward_sparsepr(ctypes.byref(p), 0x1000, 0x1000, 0x1000, ctypes.byref(r), per, rank,
+                                            ridge, 0x1000, 1 << 40, 0x1000, None)
+    assert st == status, B.lib.sparse_attn_last_error().decode()
+
+
+def test_sparsepr_workspace_size_and_capacity():
+    p = params()
+    n = ctypes.c_size_t()
+    assert B.lib.sparse_attn_sparsepr_workspace_size(ctypes.byref(p), 2, ctypes.byref(n)) == B.SA_OK
+    # N = 1000, d = 128, bf16, B*H = 2, block_q = 128: M = 8 * 2 = 16 probes
+    up = lambda x: (x + 255) // 256 * 256
+    want = (up(2 * 16 * 128 * 2) + up(2 * 16 * 128 * 4) + up(2 * 1000 * 128 * 4) + up(2 * 3 * 128 * 128 * 4)
+            + up(2 * 128 * 128 * 4) + up(2 * 128 * 4))
+    assert n.value == want
+    r = B.SaRoute(*([0x1000] * len(B.BUFFERS)), 1 << 10)
+    st = B.lib.sparse_attn_forward_sparsepr(ctypes.byref(p), 0x1000, 0x1000, 0x1000, ctypes.byref(r), 2, 4, 1e-3,
+                                            0x1000, want - 1, 0x1000, None)
+    assert st == B.SA_ERR_CAPACITY
 
 
 def test_kv_idx_cap_rules():
