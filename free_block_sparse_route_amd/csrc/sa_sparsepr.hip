@@ -22,7 +22,7 @@
 namespace sa {
 
 constexpr int kPrThreads = 256;
-constexpr int kPrIters = 60;             // subspace iterations
+constexpr int kPrIters = 40;             // subspace iterations
 
 __device__ __forceinline__ int probe_row(int j, const PrArgs &a) {
     const int I = j / a.per_block, jj = j - I * a.per_block;
@@ -48,6 +48,25 @@ __global__ __launch_bounds__(kPrThreads) void probe_gather_kernel(const T *__res
 // Lower triangle of a D x D matrix, packed by rows.
 __device__ __forceinline__ int tri(int i, int j) { return i * (i + 1) / 2 + j; }
 
+// sum over k = k0, k0 + step, ... < k1 of x[k * sx] * y[k * sy] (LDS), with eight
+// independent partial sums so that the reads are issued ahead of their use
+__device__ __forceinline__ float lds_dot(const float *x, int sx, const float *y, int sy, int k0, int k1, int step) {
+    float p[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int k = k0;
+    for (; k + 7 * step < k1; k += 8 * step) {
+        float xv[8], yv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            xv[u] = x[(k + u * step) * sx];
+            yv[u] = y[(k + u * step) * sy];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) p[u] = fmaf(xv[u], yv[u], p[u]);
+    }
+    for (; k < k1; k += step) p[0] = fmaf(x[k * sx], y[k * sy], p[0]);
+    return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+}
+
 // sum over the probes of A[j][r] * B[j][c] for the D x D entries a thread owns
 // (row r, columns c0 .. c0 + D/2 - 1); A, B in {0: x - xm, 1: r - rm, 2: r}.
 // Probe rows are staged in LDS 16 at a time.
@@ -70,6 +89,7 @@ __device__ void gram(const PrArgs &a, int bh, const float *xm, const float *rm, 
     };
     for (int j0 = 0; j0 < a.M; j0 += JS) {
         __syncthreads();
+#pragma unroll
         for (int e = threadIdx.x; e < JS * D; e += kPrThreads) {
             const int j = j0 + e / D, f = e % D;
             SA[e] = j < a.M ? val(ka, j, f) : 0.f;
@@ -88,15 +108,29 @@ __device__ void gram(const PrArgs &a, int bh, const float *xm, const float *rm, 
         for (int c = 0; c < H; ++c) out[r * D + c0 + c] = acc[c];
 }
 
+// LDS of the fit, one pool: the packed factor (later R^T R, then B Q), the
+// means, and a region that holds the staged probe rows (Gram phase), 32
+// solution columns (solve phase) or the subspace basis (iteration phase).
+template <int D>
+struct FitLds {
+    static constexpr int kTri = D * (D + 1) / 2;
+    static constexpr int kRegion = 32 * D > 2 * 16 * D ? 32 * D : 2 * 16 * D;   // >= D * kPrMaxRank too
+    static_assert(kRegion >= D * kPrMaxRank, "basis fits the region");
+    static constexpr int kFloats = kTri + 2 * D + 64 + kRegion;
+};
+
 template <int D>
 __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
+    using FL = FitLds<D>;
     const int bh = blockIdx.x;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
-    __shared__ float xm[D], rm[D];
-    __shared__ float L[D * (D + 1) / 2];
-    __shared__ float Qs[D * kPrMaxRank];
-    __shared__ float red[kPrThreads / kWave];
-    __shared__ float SA[16 * D], SB[16 * D];
+    __shared__ float pool[FL::kFloats];
+    float *L = pool;                         // packed lower triangle
+    float *xm = pool + FL::kTri, *rm = xm + D;
+    float *red = rm + D;                     // 64 floats of small values
+    float *wb = red + 16;
+    float *reg = red + 64;                   // the phase region
+    float *SA = reg, *SB = reg + 16 * D;
     float *Gm = a.scratch + (size_t)bh * 3 * D * D;      // centred X^T X, then X^T R, then R^T R
     float *Hm = Gm + D * D;
     float *Sm = Hm + D * D;
@@ -109,6 +143,7 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
     // means of x and r over the probes
     if (threadIdx.x < D) {
         float sx = 0.f, sr = 0.f;
+#pragma unroll 8
         for (int j = 0; j < a.M; ++j) {
             const float x = Os[(size_t)probe_row(j, a) * D + threadIdx.x];
             sx += x;
@@ -134,12 +169,10 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
 #pragma unroll
     for (int w = 0; w < kPrThreads / kWave; ++w) trace += red[w];
     const float lam = a.ridge * trace / (float)D;
-    for (int e = threadIdx.x; e < D * (D + 1) / 2; e += kPrThreads) {
-        int i = (int)((sqrtf(8.f * e + 1.f) - 1.f) * 0.5f);
-        while (tri(i + 1, 0) <= e) ++i;
-        while (tri(i, 0) > e) --i;
-        const int j = e - tri(i, 0);
-        L[e] = Gm[i * D + j] + (i == j ? lam : 0.f);
+#pragma unroll 16
+    for (int e = threadIdx.x; e < D * D; e += kPrThreads) {
+        const int i = e / D, j = e - (e / D) * D;
+        if (j <= i) L[tri(i, j)] = Gm[e] + (i == j ? lam : 0.f);
     }
     __syncthreads();
 
@@ -151,15 +184,22 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
             if (lane == 0) L[tri(j, j)] = djj;
             __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): this wave's LDS writes are done
             __builtin_amdgcn_wave_barrier();
-            // trailing update of the lower triangle below row j
-            const int n = D - j - 1;
-            for (int e = lane; e < n * (n + 1) / 2; e += kWave) {
-                int ii = (int)((sqrtf(8.f * e + 1.f) - 1.f) * 0.5f);
-                while ((ii + 1) * (ii + 2) / 2 <= e) ++ii;
-                while (ii * (ii + 1) / 2 > e) --ii;
-                const int kk = e - ii * (ii + 1) / 2;
-                const int i = j + 1 + ii, k = j + 1 + kk;
-                L[tri(i, k)] -= L[tri(i, j)] * L[tri(k, j)];
+            // trailing update of the lower triangle below row j, a row per lane
+            for (int i = j + 1 + lane; i < D; i += kWave) {
+                const float lij = L[tri(i, j)];
+                float *Li = L + tri(i, 0);
+                int k = j + 1;
+                for (; k + 7 <= i; k += 8) {             // eight reads ahead of the writes
+                    float li[8], lk[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        li[u] = Li[k + u];
+                        lk[u] = L[tri(k + u, j)];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) Li[k + u] = li[u] - lij * lk[u];
+                }
+                for (; k <= i; ++k) Li[k] -= lij * L[tri(k, j)];
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_wave_barrier();
@@ -167,18 +207,53 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
     }
     __syncthreads();
 
-    // B = (L L^T)^-1 H, a column per thread: forward then backward substitution
-    if (threadIdx.x < D) {
-        const int c = threadIdx.x;
-        for (int i = 0; i < D; ++i) {
-            float y = Hm[i * D + c];
-            for (int k = 0; k < i; ++k) y -= L[tri(i, k)] * Bm[k * D + c];
-            Bm[i * D + c] = y / L[tri(i, i)];
-        }
-        for (int i = D - 1; i >= 0; --i) {
-            float y = Bm[i * D + c];
-            for (int k = i + 1; k < D; ++k) y -= L[tri(k, i)] * Bm[k * D + c];
-            Bm[i * D + c] = y / L[tri(i, i)];
+    // B = (L L^T)^-1 H, 32 columns at a time in LDS, by one wave: lane (hh, c)
+    // takes column c and half of each dot product; the halves meet by a swap
+    // of the wave's halves
+    if (wave == 0) {
+        float *T = reg;                                   // T[i * 32 + c]
+        const int c = lane & 31, hh = lane >> 5;
+        for (int c0 = 0; c0 < D; c0 += 32) {
+#pragma unroll 16
+            for (int i = hh; i < D; i += 2) T[i * 32 + c] = Hm[i * D + c0 + c];
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            for (int i = 0; i < D; ++i) {                 // forward: L y = h
+                const float *Li = L + tri(i, 0);
+                float s = lds_dot(Li, 1, T + c, 32, hh, i, 2);
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+                s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                if (hh == 0) T[i * 32 + c] = (T[i * 32 + c] - s) / Li[i];
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                __builtin_amdgcn_wave_barrier();
+            }
+            for (int i = D - 1; i >= 0; --i) {            // backward: L^T b = y
+                float s = 0.f;
+                {
+                    float p[4] = {0.f, 0.f, 0.f, 0.f};
+                    int k = i + 1 + hh;
+                    for (; k + 6 < D; k += 8) {
+                        float lv[4], tv[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            lv[u] = L[tri(k + 2 * u, i)];
+                            tv[u] = T[(k + 2 * u) * 32 + c];
+                        }
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) p[u] = fmaf(lv[u], tv[u], p[u]);
+                    }
+                    for (; k < D; k += 2) p[0] = fmaf(L[tri(k, i)], T[k * 32 + c], p[0]);
+                    s = (p[0] + p[1]) + (p[2] + p[3]);
+                }
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+                s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                if (hh == 0) T[i * 32 + c] = (T[i * 32 + c] - s) / L[tri(i, i)];
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                __builtin_amdgcn_wave_barrier();
+            }
+            for (int i = hh; i < D; i += 2) Bm[i * D + c0 + c] = T[i * 32 + c];
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
         }
     }
     __threadfence_block();
@@ -186,18 +261,28 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
     // intercept b = rm - xm B
     if (threadIdx.x < D) {
         float s = rm[threadIdx.x];
+#pragma unroll 16
         for (int i = 0; i < D; ++i) s -= xm[i] * Bm[i * D + threadIdx.x];
         bv[threadIdx.x] = s;
     }
 
-    // leading eigenvectors of S = R^T R by subspace iteration from a fixed start
+    // leading eigenvectors of S = R^T R by subspace iteration from a fixed start;
+    // S (symmetric) packed into LDS over the factor, which is no longer needed
+    __syncthreads();
+    float *Sp = L;
+    float *Qs = reg;                                      // Qs[i * K + c]
+#pragma unroll 16
+    for (int e = threadIdx.x; e < D * D; e += kPrThreads) {
+        const int i = e / D, j = e - (e / D) * D;
+        if (j <= i) Sp[tri(i, j)] = Sm[e];
+    }
     const int K = a.rank;
     for (int e = threadIdx.x; e < D * K; e += kPrThreads) {
         uint32_t hsh = (uint32_t)e * 2654435761u + 0x9e3779b9u;
         hsh ^= hsh >> 15;
         hsh *= 2246822519u;
         hsh ^= hsh >> 13;
-        Qs[e] = (float)(hsh & 0xffff) / 32768.f - 1.f;      // Qs[i * K + c]
+        Qs[e] = (float)(hsh & 0xffff) / 32768.f - 1.f;
     }
     __syncthreads();
     for (int it = 0; it <= kPrIters; ++it) {
@@ -207,8 +292,23 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
             int n_own = 0;
             for (int e = threadIdx.x; e < D * K; e += kPrThreads) {
                 const int i = e / K, c = e - (e / K) * K;
-                float s = 0.f;
-                for (int l = 0; l < D; ++l) s += Sm[i * D + l] * Qs[l * K + c];
+                float s = lds_dot(Sp + tri(i, 0), 1, Qs + c, K, 0, i, 1);
+                {
+                    float p[4] = {0.f, 0.f, 0.f, 0.f};
+                    int l = i;
+                    for (; l + 3 < D; l += 4) {
+                        float sv[4], qv[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            sv[u] = Sp[tri(l + u, i)];
+                            qv[u] = Qs[(l + u) * K + c];
+                        }
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) p[u] = fmaf(sv[u], qv[u], p[u]);
+                    }
+                    for (; l < D; ++l) p[0] = fmaf(Sp[tri(l, i)], Qs[l * K + c], p[0]);
+                    s += (p[0] + p[1]) + (p[2] + p[3]);
+                }
                 z[n_own++] = s;
             }
             __syncthreads();
@@ -237,17 +337,19 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
         __syncthreads();
     }
 
-    // W = B Q (D x K) in the rows of L (no longer needed), then C_B = W Q^T, C_b = (b Q) Q^T
+    // W = B Q (D x K) over the packed S (no longer needed), then
+    // C_B = W Q^T, C_b = (b Q) Q^T
     float *W = L;
     for (int e = threadIdx.x; e < D * K; e += kPrThreads) {
         const int i = e / K, c = e - (e / K) * K;
         float s = 0.f;
+#pragma unroll 16
         for (int l = 0; l < D; ++l) s += Bm[i * D + l] * Qs[l * K + c];
         W[e] = s;
     }
-    __shared__ float wb[kPrMaxRank];
     if (threadIdx.x < K) {
         float s = 0.f;
+#pragma unroll 16
         for (int l = 0; l < D; ++l) s += bv[l] * Qs[l * K + threadIdx.x];
         wb[threadIdx.x] = s;
     }
@@ -267,52 +369,70 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
 }
 
 // ------------------------------------------------------------------ apply
-// 64 rows per workgroup; thread t: row t / 4, output columns (t % 4) * D/4 ..
+// 64 rows per workgroup; thread t takes rows 4 (t / 16) .. +3 and columns
+// (t % 16) * D/16 .. (a 4 x D/16 register block).  X rows are padded by one
+// float so that the four rows a thread reads sit on different banks.
 template <typename T, int D>
 __global__ __launch_bounds__(kPrThreads) void pr_apply_kernel(T *__restrict__ o, PrArgs a) {
-    constexpr int CW = D / 4;                 // columns per thread
+    constexpr int CW = D / 16;                // columns per thread
     constexpr int KC = 32;                    // rows of C_B per staging step
+    constexpr int XS = D + 1;                 // padded row stride of X
     const int bh = blockIdx.y;
     const int r0 = blockIdx.x * 64;
-    __shared__ float X[64 * D];
+    __shared__ float X[64 * XS];
     __shared__ float Cs[KC * D];
     const float *Os = a.O32 + (size_t)bh * a.N * D;
     const float *CB = a.CB + (size_t)bh * D * D;
     const float *Cb = a.Cb + (size_t)bh * D;
     for (int e = threadIdx.x; e < 64 * D; e += kPrThreads) {
-        const int r = r0 + e / D;
-        X[e] = r < a.N ? Os[(size_t)r * D + (e % D)] : 0.f;
+        const int rr = e / D, f = e - (e / D) * D;
+        const int r = r0 + rr;
+        X[rr * XS + f] = r < a.N ? Os[(size_t)r * D + f] : 0.f;
     }
-    const int rl = threadIdx.x / 4, c0 = (threadIdx.x % 4) * CW;
-    float acc[CW];
+    const int rg = threadIdx.x / 16, c0 = (threadIdx.x % 16) * CW;
+    float acc[4][CW];
 #pragma unroll
-    for (int c = 0; c < CW; ++c) acc[c] = Cb[c0 + c];
+    for (int c = 0; c < CW; ++c) {
+        const float bc = Cb[c0 + c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][c] = bc;
+    }
     for (int k0 = 0; k0 < D; k0 += KC) {
         __syncthreads();
         for (int e = threadIdx.x; e < KC * D; e += kPrThreads) Cs[e] = CB[(size_t)k0 * D + e];
         __syncthreads();
+#pragma unroll 4
         for (int kk = 0; kk < KC; ++kk) {
-            const float x = X[rl * D + k0 + kk];
+            float x[4], cs[CW];
 #pragma unroll
-            for (int c = 0; c < CW; ++c) acc[c] = fmaf(x, Cs[kk * D + c0 + c], acc[c]);
+            for (int i = 0; i < 4; ++i) x[i] = X[(4 * rg + i) * XS + k0 + kk];
+#pragma unroll
+            for (int c = 0; c < CW; ++c) cs[c] = Cs[kk * D + c0 + c];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < CW; ++c) acc[i][c] = fmaf(x[i], cs[c], acc[i][c]);
         }
     }
-    const int r = r0 + rl;
-    if (r >= a.N) return;
-    // probed rows take their dense values
-    const int I = r / a.block_q, off = r - I * a.block_q;
-    const int m = min(a.block_q, a.N - I * a.block_q);
-    int probe = -1;
-    for (int jj = 0; jj < a.per_block; ++jj)
-        if ((2 * jj + 1) * m / (2 * a.per_block) == off) probe = I * a.per_block + jj;
-    T *orow = o + ((size_t)bh * a.N + r) * D + c0;
-    if (probe >= 0) {
-        const float *od = a.Od32 + ((size_t)bh * a.M + probe) * D + c0;
 #pragma unroll
-        for (int c = 0; c < CW; ++c) orow[c] = (T)od[c];
-    } else {
+    for (int i = 0; i < 4; ++i) {
+        const int rl = 4 * rg + i, r = r0 + rl;
+        if (r >= a.N) break;
+        // probed rows take their dense values
+        const int I = r / a.block_q, off = r - I * a.block_q;
+        const int m = min(a.block_q, a.N - I * a.block_q);
+        int probe = -1;
+        for (int jj = 0; jj < a.per_block; ++jj)
+            if ((2 * jj + 1) * m / (2 * a.per_block) == off) probe = I * a.per_block + jj;
+        T *orow = o + ((size_t)bh * a.N + r) * D + c0;
+        if (probe >= 0) {
+            const float *od = a.Od32 + ((size_t)bh * a.M + probe) * D + c0;
 #pragma unroll
-        for (int c = 0; c < CW; ++c) orow[c] = (T)(X[rl * D + c0 + c] + acc[c]);
+            for (int c = 0; c < CW; ++c) orow[c] = (T)od[c];
+        } else {
+#pragma unroll
+            for (int c = 0; c < CW; ++c) orow[c] = (T)(X[rl * XS + c0 + c] + acc[i][c]);
+        }
     }
 }
 
