@@ -206,8 +206,10 @@ sa_status sparse_attn_dense_ref_gpu(const sa_params *p, const void *q, const voi
  *      the map is projected on the `rank` leading right singular vectors of R;
  *   4. o = O_s + (b + O_s B) Pk on every row that is not a probe, O_dense on
  *      probe rows.
- * All intermediates are fp32 in the caller's workspace, of the size
- * sparse_attn_sparsepr_workspace_size() gives (host only, no HIP calls).
+ * Intermediates live in the caller's workspace, of the size
+ * sparse_attn_sparsepr_workspace_size() gives (host only, no HIP calls): the
+ * gathered probe queries in q's dtype; O_s, the probes' dense outputs and the
+ * fitted map (b, B Pk) in fp32.
  * probes_per_block in [1, 16], rank in [1, min(16, d)], ridge >= 0; the route
  * must not be fused.  o has the layout and dtype of q.  The workspace must not
  * be shared by concurrent calls. */
