@@ -99,6 +99,20 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Workgroup i of a launch runs on GPU die (XCD) i % 8: the dispatcher deals
+// workgroups to the 8 dies in turn.  die_task maps launch slot i of W to a
+// task so that, in each group of 8 * run consecutive slots, die x takes the
+// run consecutive tasks x * run .. x * run + run - 1 of the group; the last,
+// partial group keeps the plain order.  Tasks that share data (the work of
+// one head) then meet in one die's L2.  A bijection on 0..W-1.
+__device__ __forceinline__ int die_task(int i, int W, int run) {
+    const int span = 8 * run;
+    const int base = i - i % span;
+    if (base + span > W) return i;
+    const int r = i - base;
+    return base + (r & 7) * run + (r >> 3);
+}
+
 // Constant address space: loads through it at a wave-uniform address go
 // through the scalar cache.  Only for memory that nothing writes while the
 // kernel runs (buffers a previous kernel wrote).

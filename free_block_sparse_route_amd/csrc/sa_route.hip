@@ -59,16 +59,21 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const T *__restrict_
     for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[b][i] = 0.f;
+    // every load is issued before the first sum (a load under a branch would
+    // wait for the one before it); rows past the span re-read the span's last
+    // row and add nothing
+    constexpr int IT = 128 / RG;
+    float x[IT][8];
 #pragma unroll
-    for (int it = 0; it < 128 / RG; ++it) {
+    for (int it = 0; it < IT; ++it)
+        Ld8<T>::load_f32(X + (size_t)(r0 + min(g + it * RG, span - 1)) * D + c * 8, x[it]);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
         const int r = g + it * RG;
-        if (r < span) {
-            float x[8];
-            Ld8<T>::load_f32(X + (size_t)(r0 + r) * D + c * 8, x);
-            const int b = r >= bs;             // RG divides bs: uniform per iteration
+        const bool in = r < span;
+        const int b = r >= bs;                 // RG divides bs: uniform per iteration
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[b][i] += x[i];
-        }
+        for (int i = 0; i < 8; ++i) acc[b][i] += in ? x[it][i] : 0.f;
     }
     __shared__ float part[2][RG * D];
 #pragma unroll
@@ -435,12 +440,27 @@ __device__ __forceinline__ void row_stats_only(const float *S, int bh, int I, co
     }
 }
 
+// The pointer passes through the empty statement as a global-memory pointer,
+// so that the stores through it stay global stores (as a generic pointer they
+// would become flat stores, which also count on the LDS counter: every later
+// LDS wait would then wait for the stores too).
+template <typename T>
+__device__ __forceinline__ void launder_global(T *&p) {
+    __attribute__((address_space(1))) T *g = (__attribute__((address_space(1))) T *)p;
+    asm volatile("" : "+s"(g));
+    p = (T *)g;
+}
+
 __device__ __forceinline__ void launder(SelectArgs &a) {
     asm volatile("" : "+s"(a.N), "+s"(a.block_q), "+s"(a.block_k), "+s"(a.n_qb), "+s"(a.n_kb), "+s"(a.mask_words));
     asm volatile("" : "+s"(a.kv_idx_cap), "+s"(a.exact_tile_rows), "+s"(a.tau_mode), "+s"(a.max_keep),
                  "+s"(a.min_keep), "+s"(a.n_prefix), "+s"(a.stats_only));
     asm volatile("" : "+s"(a.scale), "+s"(a.ln_tau), "+s"(a.topp_target));
-    asm volatile("" : "+s"(a.kv_count), "+s"(a.kv_idx), "+s"(a.cost), "+s"(a.kv_mask), "+s"(a.row_stats));
+    launder_global(a.kv_count);
+    launder_global(a.kv_idx);
+    launder_global(a.cost);
+    launder_global(a.kv_mask);
+    launder_global(a.row_stats);
 }
 
 // R: proxy row chunks of 64 held in registers (R * 64 >= n_kb), 0: longer rows
@@ -448,8 +468,11 @@ __device__ __forceinline__ void launder(SelectArgs &a) {
 template <int D, int G, int R>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     extern __shared__ __attribute__((aligned(16))) float smem[];
-    const int bh = blockIdx.y;
-    const int I0 = blockIdx.x * G;
+    // one head's groups run on one die, which reads that head's key means once
+    const int n_grp = (a.n_qb + G - 1) / G;
+    const int task = die_task(blockIdx.x, (int)gridDim.x, n_grp);
+    const int bh = task / n_grp;
+    const int I0 = (task - bh * n_grp) * G;
     const int g_cnt = min(G, a.n_qb - I0);
     const int n = a.n_kb;
     float *S = smem;                                      // [G][n]
@@ -470,7 +493,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
             const float *src = a.q_mean + ((size_t)bh * a.n_qb + I0 + (ok ? i16 : 0)) * D + kg * KS;
 #pragma unroll
             for (int e = 0; e < KS; e += 4) {
-                const f32x4 x = ok ? *reinterpret_cast<const f32x4 *>(src + e) : f32x4{};
+                const f32x4 y = *reinterpret_cast<const f32x4 *>(src + e);   // row clamped: in bounds
+                const f32x4 x = ok ? y : f32x4{};
                 qv[e] = x[0];
                 qv[e + 1] = x[1];
                 qv[e + 2] = x[2];
@@ -485,7 +509,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
             const float *src = kb + (size_t)(J < n ? J : 0) * D + kg * KS;
 #pragma unroll
             for (int e = 0; e < KS; e += 4) {
-                const f32x4 x = J < n ? *reinterpret_cast<const f32x4 *>(src + e) : f32x4{};
+                const f32x4 y = *reinterpret_cast<const f32x4 *>(src + e);   // block clamped: in bounds
+                const f32x4 x = J < n ? y : f32x4{};
                 kv[e] = x[0];
                 kv[e + 1] = x[1];
                 kv[e + 2] = x[2];
@@ -620,7 +645,8 @@ __global__ __launch_bounds__(BQ * 2) void pama_kernel(const T *__restrict__ q, S
     float *part = smem + St::BYTES / 4;          // [WAVES][n]
     float *row = part + WAVES * n;               // [n]: ln A
     float *cq = row + n;                         // [BQ]: per-query log2 normaliser
-    const int bh = blockIdx.y, I = blockIdx.x;
+    const int task = die_task(blockIdx.x, (int)gridDim.x, a.n_qb);   // one head per die, as in select
+    const int bh = task / a.n_qb, I = task - bh * a.n_qb;
     const int lane = lane_id(), h = lane >> 5, l32 = lane & 31;
     const int wave = threadIdx.x / kWave;
     const int q0 = I * a.block_q;
@@ -749,7 +775,7 @@ size_t pama_lds_bytes(int n_kb, int BQ) {
 
 template <typename T, int D, int BQ, int R>
 static hipError_t launch_pama_t(const void *q, const SelectArgs &a, int BH, hipStream_t st) {
-    hipLaunchKernelGGL((pama_kernel<T, D, BQ, R>), dim3(a.n_qb, BH), dim3(BQ * 2), pama_lds_bytes(a.n_kb, BQ), st,
+    hipLaunchKernelGGL((pama_kernel<T, D, BQ, R>), dim3(a.n_qb * BH), dim3(BQ * 2), pama_lds_bytes(a.n_kb, BQ), st,
                        (const T *)q, a);
     return hipGetLastError();
 }
@@ -884,7 +910,7 @@ size_t select_lds_bytes(int G, int n_kb, int D) {
 template <int D, int G, int R>
 static hipError_t launch_select_t(const SelectArgs &a, int BH, hipStream_t st) {
     const size_t lds = select_lds_bytes(G, a.n_kb, D);
-    dim3 grid((a.n_qb + G - 1) / G, BH);
+    dim3 grid((a.n_qb + G - 1) / G * BH);
     hipLaunchKernelGGL((select_kernel<D, G, R>), grid, dim3(kSelectThreads), lds, st, a);
     return hipGetLastError();
 }

@@ -330,6 +330,30 @@ def test_work_order_by_cost_band():
     assert torch.equal(rt2.work_order, rt.work_order)
 
 
+def test_work_order_large():
+    """Enough items that the ordering workgroup cuts them into two-chunk tiles and
+    each wave loads its chunks in several batches; per-head query scales spread
+    the costs over many bands."""
+    m = sa()
+    B, H, N, d = 1, 240, 8192, 64
+    say(f"[case] schedule large B{B} H{H} N{N} d{d}")
+    g = torch.Generator(device="cuda").manual_seed(7)
+    # a random direction per 64-token block, shared by its queries and keys, so
+    # that block means are informative; query scales from flat to peaked heads
+    E = torch.randn(B, H, N // 64, 1, d, device="cuda", generator=g).expand(B, H, N // 64, 64, d).reshape(B, H, N, d)
+    s = torch.linspace(0.05, 1.5, H, device="cuda").view(1, H, 1, 1)
+    Q = (s * (E + 0.5 * torch.randn(B, H, N, d, device="cuda", generator=g))).to(torch.bfloat16)
+    K = (E + 0.5 * torch.randn(B, H, N, d, device="cuda", generator=g)).to(torch.bfloat16)
+    V = torch.randn(B, H, N, d, device="cuda", generator=g).to(torch.bfloat16)
+    rt = m.route(Q, K, V, m.Config(block_q=64, block_k=64, tau=0.02))
+    torch.cuda.synchronize()
+    cost = rt.cost.cpu().numpy().ravel().astype(np.int64)
+    assert cost.size == B * H * (N // 64) and cost.size > 64 * 448
+    band = np.floor(np.log2(np.maximum(cost, 1))).astype(np.int64)
+    assert len(np.unique(band)) > 3
+    assert np.array_equal(rt.work_order.cpu().numpy(), np.lexsort((np.arange(cost.size), -band)))
+
+
 def test_work_order_many_items():
     """More items than the ordering workgroup has threads, with ragged chunks."""
     w = S.small("sched_many", 2, 6, 64, (5, 12, 45), 64, 64, 0.02)
