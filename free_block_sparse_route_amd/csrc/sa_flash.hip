@@ -915,7 +915,7 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
 // the group, so that neighbouring query blocks, which keep mostly the same key
 // blocks, meet in one die's L2, while the order of the work list holds at the
 // scale of a group.  The last, partial group keeps the plain order.
-constexpr int kDieRun = 16;
+constexpr int kDieRun = 32;
 
 __device__ __forceinline__ int grid_position(int i, int W) {
     constexpr int kGroup = 8 * kDieRun;
