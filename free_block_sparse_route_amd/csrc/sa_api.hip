@@ -286,8 +286,8 @@ sa_status sparse_attn_permute_tokens(int32_t B, int32_t H, int32_t N, int32_t d,
 // Probe-fitted residual: workspace pieces, each 256-byte aligned.
 namespace {
 struct PrLayout {
-    size_t qp, od32, o32, scratch, cb_mat, cb_vec, total;
-    int M;
+    size_t qp, od32, o32, scratch, part, cmean, cb_mat, cb_vec, total;
+    int M, n_chunks;
 };
 PrLayout pr_layout(const sa_params *p, int per_block) {
     const Dims d = dims_of(p);
@@ -301,6 +301,9 @@ PrLayout pr_layout(const sa_params *p, int per_block) {
     L.od32 = off; off += up(BH * L.M * D * 4);
     L.o32 = off; off += up(BH * (size_t)p->N * D * 4);
     L.scratch = off; off += up(BH * 3 * D * D * 4);
+    L.n_chunks = (L.M + sa::kPrChunk - 1) / sa::kPrChunk;
+    L.part = off; off += up(BH * L.n_chunks * 3 * D * D * 4);
+    L.cmean = off; off += up(BH * L.n_chunks * 2 * D * 4);
     L.cb_mat = off; off += up(BH * D * D * 4);
     L.cb_vec = off; off += up(BH * D * 4);
     L.total = off;
@@ -355,6 +358,9 @@ sa_status sparse_attn_forward_sparsepr(const sa_params *p, const void *q, const 
     a.O32 = (const float *)(ws + L.o32);
     a.Od32 = (const float *)(ws + L.od32);
     a.scratch = (float *)(ws + L.scratch);
+    a.n_chunks = L.n_chunks;
+    a.part = (float *)(ws + L.part);
+    a.cmean = (float *)(ws + L.cmean);
     a.CB = (float *)(ws + L.cb_mat);
     a.Cb = (float *)(ws + L.cb_vec);
     // 1. sparse output over the kept tokens only, fp32

@@ -75,6 +75,7 @@ hipError_t launch_flash(int dtype, int D, int BQ, const void *q, const void *k, 
 
 // Probe-fitted residual correction.
 constexpr int kPrMaxRank = 16;
+constexpr int kPrChunk = 128;                    // probe rows per Gram workgroup
 constexpr int kPrMaxPerBlock = 16;
 struct PrArgs {
     int N, M, per_block, block_q, rank;  // M = n_qb * per_block probes per (b, h)
@@ -82,6 +83,9 @@ struct PrArgs {
     const float *O32;                    // [BH, N, D] sparse output (kept tokens only), fp32
     const float *Od32;                   // [BH, M, D] dense output at the probes, fp32
     float *scratch;                      // [BH, 3, D, D] Gram matrices
+    int n_chunks;                        // probe chunks of kPrChunk rows per (b, h)
+    float *part;                         // [BH, n_chunks, 3, D, D] Gram matrices of each chunk
+    float *cmean;                        // [BH, n_chunks, 2, D] chunk means of x and r
     float *CB;                           // [BH, D, D] B, then B Pk
     float *Cb;                           // [BH, D] b, then b Pk
 };

@@ -5,11 +5,16 @@
 //      no block residual);
 //   2. probe rows, P per query block evenly spread (row I*bq + floor((j+1/2) m_I / P)),
 //      gathered and attended densely (forward kernel, dense path), in fp32;
-//   3. per (b, h), one workgroup fits R = O_d - O_s at the probes as an affine
-//      map of x = O_s: centred Gram matrices, a ridge lam = ridge * trace / d,
-//      a Cholesky solve for B, the intercept b = rm - xm B; the k leading
-//      eigenvectors of R^T R (the right singular vectors of R) by subspace
-//      iteration; and the projected map C_B = B Pk, C_b = b Pk, Pk = V_k V_k^T;
+//   3. per (b, h) and chunk of kPrChunk probes, one workgroup forms the chunk's
+//      means and centred Gram matrices; then per (b, h) one workgroup combines
+//      the chunks (the centred scatter of a union is the sum of the chunks'
+//      plus n_c (m_c - m)(m_c - m)^T per chunk, which keeps the centring exact
+//      in fp32) and fits R = O_d - O_s at the probes as an affine
+//      map of x = O_s, B = (G + lam I)^-1 H with a ridge lam = ridge * trace / d
+//      and the intercept b = rm - xm B, projected on the k leading eigenvectors
+//      Q of R^T R (the right singular vectors of R, by subspace iteration),
+//      Pk = Q Q^T.  Only B Q is formed: a Cholesky solve with the k columns of
+//      H Q; then C_B = (B Q) Q^T and C_b = (rm Q - xm B Q) Q^T;
 //   4. every row not probed takes O_s + C_b + O_s C_B, probed rows take O_d.
 //
 // Steps 3 and 4 are small: d x d matrices per head and one d x d product per row.
@@ -67,12 +72,12 @@ __device__ __forceinline__ float lds_dot(const float *x, int sx, const float *y,
     return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 }
 
-// sum over the probes of A[j][r] * B[j][c] for the D x D entries a thread owns
-// (row r, columns c0 .. c0 + D/2 - 1); A, B in {0: x - xm, 1: r - rm, 2: r}.
-// Probe rows are staged in LDS 16 at a time.
+// sum over the probes jb .. je - 1 of A[j][r] * B[j][c] for the D x D entries
+// a thread owns (row r, columns c0 .. c0 + D/2 - 1); A, B in {0: x - xm,
+// 1: r - rm, 2: r}.  Probe rows are staged in LDS 16 at a time.
 template <int D>
-__device__ void gram(const PrArgs &a, int bh, const float *xm, const float *rm, int ka, int kb, float *out,
-                     float *SA, float *SB) {
+__device__ void gram(const PrArgs &a, int bh, int jb, int je, const float *xm, const float *rm, int ka, int kb,
+                     float *out, float *SA, float *SB) {
     constexpr int H = D / 2, JS = 16;
     const int r = threadIdx.x / 2, c0 = (threadIdx.x & 1) * H;
     const bool active = threadIdx.x < 2 * D;
@@ -87,13 +92,13 @@ __device__ void gram(const PrArgs &a, int bh, const float *xm, const float *rm, 
         const float rr = Od[(size_t)j * D + f] - x;
         return k == 1 ? rr - rm[f] : rr;
     };
-    for (int j0 = 0; j0 < a.M; j0 += JS) {
+    for (int j0 = jb; j0 < je; j0 += JS) {
         __syncthreads();
 #pragma unroll
         for (int e = threadIdx.x; e < JS * D; e += kPrThreads) {
             const int j = j0 + e / D, f = e % D;
-            SA[e] = j < a.M ? val(ka, j, f) : 0.f;
-            SB[e] = j < a.M ? val(kb, j, f) : 0.f;
+            SA[e] = j < je ? val(ka, j, f) : 0.f;
+            SB[e] = j < je ? val(kb, j, f) : 0.f;
         }
         __syncthreads();
         if (active)
@@ -108,15 +113,60 @@ __device__ void gram(const PrArgs &a, int bh, const float *xm, const float *rm, 
         for (int c = 0; c < H; ++c) out[r * D + c0 + c] = acc[c];
 }
 
-// LDS of the fit, one pool: the packed factor (later R^T R, then B Q), the
-// means, and a region that holds the staged probe rows (Gram phase), 32
-// solution columns (solve phase) or the subspace basis (iteration phase).
+// One chunk of kPrChunk probes of one (b, h): its means of x and r, its
+// centred x^T x and x^T r, and its uncentred r^T r.
+template <int D>
+__global__ __launch_bounds__(kPrThreads) void pr_gram_kernel(PrArgs a) {
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int jb = c * kPrChunk, je = min(a.M, jb + kPrChunk);
+    __shared__ float SA[16 * D], SB[16 * D];
+    __shared__ float ps[kPrThreads / D][2][D];
+    __shared__ float xm[D], rm[D];
+    const float *Os = a.O32 + (size_t)bh * a.N * D;
+    const float *Od = a.Od32 + (size_t)bh * a.M * D;
+    {
+        constexpr int NP = kPrThreads / D;                // threads per feature
+        const int f = threadIdx.x % D, part = threadIdx.x / D;
+        float sx = 0.f, sr = 0.f;
+#pragma unroll 8
+        for (int j = jb + part; j < je; j += NP) {
+            const float x = Os[(size_t)probe_row(j, a) * D + f];
+            sx += x;
+            sr += Od[(size_t)j * D + f] - x;
+        }
+        ps[part][0][f] = sx;
+        ps[part][1][f] = sr;
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
+        float sx = 0.f, sr = 0.f;
+#pragma unroll
+        for (int q = 0; q < kPrThreads / D; ++q) {
+            sx += ps[q][0][threadIdx.x];
+            sr += ps[q][1][threadIdx.x];
+        }
+        const float inv = 1.f / (float)(je - jb);
+        xm[threadIdx.x] = sx * inv;
+        rm[threadIdx.x] = sr * inv;
+        float *cm = a.cmean + ((size_t)bh * a.n_chunks + c) * 2 * D;
+        cm[threadIdx.x] = sx * inv;
+        cm[D + threadIdx.x] = sr * inv;
+    }
+    __syncthreads();
+    float *out = a.part + ((size_t)bh * a.n_chunks + c) * 3 * D * D;
+    gram<D>(a, bh, jb, je, xm, rm, 0, 0, out, SA, SB);
+    gram<D>(a, bh, jb, je, xm, rm, 0, 1, out + D * D, SA, SB);
+    gram<D>(a, bh, jb, je, xm, rm, 2, 2, out + 2 * D * D, SA, SB);
+}
+
+// LDS of the fit, one pool: packed R^T R (subspace phase), then the packed
+// factor; the means; 32 solution columns; the subspace basis.
 template <int D>
 struct FitLds {
     static constexpr int kTri = D * (D + 1) / 2;
     static constexpr int kRegion = 32 * D > 2 * 16 * D ? 32 * D : 2 * 16 * D;   // >= D * kPrMaxRank too
     static_assert(kRegion >= D * kPrMaxRank, "basis fits the region");
-    static constexpr int kFloats = kTri + 2 * D + 64 + kRegion;
+    static constexpr int kFloats = kTri + 2 * D + 64 + kRegion + D * kPrMaxRank;
 };
 
 template <int D>
@@ -129,33 +179,49 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
     float *xm = pool + FL::kTri, *rm = xm + D;
     float *red = rm + D;                     // 64 floats of small values
     float *wb = red + 16;
-    float *reg = red + 64;                   // the phase region
-    float *SA = reg, *SB = reg + 16 * D;
+    float *reg = red + 64;                   // the solve's 32 columns
+    float *Qs = reg + FL::kRegion;           // the subspace basis, Qs[i * KP + c]
     float *Gm = a.scratch + (size_t)bh * 3 * D * D;      // centred X^T X, then X^T R, then R^T R
     float *Hm = Gm + D * D;
     float *Sm = Hm + D * D;
     float *Bm = a.CB + (size_t)bh * D * D;
     float *bv = a.Cb + (size_t)bh * D;
-    const float *Os = a.O32 + (size_t)bh * a.N * D;
-    const float *Od = a.Od32 + (size_t)bh * a.M * D;
     const float invM = 1.f / (float)a.M;
 
-    // means of x and r over the probes
+    // means of x and r over the probes: the chunks' means weighted by their rows
+    const int C = a.n_chunks;
+    const float *cmean = a.cmean + (size_t)bh * C * 2 * D;
+    const float *part = a.part + (size_t)bh * C * 3 * D * D;
+    auto rows_of = [&](int c) { return (float)(min(a.M, (c + 1) * kPrChunk) - c * kPrChunk); };
     if (threadIdx.x < D) {
         float sx = 0.f, sr = 0.f;
-#pragma unroll 8
-        for (int j = 0; j < a.M; ++j) {
-            const float x = Os[(size_t)probe_row(j, a) * D + threadIdx.x];
-            sx += x;
-            sr += Od[(size_t)j * D + threadIdx.x] - x;
+        for (int c = 0; c < C; ++c) {
+            const float n = rows_of(c);
+            sx += n * cmean[(size_t)c * 2 * D + threadIdx.x];
+            sr += n * cmean[(size_t)c * 2 * D + D + threadIdx.x];
         }
         xm[threadIdx.x] = sx * invM;
         rm[threadIdx.x] = sr * invM;
     }
     __syncthreads();
-    gram<D>(a, bh, xm, rm, 0, 0, Gm, SA, SB);
-    gram<D>(a, bh, xm, rm, 0, 1, Hm, SA, SB);
-    gram<D>(a, bh, xm, rm, 2, 2, Sm, SA, SB);
+    // G = sum_c (G_c + n_c dx_c dx_c^T), H = sum_c (H_c + n_c dx_c dr_c^T), S = sum_c S_c,
+    // with dx_c = xm_c - xm and dr_c = rm_c - rm
+    for (int e = threadIdx.x; e < D * D; e += kPrThreads) {
+        const int i = e / D, j = e - (e / D) * D;
+        float g = 0.f, hh = 0.f, sv = 0.f;
+        for (int c = 0; c < C; ++c) {
+            const float *pc = part + (size_t)c * 3 * D * D;
+            const float *mc = cmean + (size_t)c * 2 * D;
+            const float n = rows_of(c);
+            const float dxi = mc[i] - xm[i], dxj = mc[j] - xm[j], drj = mc[D + j] - rm[j];
+            g += pc[e] + n * dxi * dxj;
+            hh += pc[D * D + e] + n * dxi * drj;
+            sv += pc[2 * D * D + e];
+        }
+        Gm[e] = g;
+        Hm[e] = hh;
+        Sm[e] = sv;
+    }
     __threadfence_block();
     __syncthreads();
 
@@ -169,10 +235,106 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
 #pragma unroll
     for (int w = 0; w < kPrThreads / kWave; ++w) trace += red[w];
     const float lam = a.ridge * trace / (float)D;
+
+    // Only B Pk = B Q Q^T is needed (Q: the k leading eigenvectors of R^T R), and
+    // B Q = (G + lam I)^-1 (H Q): the subspace comes first, then a solve with k
+    // right-hand sides instead of D.
+
+    // leading eigenvectors of S = R^T R by subspace iteration from a fixed start;
+    // S (symmetric) packed into LDS
+    float *Sp = L;
+    const int K = a.rank;
+    const int KP = (K + 3) & ~3;                          // row stride of the basis (zero columns past K)
+#pragma unroll 16
+    for (int e = threadIdx.x; e < D * D; e += kPrThreads) {
+        const int i = e / D, j = e - (e / D) * D;
+        if (j <= i) Sp[tri(i, j)] = Sm[e];
+    }
+    for (int e = threadIdx.x; e < D * KP; e += kPrThreads) {
+        const int i = e / KP, c = e - (e / KP) * KP;
+        const int f = i * K + c;                          // the start's entry (i, c)
+        uint32_t hsh = (uint32_t)f * 2654435761u + 0x9e3779b9u;
+        hsh ^= hsh >> 15;
+        hsh *= 2246822519u;
+        hsh ^= hsh >> 13;
+        Qs[e] = c < K ? (float)(hsh & 0xffff) / 32768.f - 1.f : 0.f;
+    }
+    __syncthreads();
+    for (int it = 0; it <= kPrIters; ++it) {
+        if (it > 0) {
+            // Z = S Q: thread (i, half) forms row i over half of the l range for
+            // every column (each S entry read once), the halves meet by a lane swap
+            constexpr int TPR = kPrThreads / D;          // threads per row: 2 (D = 128) or 4 (D = 64)
+            const int i = threadIdx.x / TPR, part = threadIdx.x % TPR;
+            f32x4 z[kPrMaxRank / 4];
+#pragma unroll
+            for (int g = 0; g < kPrMaxRank / 4; ++g) z[g] = f32x4{};
+            const int l0 = part * (D / TPR), l1 = l0 + D / TPR;
+            const int G4 = KP / 4;
+            for (int l = l0; l < l1; ++l) {
+                const float sv = l <= i ? Sp[tri(i, l)] : Sp[tri(l, i)];
+                const f32x4 *ql = reinterpret_cast<const f32x4 *>(Qs + l * KP);
+#pragma unroll
+                for (int g = 0; g < kPrMaxRank / 4; ++g)
+                    if (g < G4) z[g] += sv * ql[g];
+            }
+#pragma unroll
+            for (int g = 0; g < kPrMaxRank / 4; ++g) {
+                if (g < G4) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        float v = z[g][u];
+                        v += __shfl_xor(v, 1, kWave);
+                        if constexpr (TPR == 4) v += __shfl_xor(v, 2, kWave);
+                        z[g][u] = v;
+                    }
+                }
+            }
+            __syncthreads();
+            if (part == 0)
+#pragma unroll
+                for (int g = 0; g < kPrMaxRank / 4; ++g)
+                    if (g < G4) *reinterpret_cast<f32x4 *>(Qs + i * KP + 4 * g) = z[g];
+            __syncthreads();
+        }
+        // modified Gram-Schmidt on the columns, by one wave
+        if (wave == 0) {
+            for (int c = 0; c < K; ++c) {
+                for (int pcol = 0; pcol < c; ++pcol) {
+                    float dp = 0.f;
+                    for (int i = lane; i < D; i += kWave) dp += Qs[i * KP + pcol] * Qs[i * KP + c];
+                    dp = wave_sum(dp);
+                    for (int i = lane; i < D; i += kWave) Qs[i * KP + c] -= dp * Qs[i * KP + pcol];
+                }
+                float nn = 0.f;
+                for (int i = lane; i < D; i += kWave) nn += Qs[i * KP + c] * Qs[i * KP + c];
+                nn = wave_sum(nn);
+                const float inv = nn > 0.f ? 1.f / sqrtf(nn) : 0.f;
+                for (int i = lane; i < D; i += kWave) Qs[i * KP + c] *= inv;
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
+        __syncthreads();
+    }
+
+    // G + lam I, packed over S (no longer needed)
 #pragma unroll 16
     for (int e = threadIdx.x; e < D * D; e += kPrThreads) {
         const int i = e / D, j = e - (e / D) * D;
         if (j <= i) L[tri(i, j)] = Gm[e] + (i == j ? lam : 0.f);
+    }
+    // right-hand sides T = H Q (columns c < K of the 32-column region, the rest zero)
+    float *T = reg;                                       // T[i * 32 + c]
+    for (int e = threadIdx.x; e < D * 32; e += kPrThreads) {
+        const int i = e / 32, c = e - (e / 32) * 32;
+        float v = 0.f;
+        if (c < K) {
+            const float *hrow = Hm + (size_t)i * D;
+#pragma unroll 8
+            for (int l = 0; l < D; ++l) v = fmaf(hrow[l], Qs[l * KP + c], v);
+        }
+        T[e] = v;
     }
     __syncthreads();
 
@@ -204,166 +366,65 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
             __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_wave_barrier();
         }
-    }
-    __syncthreads();
 
-    // B = (L L^T)^-1 H, 32 columns at a time in LDS, by one wave: lane (hh, c)
-    // takes column c and half of each dot product; the halves meet by a swap
-    // of the wave's halves
-    if (wave == 0) {
-        float *T = reg;                                   // T[i * 32 + c]
+        // W = (L L^T)^-1 T in place, by the same wave: lane (hh, c) takes column
+        // c and half of each dot product; the halves meet by a swap of the
+        // wave's halves
         const int c = lane & 31, hh = lane >> 5;
-        for (int c0 = 0; c0 < D; c0 += 32) {
-#pragma unroll 16
-            for (int i = hh; i < D; i += 2) T[i * 32 + c] = Hm[i * D + c0 + c];
+        for (int i = 0; i < D; ++i) {                     // forward: L y = t
+            const float *Li = L + tri(i, 0);
+            float s = lds_dot(Li, 1, T + c, 32, hh, i, 2);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+            s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            if (hh == 0) T[i * 32 + c] = (T[i * 32 + c] - s) / Li[i];
             __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_wave_barrier();
-            for (int i = 0; i < D; ++i) {                 // forward: L y = h
-                const float *Li = L + tri(i, 0);
-                float s = lds_dot(Li, 1, T + c, 32, hh, i, 2);
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-                s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                if (hh == 0) T[i * 32 + c] = (T[i * 32 + c] - s) / Li[i];
-                __builtin_amdgcn_s_waitcnt(0xc07f);
-                __builtin_amdgcn_wave_barrier();
-            }
-            for (int i = D - 1; i >= 0; --i) {            // backward: L^T b = y
-                float s = 0.f;
-                {
-                    float p[4] = {0.f, 0.f, 0.f, 0.f};
-                    int k = i + 1 + hh;
-                    for (; k + 6 < D; k += 8) {
-                        float lv[4], tv[4];
+        }
+        for (int i = D - 1; i >= 0; --i) {                // backward: L^T w = y
+            float s = 0.f;
+            {
+                float p[4] = {0.f, 0.f, 0.f, 0.f};
+                int k = i + 1 + hh;
+                for (; k + 6 < D; k += 8) {
+                    float lv[4], tv[4];
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            lv[u] = L[tri(k + 2 * u, i)];
-                            tv[u] = T[(k + 2 * u) * 32 + c];
-                        }
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) p[u] = fmaf(lv[u], tv[u], p[u]);
+                    for (int u = 0; u < 4; ++u) {
+                        lv[u] = L[tri(k + 2 * u, i)];
+                        tv[u] = T[(k + 2 * u) * 32 + c];
                     }
-                    for (; k < D; k += 2) p[0] = fmaf(L[tri(k, i)], T[k * 32 + c], p[0]);
-                    s = (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) p[u] = fmaf(lv[u], tv[u], p[u]);
                 }
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-                s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                if (hh == 0) T[i * 32 + c] = (T[i * 32 + c] - s) / L[tri(i, i)];
-                __builtin_amdgcn_s_waitcnt(0xc07f);
-                __builtin_amdgcn_wave_barrier();
+                for (; k < D; k += 2) p[0] = fmaf(L[tri(k, i)], T[k * 32 + c], p[0]);
+                s = (p[0] + p[1]) + (p[2] + p[3]);
             }
-            for (int i = hh; i < D; i += 2) Bm[i * D + c0 + c] = T[i * 32 + c];
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+            s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            if (hh == 0) T[i * 32 + c] = (T[i * 32 + c] - s) / L[tri(i, i)];
             __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_wave_barrier();
         }
     }
-    __threadfence_block();
     __syncthreads();
-    // intercept b = rm - xm B
-    if (threadIdx.x < D) {
-        float s = rm[threadIdx.x];
-#pragma unroll 16
-        for (int i = 0; i < D; ++i) s -= xm[i] * Bm[i * D + threadIdx.x];
-        bv[threadIdx.x] = s;
-    }
 
-    // leading eigenvectors of S = R^T R by subspace iteration from a fixed start;
-    // S (symmetric) packed into LDS over the factor, which is no longer needed
-    __syncthreads();
-    float *Sp = L;
-    float *Qs = reg;                                      // Qs[i * K + c]
-#pragma unroll 16
-    for (int e = threadIdx.x; e < D * D; e += kPrThreads) {
-        const int i = e / D, j = e - (e / D) * D;
-        if (j <= i) Sp[tri(i, j)] = Sm[e];
-    }
-    const int K = a.rank;
-    for (int e = threadIdx.x; e < D * K; e += kPrThreads) {
-        uint32_t hsh = (uint32_t)e * 2654435761u + 0x9e3779b9u;
-        hsh ^= hsh >> 15;
-        hsh *= 2246822519u;
-        hsh ^= hsh >> 13;
-        Qs[e] = (float)(hsh & 0xffff) / 32768.f - 1.f;
-    }
-    __syncthreads();
-    for (int it = 0; it <= kPrIters; ++it) {
-        if (it > 0) {
-            // Z = S Q into registers, then back to Qs
-            float z[(D * kPrMaxRank + kPrThreads - 1) / kPrThreads];
-            int n_own = 0;
-            for (int e = threadIdx.x; e < D * K; e += kPrThreads) {
-                const int i = e / K, c = e - (e / K) * K;
-                float s = lds_dot(Sp + tri(i, 0), 1, Qs + c, K, 0, i, 1);
-                {
-                    float p[4] = {0.f, 0.f, 0.f, 0.f};
-                    int l = i;
-                    for (; l + 3 < D; l += 4) {
-                        float sv[4], qv[4];
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            sv[u] = Sp[tri(l + u, i)];
-                            qv[u] = Qs[(l + u) * K + c];
-                        }
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) p[u] = fmaf(sv[u], qv[u], p[u]);
-                    }
-                    for (; l < D; ++l) p[0] = fmaf(Sp[tri(l, i)], Qs[l * K + c], p[0]);
-                    s += (p[0] + p[1]) + (p[2] + p[3]);
-                }
-                z[n_own++] = s;
-            }
-            __syncthreads();
-            n_own = 0;
-            for (int e = threadIdx.x; e < D * K; e += kPrThreads) Qs[e] = z[n_own++];
-            __syncthreads();
-        }
-        // modified Gram-Schmidt on the columns, by one wave
-        if (wave == 0) {
-            for (int c = 0; c < K; ++c) {
-                for (int pcol = 0; pcol < c; ++pcol) {
-                    float dp = 0.f;
-                    for (int i = lane; i < D; i += kWave) dp += Qs[i * K + pcol] * Qs[i * K + c];
-                    dp = wave_sum(dp);
-                    for (int i = lane; i < D; i += kWave) Qs[i * K + c] -= dp * Qs[i * K + pcol];
-                }
-                float nn = 0.f;
-                for (int i = lane; i < D; i += kWave) nn += Qs[i * K + c] * Qs[i * K + c];
-                nn = wave_sum(nn);
-                const float inv = nn > 0.f ? 1.f / sqrtf(nn) : 0.f;
-                for (int i = lane; i < D; i += kWave) Qs[i * K + c] *= inv;
-                __builtin_amdgcn_s_waitcnt(0xc07f);
-                __builtin_amdgcn_wave_barrier();
-            }
-        }
-        __syncthreads();
-    }
-
-    // W = B Q (D x K) over the packed S (no longer needed), then
-    // C_B = W Q^T, C_b = (b Q) Q^T
-    float *W = L;
-    for (int e = threadIdx.x; e < D * K; e += kPrThreads) {
-        const int i = e / K, c = e - (e / K) * K;
-        float s = 0.f;
-#pragma unroll 16
-        for (int l = 0; l < D; ++l) s += Bm[i * D + l] * Qs[l * K + c];
-        W[e] = s;
-    }
+    // W = B Q sits in T; b Q = rm Q - xm W; then C_B = W Q^T, C_b = (b Q) Q^T
     if (threadIdx.x < K) {
+        const int c = threadIdx.x;
         float s = 0.f;
 #pragma unroll 16
-        for (int l = 0; l < D; ++l) s += bv[l] * Qs[l * K + threadIdx.x];
-        wb[threadIdx.x] = s;
+        for (int l = 0; l < D; ++l) s += rm[l] * Qs[l * KP + c] - xm[l] * T[l * 32 + c];
+        wb[c] = s;
     }
-    __threadfence_block();
     __syncthreads();
     for (int e = threadIdx.x; e < D * D; e += kPrThreads) {
         const int i = e / D, j = e - (e / D) * D;
         float s = 0.f;
-        for (int c = 0; c < K; ++c) s += W[i * K + c] * Qs[j * K + c];
+        for (int c = 0; c < K; ++c) s += T[i * 32 + c] * Qs[j * KP + c];
         Bm[e] = s;
     }
     if (threadIdx.x < D) {
         float s = 0.f;
-        for (int c = 0; c < K; ++c) s += wb[c] * Qs[threadIdx.x * K + c];
+        for (int c = 0; c < K; ++c) s += wb[c] * Qs[threadIdx.x * KP + c];
         bv[threadIdx.x] = s;
     }
 }
@@ -447,6 +508,9 @@ static hipError_t launch_pr_d(int dtype, const void *q, void *qp, void *o, const
         else
             hipLaunchKernelGGL(probe_gather_kernel<float>, grid, dim3(kPrThreads), 0, st, (const float *)q, (float *)qp, a, D);
     } else if (step == 1) {
+        hipLaunchKernelGGL(pr_gram_kernel<D>, dim3(a.n_chunks, BH), dim3(kPrThreads), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
         hipLaunchKernelGGL(pr_fit_kernel<D>, dim3(BH), dim3(kPrThreads), 0, st, a);
     } else {
         dim3 grid((a.N + 63) / 64, BH);
