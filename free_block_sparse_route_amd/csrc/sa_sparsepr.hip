@@ -206,21 +206,35 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
     __syncthreads();
     // G = sum_c (G_c + n_c dx_c dx_c^T), H = sum_c (H_c + n_c dx_c dr_c^T), S = sum_c S_c,
     // with dx_c = xm_c - xm and dr_c = rm_c - rm
-    for (int e = threadIdx.x; e < D * D; e += kPrThreads) {
-        const int i = e / D, j = e - (e / D) * D;
-        float g = 0.f, hh = 0.f, sv = 0.f;
+    // (four entries e, e + 256, ... per thread, so that their loads overlap)
+    constexpr int EU = 4;
+    static_assert(D * D % (EU * kPrThreads) == 0, "entries split evenly");
+    for (int e0 = threadIdx.x; e0 < D * D; e0 += EU * kPrThreads) {
+        float g[EU], hh[EU], sv[EU];
+#pragma unroll
+        for (int u = 0; u < EU; ++u) g[u] = hh[u] = sv[u] = 0.f;
+        const int j = e0 % D;                             // the same column for the four entries
         for (int c = 0; c < C; ++c) {
             const float *pc = part + (size_t)c * 3 * D * D;
             const float *mc = cmean + (size_t)c * 2 * D;
             const float n = rows_of(c);
-            const float dxi = mc[i] - xm[i], dxj = mc[j] - xm[j], drj = mc[D + j] - rm[j];
-            g += pc[e] + n * dxi * dxj;
-            hh += pc[D * D + e] + n * dxi * drj;
-            sv += pc[2 * D * D + e];
+            const float dxj = mc[j] - xm[j], drj = mc[D + j] - rm[j];
+#pragma unroll
+            for (int u = 0; u < EU; ++u) {
+                const int e = e0 + u * kPrThreads, i = e / D;
+                const float dxi = mc[i] - xm[i];
+                g[u] += pc[e] + n * dxi * dxj;
+                hh[u] += pc[D * D + e] + n * dxi * drj;
+                sv[u] += pc[2 * D * D + e];
+            }
         }
-        Gm[e] = g;
-        Hm[e] = hh;
-        Sm[e] = sv;
+#pragma unroll
+        for (int u = 0; u < EU; ++u) {
+            const int e = e0 + u * kPrThreads;
+            Gm[e] = g[u];
+            Hm[e] = hh[u];
+            Sm[e] = sv[u];
+        }
     }
     __threadfence_block();
     __syncthreads();
@@ -271,6 +285,7 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
             for (int g = 0; g < kPrMaxRank / 4; ++g) z[g] = f32x4{};
             const int l0 = part * (D / TPR), l1 = l0 + D / TPR;
             const int G4 = KP / 4;
+#pragma unroll 8
             for (int l = l0; l < l1; ++l) {
                 const float sv = l <= i ? Sp[tri(i, l)] : Sp[tri(l, i)];
                 const f32x4 *ql = reinterpret_cast<const f32x4 *>(Qs + l * KP);
@@ -297,23 +312,40 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
                     if (g < G4) *reinterpret_cast<f32x4 *>(Qs + i * KP + 4 * g) = z[g];
             __syncthreads();
         }
-        // modified Gram-Schmidt on the columns, by one wave
+        // modified Gram-Schmidt on the columns, by one wave, in registers: lane
+        // l holds rows l, l + 64, ..
         if (wave == 0) {
-            for (int c = 0; c < K; ++c) {
+            constexpr int RL = D / kWave;                 // rows per lane
+            float qv[RL][kPrMaxRank];
+#pragma unroll
+            for (int r = 0; r < RL; ++r)
+#pragma unroll
+                for (int c = 0; c < kPrMaxRank; ++c) qv[r][c] = c < K ? Qs[(lane + r * kWave) * KP + c] : 0.f;
+#pragma unroll
+            for (int c = 0; c < kPrMaxRank; ++c) {
+                if (c >= K) break;
+#pragma unroll
                 for (int pcol = 0; pcol < c; ++pcol) {
                     float dp = 0.f;
-                    for (int i = lane; i < D; i += kWave) dp += Qs[i * KP + pcol] * Qs[i * KP + c];
+#pragma unroll
+                    for (int r = 0; r < RL; ++r) dp = fmaf(qv[r][pcol], qv[r][c], dp);
                     dp = wave_sum(dp);
-                    for (int i = lane; i < D; i += kWave) Qs[i * KP + c] -= dp * Qs[i * KP + pcol];
+#pragma unroll
+                    for (int r = 0; r < RL; ++r) qv[r][c] = fmaf(-dp, qv[r][pcol], qv[r][c]);
                 }
                 float nn = 0.f;
-                for (int i = lane; i < D; i += kWave) nn += Qs[i * KP + c] * Qs[i * KP + c];
+#pragma unroll
+                for (int r = 0; r < RL; ++r) nn = fmaf(qv[r][c], qv[r][c], nn);
                 nn = wave_sum(nn);
                 const float inv = nn > 0.f ? 1.f / sqrtf(nn) : 0.f;
-                for (int i = lane; i < D; i += kWave) Qs[i * KP + c] *= inv;
-                __builtin_amdgcn_s_waitcnt(0xc07f);
-                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int r = 0; r < RL; ++r) qv[r][c] *= inv;
             }
+#pragma unroll
+            for (int r = 0; r < RL; ++r)
+#pragma unroll
+                for (int c = 0; c < kPrMaxRank; ++c)
+                    if (c < K) Qs[(lane + r * kWave) * KP + c] = qv[r][c];
         }
         __syncthreads();
     }
@@ -338,69 +370,71 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
     }
     __syncthreads();
 
-    // Cholesky G + lam I = L L^T, by one wave (LDS operations of a wave are in order)
-    if (wave == 0) {
-        for (int j = 0; j < D; ++j) {
-            const float djj = sqrtf(fmaxf(L[tri(j, j)], 1e-30f));
-            for (int i = j + 1 + lane; i < D; i += kWave) L[tri(i, j)] /= djj;
-            if (lane == 0) L[tri(j, j)] = djj;
-            __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): this wave's LDS writes are done
-            __builtin_amdgcn_wave_barrier();
-            // trailing update of the lower triangle below row j, a row per lane
-            for (int i = j + 1 + lane; i < D; i += kWave) {
-                const float lij = L[tri(i, j)];
-                float *Li = L + tri(i, 0);
-                int k = j + 1;
-                for (; k + 7 <= i; k += 8) {             // eight reads ahead of the writes
-                    float li[8], lk[8];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        li[u] = Li[k + u];
-                        lk[u] = L[tri(k + u, j)];
-                    }
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) Li[k + u] = li[u] - lij * lk[u];
-                }
-                for (; k <= i; ++k) Li[k] -= lij * L[tri(k, j)];
-            }
-            __builtin_amdgcn_s_waitcnt(0xc07f);
-            __builtin_amdgcn_wave_barrier();
+    // Cholesky G + lam I = L L^T, left-looking, in place (row i of the packed
+    // triangle holds L[i][0..j-1] and the matrix entries from j on): column j
+    // needs its diagonal, a dot product of row j with itself (wave 0), then for
+    // every row below it a dot product with row j (two threads per row, a half
+    // of the terms each).
+    for (int j = 0; j < D; ++j) {
+        const float *Lj = L + tri(j, 0);
+        if (wave == 0) {
+            float dsum = 0.f;
+            for (int k = lane; k < j; k += kWave) dsum = fmaf(Lj[k], Lj[k], dsum);
+            dsum = wave_sum(dsum);
+            if (lane == 0) L[tri(j, j)] = sqrtf(fmaxf(L[tri(j, j)] - dsum, 1e-30f));
         }
+        __syncthreads();
+        const float djj = L[tri(j, j)];
+        for (int t = threadIdx.x; t < 2 * (D - 1 - j); t += kPrThreads) {
+            const int i = j + 1 + (t >> 1), half = t & 1;
+            const float *Li = L + tri(i, 0);
+            float p[4] = {0.f, 0.f, 0.f, 0.f};
+            int k = half;
+            for (; k + 6 < j; k += 8) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) p[u] = fmaf(Li[k + 2 * u], Lj[k + 2 * u], p[u]);
+            }
+            for (; k < j; k += 2) p[0] = fmaf(Li[k], Lj[k], p[0]);
+            float sdot = (p[0] + p[1]) + (p[2] + p[3]);
+            sdot += __shfl_xor(sdot, 1, kWave);
+            if (half == 0) L[tri(i, j)] = (L[tri(i, j)] - sdot) / djj;
+        }
+        __syncthreads();
+    }
 
-        // W = (L L^T)^-1 T in place, by the same wave: lane (hh, c) takes column
-        // c and half of each dot product; the halves meet by a swap of the
-        // wave's halves
-        const int c = lane & 31, hh = lane >> 5;
+    // W = (L L^T)^-1 T in place, by one wave: lane (part, c) takes column c
+    // (< 16 >= K) and the terms k = part mod 4 of each dot product; the four
+    // parts meet by lane swaps
+    if (wave == 0) {
+        const int c = lane & 15, part = lane >> 4;
+        auto meet = [&](float v) {
+            v += __shfl_xor(v, 16, kWave);
+            v += __shfl_xor(v, 32, kWave);
+            return v;
+        };
         for (int i = 0; i < D; ++i) {                     // forward: L y = t
             const float *Li = L + tri(i, 0);
-            float s = lds_dot(Li, 1, T + c, 32, hh, i, 2);
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-            s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-            if (hh == 0) T[i * 32 + c] = (T[i * 32 + c] - s) / Li[i];
-            __builtin_amdgcn_s_waitcnt(0xc07f);
+            const float s = meet(lds_dot(Li, 1, T + c, 32, part, i, 4));
+            if (part == 0) T[i * 32 + c] = (T[i * 32 + c] - s) / Li[i];
+            __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): this wave's LDS writes are done
             __builtin_amdgcn_wave_barrier();
         }
         for (int i = D - 1; i >= 0; --i) {                // backward: L^T w = y
-            float s = 0.f;
-            {
-                float p[4] = {0.f, 0.f, 0.f, 0.f};
-                int k = i + 1 + hh;
-                for (; k + 6 < D; k += 8) {
-                    float lv[4], tv[4];
+            float p[4] = {0.f, 0.f, 0.f, 0.f};
+            int k = i + 1 + part;
+            for (; k + 12 < D; k += 16) {
+                float lv[4], tv[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        lv[u] = L[tri(k + 2 * u, i)];
-                        tv[u] = T[(k + 2 * u) * 32 + c];
-                    }
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) p[u] = fmaf(lv[u], tv[u], p[u]);
+                for (int u = 0; u < 4; ++u) {
+                    lv[u] = L[tri(k + 4 * u, i)];
+                    tv[u] = T[(k + 4 * u) * 32 + c];
                 }
-                for (; k < D; k += 2) p[0] = fmaf(L[tri(k, i)], T[k * 32 + c], p[0]);
-                s = (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) p[u] = fmaf(lv[u], tv[u], p[u]);
             }
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-            s = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-            if (hh == 0) T[i * 32 + c] = (T[i * 32 + c] - s) / L[tri(i, i)];
+            for (; k < D; k += 4) p[0] = fmaf(L[tri(k, i)], T[k * 32 + c], p[0]);
+            const float s = meet((p[0] + p[1]) + (p[2] + p[3]));
+            if (part == 0) T[i * 32 + c] = (T[i * 32 + c] - s) / L[tri(i, i)];
             __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_wave_barrier();
         }
