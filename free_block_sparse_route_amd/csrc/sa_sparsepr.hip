@@ -72,54 +72,20 @@ __device__ __forceinline__ float lds_dot(const float *x, int sx, const float *y,
     return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 }
 
-// sum over the probes jb .. je - 1 of A[j][r] * B[j][c] for the D x D entries
-// a thread owns (row r, columns c0 .. c0 + D/2 - 1); A, B in {0: x - xm,
-// 1: r - rm, 2: r}.  Probe rows are staged in LDS 16 at a time.
-template <int D>
-__device__ void gram(const PrArgs &a, int bh, int jb, int je, const float *xm, const float *rm, int ka, int kb,
-                     float *out, float *SA, float *SB) {
-    constexpr int H = D / 2, JS = 16;
-    const int r = threadIdx.x / 2, c0 = (threadIdx.x & 1) * H;
-    const bool active = threadIdx.x < 2 * D;
-    float acc[H];
-#pragma unroll
-    for (int c = 0; c < H; ++c) acc[c] = 0.f;
-    const float *Os = a.O32 + (size_t)bh * a.N * D;
-    const float *Od = a.Od32 + (size_t)bh * a.M * D;
-    auto val = [&](int k, int j, int f) -> float {
-        const float x = Os[(size_t)probe_row(j, a) * D + f];
-        if (k == 0) return x - xm[f];
-        const float rr = Od[(size_t)j * D + f] - x;
-        return k == 1 ? rr - rm[f] : rr;
-    };
-    for (int j0 = jb; j0 < je; j0 += JS) {
-        __syncthreads();
-#pragma unroll
-        for (int e = threadIdx.x; e < JS * D; e += kPrThreads) {
-            const int j = j0 + e / D, f = e % D;
-            SA[e] = j < je ? val(ka, j, f) : 0.f;
-            SB[e] = j < je ? val(kb, j, f) : 0.f;
-        }
-        __syncthreads();
-        if (active)
-            for (int jj = 0; jj < JS; ++jj) {
-                const float ar = SA[jj * D + r];
-#pragma unroll
-                for (int c = 0; c < H; ++c) acc[c] = fmaf(ar, SB[jj * D + c0 + c], acc[c]);
-            }
-    }
-    if (active)
-#pragma unroll
-        for (int c = 0; c < H; ++c) out[r * D + c0 + c] = acc[c];
-}
-
-// One chunk of kPrChunk probes of one (b, h): its means of x and r, its
-// centred x^T x and x^T r, and its uncentred r^T r.
+// One chunk of kPrChunk probes of one (b, h): its means of x and r and, with
+// xc = x - xm and rc = r - rm (chunk means), G = sum xc xc^T, H = sum xc rc^T
+// and S = sum r r^T = sum rc rc^T + n rm rm^T.  The centred rows are staged in
+// LDS 32 probes at a time; thread (bi, bj) accumulates the BE x BE blocks
+// (bi, bj) of the three matrices in registers.
 template <int D>
 __global__ __launch_bounds__(kPrThreads) void pr_gram_kernel(PrArgs a) {
+    constexpr int BE = D / 16;                            // block edge: 16 x 16 blocks
+    constexpr int JS = 32;                                // probes per staging step
+    static_assert(BE % 4 == 0, "blocks of whole float4s");
     const int c = blockIdx.x, bh = blockIdx.y;
     const int jb = c * kPrChunk, je = min(a.M, jb + kPrChunk);
-    __shared__ float SA[16 * D], SB[16 * D];
+    __shared__ __attribute__((aligned(16))) float XC[JS * D];
+    __shared__ __attribute__((aligned(16))) float RC[JS * D];
     __shared__ float ps[kPrThreads / D][2][D];
     __shared__ float xm[D], rm[D];
     const float *Os = a.O32 + (size_t)bh * a.N * D;
@@ -138,6 +104,7 @@ __global__ __launch_bounds__(kPrThreads) void pr_gram_kernel(PrArgs a) {
         ps[part][1][f] = sr;
     }
     __syncthreads();
+    const float n_rows = (float)(je - jb);
     if (threadIdx.x < D) {
         float sx = 0.f, sr = 0.f;
 #pragma unroll
@@ -145,18 +112,71 @@ __global__ __launch_bounds__(kPrThreads) void pr_gram_kernel(PrArgs a) {
             sx += ps[q][0][threadIdx.x];
             sr += ps[q][1][threadIdx.x];
         }
-        const float inv = 1.f / (float)(je - jb);
-        xm[threadIdx.x] = sx * inv;
-        rm[threadIdx.x] = sr * inv;
+        xm[threadIdx.x] = sx / n_rows;
+        rm[threadIdx.x] = sr / n_rows;
         float *cm = a.cmean + ((size_t)bh * a.n_chunks + c) * 2 * D;
-        cm[threadIdx.x] = sx * inv;
-        cm[D + threadIdx.x] = sr * inv;
+        cm[threadIdx.x] = sx / n_rows;
+        cm[D + threadIdx.x] = sr / n_rows;
     }
-    __syncthreads();
+    const int bi = threadIdx.x / 16, bj = threadIdx.x % 16;
+    float g[BE][BE], hm[BE][BE], sm[BE][BE];
+#pragma unroll
+    for (int u = 0; u < BE; ++u)
+#pragma unroll
+        for (int v = 0; v < BE; ++v) g[u][v] = hm[u][v] = sm[u][v] = 0.f;
+    for (int j0 = jb; j0 < je; j0 += JS) {
+        __syncthreads();                                  // the means are in; the last step's rows are read
+        for (int e = threadIdx.x; e < JS * D; e += kPrThreads) {
+            const int j = j0 + e / D, f = e % D;
+            float xc = 0.f, rc = 0.f;
+            if (j < je) {
+                const float x = Os[(size_t)probe_row(j, a) * D + f];
+                xc = x - xm[f];
+                rc = (Od[(size_t)j * D + f] - x) - rm[f];
+            }
+            XC[e] = xc;
+            RC[e] = rc;
+        }
+        __syncthreads();
+        const int jn = min(JS, je - j0);
+        for (int jj = 0; jj < jn; ++jj) {
+            float xa[BE], ra[BE], xb[BE], rb[BE];
+#pragma unroll
+            for (int q = 0; q < BE; q += 4) {
+                const f32x4 x4a = *reinterpret_cast<const f32x4 *>(XC + jj * D + bi * BE + q);
+                const f32x4 r4a = *reinterpret_cast<const f32x4 *>(RC + jj * D + bi * BE + q);
+                const f32x4 x4b = *reinterpret_cast<const f32x4 *>(XC + jj * D + bj * BE + q);
+                const f32x4 r4b = *reinterpret_cast<const f32x4 *>(RC + jj * D + bj * BE + q);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    xa[q + w] = x4a[w];
+                    ra[q + w] = r4a[w];
+                    xb[q + w] = x4b[w];
+                    rb[q + w] = r4b[w];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < BE; ++u)
+#pragma unroll
+                for (int v = 0; v < BE; ++v) {
+                    g[u][v] = fmaf(xa[u], xb[v], g[u][v]);
+                    hm[u][v] = fmaf(xa[u], rb[v], hm[u][v]);
+                    sm[u][v] = fmaf(ra[u], rb[v], sm[u][v]);
+                }
+        }
+    }
     float *out = a.part + ((size_t)bh * a.n_chunks + c) * 3 * D * D;
-    gram<D>(a, bh, jb, je, xm, rm, 0, 0, out, SA, SB);
-    gram<D>(a, bh, jb, je, xm, rm, 0, 1, out + D * D, SA, SB);
-    gram<D>(a, bh, jb, je, xm, rm, 2, 2, out + 2 * D * D, SA, SB);
+#pragma unroll
+    for (int u = 0; u < BE; ++u) {
+        const int i = bi * BE + u;
+#pragma unroll
+        for (int v = 0; v < BE; ++v) {
+            const int j = bj * BE + v;
+            out[i * D + j] = g[u][v];
+            out[D * D + i * D + j] = hm[u][v];
+            out[2 * D * D + i * D + j] = sm[u][v] + n_rows * rm[i] * rm[j];
+        }
+    }
 }
 
 // LDS of the fit, one pool: packed R^T R (subspace phase), then the packed
