@@ -286,8 +286,8 @@ sa_status sparse_attn_permute_tokens(int32_t B, int32_t H, int32_t N, int32_t d,
 // Probe-fitted residual: workspace pieces, each 256-byte aligned.
 namespace {
 struct PrLayout {
-    size_t qp, od32, o32, scratch, part, cmean, cb_mat, cb_vec, total;
-    int M, n_chunks;
+    size_t qp, od32, o32, scratch, part, cmean, cb_mat, cb_vec, osplit, lsplit, total;
+    int M, n_chunks, kv_splits;
 };
 PrLayout pr_layout(const sa_params *p, int per_block) {
     const Dims d = dims_of(p);
@@ -306,6 +306,21 @@ PrLayout pr_layout(const sa_params *p, int per_block) {
     L.cmean = off; off += up(BH * L.n_chunks * 2 * D * 4);
     L.cb_mat = off; off += up(BH * D * D * 4);
     L.cb_vec = off; off += up(BH * D * 4);
+    // The probe pass has few query blocks (P per block_q query rows): its key
+    // tiles are split into ranges so that about 2048 workgroups run, each range
+    // at least 8 tiles, at most 32 ranges; the ranges' outputs are merged.
+    {
+        const int64_t items = (int64_t)BH * ((L.M + p->block_q - 1) / p->block_q);
+        const int64_t tiles = (p->N + (p->dtype == SA_BF16 ? 64 : 32) - 1) / (p->dtype == SA_BF16 ? 64 : 32);
+        int64_t S = (2048 + items - 1) / items;
+        S = S < 32 ? S : 32;
+        S = S < tiles / 8 ? S : tiles / 8;
+        L.kv_splits = S > 1 ? (int)S : 1;
+    }
+    L.osplit = off;
+    if (L.kv_splits > 1) off += up((size_t)L.kv_splits * BH * L.M * D * 4);
+    L.lsplit = off;
+    if (L.kv_splits > 1) off += up((size_t)L.kv_splits * BH * L.M * 4);
     L.total = off;
     return L;
 }
@@ -362,6 +377,9 @@ sa_status sparse_attn_forward_sparsepr(const sa_params *p, const void *q, const 
     a.part = (float *)(ws + L.part);
     a.cmean = (float *)(ws + L.cmean);
     a.CB = (float *)(ws + L.cb_mat);
+    a.kv_splits = L.kv_splits;
+    a.Osplit = (const float *)(ws + L.osplit);
+    a.Lsplit = (const float *)(ws + L.lsplit);
     a.Cb = (float *)(ws + L.cb_vec);
     // 1. sparse output over the kept tokens only, fp32
     if ((s = run_flash(p, q, k, v, r, nullptr, nullptr, stream, "sparsepr: sparse pass", (float *)(ws + L.o32),
@@ -376,9 +394,21 @@ sa_status sparse_attn_forward_sparsepr(const sa_params *p, const void *q, const 
     fa.n_qb = (L.M + p->block_q - 1) / p->block_q; fa.n_kb = d.n_kb; fa.mask_words = d.words;
     const double scale = p->scale > 0.f ? (double)p->scale : 1.0 / sqrt((double)p->d);
     fa.scale_log2 = (float)(scale * 1.4426950408889634);
-    fa.o32 = (float *)(ws + L.od32);
+    if (L.kv_splits > 1) {
+        fa.kv_splits = L.kv_splits;
+        fa.o32 = (float *)(ws + L.osplit);
+        fa.lse = (float *)(ws + L.lsplit);
+        fa.split_o = d.BH * (size_t)L.M * p->d;
+        fa.split_l = d.BH * (size_t)L.M;
+    } else {
+        fa.o32 = (float *)(ws + L.od32);
+    }
     e = sa::launch_flash(p->dtype, p->d, p->block_q, ws + L.qp, k, v, nullptr, fa, (int)d.BH, st);
     if (e != hipSuccess) return hip_fail(e, "sparsepr: probe pass launch");
+    if (L.kv_splits > 1) {
+        e = sa::launch_sparsepr_step(3, p->dtype, p->d, nullptr, nullptr, nullptr, a, (int)d.BH, st);
+        if (e != hipSuccess) return hip_fail(e, "sparsepr: probe merge launch");
+    }
     // 3. fit, 4. apply
     e = sa::launch_sparsepr_step(1, p->dtype, p->d, nullptr, nullptr, nullptr, a, (int)d.BH, st);
     if (e != hipSuccess) return hip_fail(e, "sparsepr: fit launch");

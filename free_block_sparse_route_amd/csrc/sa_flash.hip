@@ -705,6 +705,9 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
                                          uint32_t *fw) {
     using C = FC<D, BQ>;
     constexpr bool kF32 = sizeof(T) == 4;
+    // dense path with split key ranges: item = query block * kv_splits + split
+    const int kv_part = kSparse ? 0 : item % a.kv_splits;
+    if constexpr (!kSparse) item /= a.kv_splits;
     const int bh = item / a.n_qb;
     const int I = item - bh * a.n_qb;
     const int lane = lane_id();
@@ -755,8 +758,12 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
         ts.words = a.mask_words;
         ts.n_rt = (a.residual && cnt < a.n_kb) ? a.mask_words : 0;   // all kept: no residual
     } else {
-        ts.t = 0; ts.li = 0; ts.sub = 0; ts.rt = 0;
-        ts.dense_tiles = (a.N + ts.exact_rows - 1) / ts.exact_rows;
+        ts.li = 0; ts.sub = 0; ts.rt = 0;
+        {
+            const int tiles = (a.N + ts.exact_rows - 1) / ts.exact_rows;
+            ts.t = (int)((int64_t)kv_part * tiles / a.kv_splits);         // this range's key tiles
+            ts.dense_tiles = (int)((int64_t)(kv_part + 1) * tiles / a.kv_splits);
+        }
         if constexpr (kSparse) {
             ts.list = (const kconst<int32_t> *)(a.kv_idx + row_id * a.kv_idx_cap);
             ts.cnt = __builtin_amdgcn_readfirstlane(a.kv_count[row_id]);
@@ -886,7 +893,7 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (row_ok) {
         if (a.o32) {                     // fp32 output (an intermediate of a later step)
-            float *orow = a.o32 + qhead + (size_t)qrow * D;
+            float *orow = a.o32 + kv_part * a.split_o + qhead + (size_t)qrow * D;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -905,7 +912,7 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
                                   sm.acc[db][4 * g + 3] * inv);
         }
         if (a.lse && h == 0)
-            a.lse[(size_t)bh * a.Nq + qrow] = lt > 0.f ? (sm.m_ref + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+            a.lse[kv_part * a.split_l + (size_t)bh * a.Nq + qrow] = lt > 0.f ? (sm.m_ref + log2f(lt)) * 0.69314718055994531f : -INFINITY;
     }
 }
 
@@ -957,7 +964,8 @@ static hipError_t launch_flash_t(const void *q, const void *k, const void *v, vo
     using C = FC<D, BQ>;
     auto kern = flash_kernel<T, D, BQ, kSparse, kFused>;
     FlashArgs args = a;
-    args.n_items = BH * a.n_qb;
+    if (args.kv_splits < 1 || kSparse) args.kv_splits = 1;
+    args.n_items = BH * a.n_qb * args.kv_splits;
     hipLaunchKernelGGL(kern, dim3(args.n_items), dim3(C::THREADS), 0, st, (const T *)q, (const T *)k,
                        (const T *)v, (T *)o, args);
     return hipGetLastError();

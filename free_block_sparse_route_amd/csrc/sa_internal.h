@@ -34,6 +34,11 @@ struct FlashArgs {
     int N, block_q, block_k, n_qb, n_kb, mask_words, kv_idx_cap;
     int Nq;                              // query rows per (b, h): N, or the probe count of a probe pass
     float *o32;                          // when set, O is written here in fp32 (o unused)
+    // dense path only: the key tiles split into kv_splits ranges (>= 1), work
+    // item (query block, split s) writing its O and lse at o32 + s * split_o,
+    // lse + s * split_l, for a later merge
+    int kv_splits;
+    size_t split_o, split_l;
     float scale_log2;                    // logit scale times log2(e)
     int residual;                        // fold dropped blocks (route present)
     const int32_t *kv_count, *kv_idx, *work_order;
@@ -86,10 +91,14 @@ struct PrArgs {
     int n_chunks;                        // probe chunks of kPrChunk rows per (b, h)
     float *part;                         // [BH, n_chunks, 3, D, D] Gram matrices of each chunk
     float *cmean;                        // [BH, n_chunks, 2, D] chunk means of x and r
+    int kv_splits;                       // key ranges of the probe pass (1: written to Od32 directly)
+    const float *Osplit;                 // [kv_splits, BH, M, D] probe outputs of each key range
+    const float *Lsplit;                 // [kv_splits, BH, M] their log-sum-exp
     float *CB;                           // [BH, D, D] B, then B Pk
     float *Cb;                           // [BH, D] b, then b Pk
 };
-// step 0: gather the probe queries of q into qp; 1: fit; 2: apply to o
+// step 0: gather the probe queries of q into qp; 1: fit; 2: apply to o;
+// 3: merge the probe pass's key ranges into Od32
 hipError_t launch_sparsepr_step(int step, int dtype, int D, const void *q, void *qp, void *o, const PrArgs &a,
                                 int BH, hipStream_t st);
 

@@ -551,6 +551,37 @@ __global__ __launch_bounds__(kPrThreads) void pr_apply_kernel(T *__restrict__ o,
     }
 }
 
+// ------------------------------------------------------------------ merge
+// The probe pass's key ranges s give normalised rows O_s with log-sum-exp l_s;
+// the row over all keys is sum_s exp(l_s - l) O_s with l = log sum_s exp(l_s).
+// One row per wave, D / 64 features per lane.
+template <int D>
+__global__ __launch_bounds__(kPrThreads) void pr_merge_kernel(PrArgs a, int rows) {
+    constexpr int RPB = kPrThreads / kWave;               // rows per workgroup (a wave each)
+    constexpr int FPL = D / kWave;                        // features per lane
+    const int row = blockIdx.x * RPB + threadIdx.x / kWave;
+    if (row >= rows) return;
+    const int lane = lane_id();
+    const int S = a.kv_splits;
+    float lmax = -INFINITY;
+    for (int sp = 0; sp < S; ++sp) lmax = fmaxf(lmax, a.Lsplit[(size_t)sp * rows + row]);
+    float wsum = 0.f, acc[FPL];
+#pragma unroll
+    for (int f = 0; f < FPL; ++f) acc[f] = 0.f;
+    for (int sp = 0; sp < S; ++sp) {
+        const float l = a.Lsplit[(size_t)sp * rows + row];
+        const float w = l == -INFINITY ? 0.f : expf(l - lmax);
+        wsum += w;
+        const float *src = a.Osplit + ((size_t)sp * rows + row) * D;
+#pragma unroll
+        for (int f = 0; f < FPL; ++f) acc[f] = fmaf(w, src[lane + f * kWave], acc[f]);
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    float *dst = const_cast<float *>(a.Od32) + (size_t)row * D;
+#pragma unroll
+    for (int f = 0; f < FPL; ++f) dst[lane + f * kWave] = acc[f] * inv;
+}
+
 // ------------------------------------------------------------------ launch
 template <int D>
 static hipError_t launch_pr_d(int dtype, const void *q, void *qp, void *o, const PrArgs &a, int BH, int step,
@@ -566,6 +597,10 @@ static hipError_t launch_pr_d(int dtype, const void *q, void *qp, void *o, const
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(pr_fit_kernel<D>, dim3(BH), dim3(kPrThreads), 0, st, a);
+    } else if (step == 3) {
+        const int rows = BH * a.M;
+        constexpr int RPB = kPrThreads / kWave;
+        hipLaunchKernelGGL(pr_merge_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(kPrThreads), 0, st, a, rows);
     } else {
         dim3 grid((a.N + 63) / 64, BH);
         if (dtype == SA_BF16)

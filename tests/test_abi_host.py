@@ -105,9 +105,11 @@ def test_sparsepr_workspace_size_and_capacity():
     # N = 1000, d = 128, bf16, B*H = 2, block_q = 128: M = 8 * 2 = 16 probes
     up = lambda x: (x + 255) // 256 * 256
     # gathered queries, dense probe outputs, sparse outputs, Gram matrices, one
-    # chunk of Gram matrices and means (16 probes <= 128 per chunk), B, b
+    # chunk of Gram matrices and means (16 probes <= 128 per chunk), B, b, and
+    # the probe pass in 2 key ranges (2 query blocks; 16 key tiles, >= 8 a range)
     want = (up(2 * 16 * 128 * 2) + up(2 * 16 * 128 * 4) + up(2 * 1000 * 128 * 4) + up(2 * 3 * 128 * 128 * 4)
-            + up(2 * 1 * 3 * 128 * 128 * 4) + up(2 * 1 * 2 * 128 * 4) + up(2 * 128 * 128 * 4) + up(2 * 128 * 4))
+            + up(2 * 1 * 3 * 128 * 128 * 4) + up(2 * 1 * 2 * 128 * 4) + up(2 * 128 * 128 * 4) + up(2 * 128 * 4)
+            + up(2 * 2 * 16 * 128 * 4) + up(2 * 2 * 16 * 4))
     assert n.value == want
     r = B.SaRoute(*([0x1000] * len(B.BUFFERS)), 1 << 10)
     st = B.lib.sparse_attn_forward_sparsepr(ctypes.byref(p), 0x1000, 0x1000, 0x1000, ctypes.byref(r), 2, 4, 1e-3,
