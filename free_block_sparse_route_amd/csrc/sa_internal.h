@@ -94,7 +94,7 @@ struct PrArgs {
     int kv_splits;                       // key ranges of the probe pass (1: written to Od32 directly)
     const float *Osplit;                 // [kv_splits, BH, M, D] probe outputs of each key range
     const float *Lsplit;                 // [kv_splits, BH, M] their log-sum-exp
-    float *CB;                           // [BH, D, D] B, then B Pk
+    float *CB;                           // [BH, D, D] room: W = B Q [D][KP], then Q [D][KP]
     float *Cb;                           // [BH, D] b, then b Pk
 };
 // step 0: gather the probe queries of q into qp; 1: fit; 2: apply to o;

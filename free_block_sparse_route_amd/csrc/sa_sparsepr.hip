@@ -15,7 +15,8 @@
 //      Q of R^T R (the right singular vectors of R, by subspace iteration),
 //      Pk = Q Q^T.  Only B Q is formed: a Cholesky solve with the k columns of
 //      H Q; then C_B = (B Q) Q^T and C_b = (rm Q - xm B Q) Q^T;
-//   4. every row not probed takes O_s + C_b + O_s C_B, probed rows take O_d.
+//   4. every row not probed takes O_s + C_b + (O_s W) Q^T, W = B Q (the same as
+//      O_s C_B), probed rows take O_d.
 //
 // Steps 3 and 4 are small: d x d matrices per head and one d x d product per row.
 #include <math.h>
@@ -470,11 +471,11 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
         wb[c] = s;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < D * D; e += kPrThreads) {
-        const int i = e / D, j = e - (e / D) * D;
-        float s = 0.f;
-        for (int c = 0; c < K; ++c) s += T[i * 32 + c] * Qs[j * KP + c];
-        Bm[e] = s;
+    // the map's factors for the apply: W = B Q, then Q, both D x KP (zero past K)
+    for (int e = threadIdx.x; e < D * KP; e += kPrThreads) {
+        const int i = e / KP, c = e - (e / KP) * KP;
+        Bm[e] = c < K ? T[i * 32 + c] : 0.f;
+        Bm[D * KP + e] = Qs[e];
     }
     if (threadIdx.x < D) {
         float s = 0.f;
@@ -484,71 +485,111 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
 }
 
 // ------------------------------------------------------------------ apply
-// 64 rows per workgroup; thread t takes rows 4 (t / 16) .. +3 and columns
-// (t % 16) * D/16 .. (a 4 x D/16 register block).  X rows are padded by one
-// float so that the four rows a thread reads sit on different banks.
+// Four consecutive outputs in one store.
+template <typename T> struct Store4;
+template <> struct Store4<bf16> {
+    static __device__ __forceinline__ void st(bf16 *dst, const float *v) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)v[e];
+        *reinterpret_cast<bf16x4 *>(dst) = w;
+    }
+};
+template <> struct Store4<float> {
+    static __device__ __forceinline__ void st(float *dst, const float *v) {
+        *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+    }
+};
+
+// Every row takes O_s + C_b + O_s C_B with C_B = W Q^T of rank k: y = x W (k
+// values), then x + C_b + y Q^T; a row per four threads, D / 4 columns each in
+// groups of four, group g of thread p at columns 4 (p + 4 g) .. (the four
+// threads of a row read 64 contiguous bytes per load; the k partial sums of y
+// meet by lane swaps).  HBM-bound: one read of O_s and one write of O.
 template <typename T, int D>
 __global__ __launch_bounds__(kPrThreads) void pr_apply_kernel(T *__restrict__ o, PrArgs a) {
-    constexpr int CW = D / 16;                // columns per thread
-    constexpr int KC = 32;                    // rows of C_B per staging step
-    constexpr int XS = D + 1;                 // padded row stride of X
+    constexpr int TPR = 4;                    // threads per row
+    constexpr int CPT = D / TPR;              // columns per thread
+    constexpr int RPB = kPrThreads / TPR;     // rows per workgroup
     const int bh = blockIdx.y;
-    const int r0 = blockIdx.x * 64;
-    __shared__ float X[64 * XS];
-    __shared__ float Cs[KC * D];
-    const float *Os = a.O32 + (size_t)bh * a.N * D;
-    const float *CB = a.CB + (size_t)bh * D * D;
-    const float *Cb = a.Cb + (size_t)bh * D;
-    for (int e = threadIdx.x; e < 64 * D; e += kPrThreads) {
-        const int rr = e / D, f = e - (e / D) * D;
-        const int r = r0 + rr;
-        X[rr * XS + f] = r < a.N ? Os[(size_t)r * D + f] : 0.f;
+    const int K = a.rank, KP = (K + 3) & ~3;
+    __shared__ __attribute__((aligned(16))) float Ws[D * kPrMaxRank];
+    __shared__ __attribute__((aligned(16))) float Qs[D * kPrMaxRank];
+    __shared__ float Cbs[D];
+    __shared__ int probe_off[2 * kPrMaxPerBlock];         // probe rows (offsets in block) of the two blocks met
+    const float *F = a.CB + (size_t)bh * D * D;           // W [D][KP], then Q [D][KP]
+    const int I0 = blockIdx.x * RPB / a.block_q;          // first query block of this workgroup's rows
+    if (threadIdx.x < 2 * a.per_block) {
+        const int I = I0 + threadIdx.x / a.per_block, jj = threadIdx.x % a.per_block;
+        const int mI = max(0, min(a.block_q, a.N - I * a.block_q));
+        probe_off[threadIdx.x] = mI > 0 ? (2 * jj + 1) * mI / (2 * a.per_block) : -1;
     }
-    const int rg = threadIdx.x / 16, c0 = (threadIdx.x % 16) * CW;
-    float acc[4][CW];
-#pragma unroll
-    for (int c = 0; c < CW; ++c) {
-        const float bc = Cb[c0 + c];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][c] = bc;
+    for (int e = threadIdx.x; e < D * KP; e += kPrThreads) {
+        Ws[e] = F[e];
+        Qs[e] = F[D * KP + e];
     }
-    for (int k0 = 0; k0 < D; k0 += KC) {
-        __syncthreads();
-        for (int e = threadIdx.x; e < KC * D; e += kPrThreads) Cs[e] = CB[(size_t)k0 * D + e];
-        __syncthreads();
-#pragma unroll 4
-        for (int kk = 0; kk < KC; ++kk) {
-            float x[4], cs[CW];
+    for (int e = threadIdx.x; e < D; e += kPrThreads) Cbs[e] = a.Cb[(size_t)bh * D + e];
+    __syncthreads();
+    const int r = blockIdx.x * RPB + threadIdx.x / TPR;
+    const int pt = threadIdx.x % TPR;
+    auto col = [&](int c) { return 4 * (pt + TPR * (c >> 2)) + (c & 3); };   // thread's c-th column
+    if (r >= a.N) return;
+    const float *xr = a.O32 + ((size_t)bh * a.N + r) * D;
+    float x[CPT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = X[(4 * rg + i) * XS + k0 + kk];
+    for (int q = 0; q < CPT; q += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + col(q));
 #pragma unroll
-            for (int c = 0; c < CW; ++c) cs[c] = Cs[kk * D + c0 + c];
+        for (int w = 0; w < 4; ++w) x[q + w] = v[w];
+    }
+    // W and Q rows in groups of four (KP is a multiple of 4; columns past K are zero)
+    const int G4 = KP / 4;
+    f32x4 y[kPrMaxRank / 4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+    for (int g = 0; g < kPrMaxRank / 4; ++g) y[g] = f32x4{};
 #pragma unroll
-                for (int c = 0; c < CW; ++c) acc[i][c] = fmaf(x[i], cs[c], acc[i][c]);
+    for (int c = 0; c < CPT; ++c) {
+        const f32x4 *wr = reinterpret_cast<const f32x4 *>(Ws + col(c) * KP);
+#pragma unroll
+        for (int g = 0; g < kPrMaxRank / 4; ++g)
+            if (g < G4) y[g] += x[c] * wr[g];
+    }
+#pragma unroll
+    for (int g = 0; g < kPrMaxRank / 4; ++g) {
+        if (g < G4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                y[g][u] += __shfl_xor(y[g][u], 1, kWave);
+                y[g][u] += __shfl_xor(y[g][u], 2, kWave);
+            }
+        }
+    }
+    // probed rows take their dense values (the rows of a workgroup meet at most
+    // two query blocks: RPB <= block_q)
+    const int I = r / a.block_q, off = r - I * a.block_q;
+    const int* po = probe_off + (I - I0) * a.per_block;
+    int probe = -1;
+    for (int jj = 0; jj < a.per_block; ++jj)
+        if (po[jj] == off) probe = I * a.per_block + jj;
+    T *orow = o + ((size_t)bh * a.N + r) * D;
+    float out[CPT];
+    if (probe >= 0) {
+        const float *od = a.Od32 + ((size_t)bh * a.M + probe) * D;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) out[c] = od[col(c)];
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const f32x4 *qr = reinterpret_cast<const f32x4 *>(Qs + col(c) * KP);
+            f32x4 t = f32x4{};
+#pragma unroll
+            for (int g = 0; g < kPrMaxRank / 4; ++g)
+                if (g < G4) t += y[g] * qr[g];
+            out[c] = x[c] + Cbs[col(c)] + ((t[0] + t[1]) + (t[2] + t[3]));
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rl = 4 * rg + i, r = r0 + rl;
-        if (r >= a.N) break;
-        // probed rows take their dense values
-        const int I = r / a.block_q, off = r - I * a.block_q;
-        const int m = min(a.block_q, a.N - I * a.block_q);
-        int probe = -1;
-        for (int jj = 0; jj < a.per_block; ++jj)
-            if ((2 * jj + 1) * m / (2 * a.per_block) == off) probe = I * a.per_block + jj;
-        T *orow = o + ((size_t)bh * a.N + r) * D + c0;
-        if (probe >= 0) {
-            const float *od = a.Od32 + ((size_t)bh * a.M + probe) * D + c0;
-#pragma unroll
-            for (int c = 0; c < CW; ++c) orow[c] = (T)od[c];
-        } else {
-#pragma unroll
-            for (int c = 0; c < CW; ++c) orow[c] = (T)(X[rl * XS + c0 + c] + acc[i][c]);
-        }
-    }
+    for (int q = 0; q < CPT; q += 4) Store4<T>::st(orow + col(q), out + q);
 }
 
 // ------------------------------------------------------------------ merge
@@ -602,7 +643,7 @@ static hipError_t launch_pr_d(int dtype, const void *q, void *qp, void *o, const
         constexpr int RPB = kPrThreads / kWave;
         hipLaunchKernelGGL(pr_merge_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(kPrThreads), 0, st, a, rows);
     } else {
-        dim3 grid((a.N + 63) / 64, BH);
+        dim3 grid((a.N + kPrThreads / 4 - 1) / (kPrThreads / 4), BH);
         if (dtype == SA_BF16)
             hipLaunchKernelGGL((pr_apply_kernel<bf16, D>), grid, dim3(kPrThreads), 0, st, (bf16 *)o, a);
         else

@@ -208,8 +208,9 @@ sa_status sparse_attn_dense_ref_gpu(const sa_params *p, const void *q, const voi
  *      probe rows.
  * Intermediates live in the caller's workspace, of the size
  * sparse_attn_sparsepr_workspace_size() gives (host only, no HIP calls): the
- * gathered probe queries in q's dtype; O_s, the probes' dense outputs and the
- * fitted map (b, B Pk) in fp32.
+ * gathered probe queries in q's dtype; O_s, the probes' dense outputs (per key
+ * range, then merged), the Gram matrices and the fitted map (b Pk and the
+ * factors B Q and Q of B Pk) in fp32.
  * probes_per_block in [1, 16], rank in [1, min(16, d)], ridge >= 0; the route
  * must not be fused.  o has the layout and dtype of q.  The workspace must not
  * be shared by concurrent calls. */
