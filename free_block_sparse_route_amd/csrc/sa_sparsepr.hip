@@ -29,6 +29,7 @@ namespace sa {
 
 constexpr int kPrThreads = 256;
 constexpr int kPrIters = 40;             // subspace iterations
+constexpr int kFitThreads = 512;         // the fit: two waves per SIMD hide its LDS latencies (1024 is slower)
 
 __device__ __forceinline__ int probe_row(int j, const PrArgs &a) {
     const int I = j / a.per_block, jj = j - I * a.per_block;
@@ -191,7 +192,7 @@ struct FitLds {
 };
 
 template <int D>
-__global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
+__global__ __launch_bounds__(kFitThreads) void pr_fit_kernel(PrArgs a) {
     using FL = FitLds<D>;
     const int bh = blockIdx.x;
     const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -229,8 +230,8 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
     // with dx_c = xm_c - xm and dr_c = rm_c - rm
     // (four entries e, e + 256, ... per thread, so that their loads overlap)
     constexpr int EU = 4;
-    static_assert(D * D % (EU * kPrThreads) == 0, "entries split evenly");
-    for (int e0 = threadIdx.x; e0 < D * D; e0 += EU * kPrThreads) {
+    static_assert(D * D % (EU * kFitThreads) == 0, "entries split evenly");
+    for (int e0 = threadIdx.x; e0 < D * D; e0 += EU * kFitThreads) {
         float g[EU], hh[EU], sv[EU];
 #pragma unroll
         for (int u = 0; u < EU; ++u) g[u] = hh[u] = sv[u] = 0.f;
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
             const float dxj = mc[j] - xm[j], drj = mc[D + j] - rm[j];
 #pragma unroll
             for (int u = 0; u < EU; ++u) {
-                const int e = e0 + u * kPrThreads, i = e / D;
+                const int e = e0 + u * kFitThreads, i = e / D;
                 const float dxi = mc[i] - xm[i];
                 g[u] += pc[e] + n * dxi * dxj;
                 hh[u] += pc[D * D + e] + n * dxi * drj;
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < EU; ++u) {
-            const int e = e0 + u * kPrThreads;
+            const int e = e0 + u * kFitThreads;
             Gm[e] = g[u];
             Hm[e] = hh[u];
             Sm[e] = sv[u];
@@ -262,13 +263,13 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
 
     // ridge relative to the scale of the centred Gram matrix
     float tr = 0.f;
-    for (int i = threadIdx.x; i < D; i += kPrThreads) tr += Gm[i * D + i];
+    for (int i = threadIdx.x; i < D; i += kFitThreads) tr += Gm[i * D + i];
     tr = wave_sum(tr);
     if (lane == 0) red[wave] = tr;
     __syncthreads();
     float trace = 0.f;
 #pragma unroll
-    for (int w = 0; w < kPrThreads / kWave; ++w) trace += red[w];
+    for (int w = 0; w < kFitThreads / kWave; ++w) trace += red[w];
     const float lam = a.ridge * trace / (float)D;
 
     // Only B Pk = B Q Q^T is needed (Q: the k leading eigenvectors of R^T R), and
@@ -281,11 +282,11 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
     const int K = a.rank;
     const int KP = (K + 3) & ~3;                          // row stride of the basis (zero columns past K)
 #pragma unroll 16
-    for (int e = threadIdx.x; e < D * D; e += kPrThreads) {
+    for (int e = threadIdx.x; e < D * D; e += kFitThreads) {
         const int i = e / D, j = e - (e / D) * D;
         if (j <= i) Sp[tri(i, j)] = Sm[e];
     }
-    for (int e = threadIdx.x; e < D * KP; e += kPrThreads) {
+    for (int e = threadIdx.x; e < D * KP; e += kFitThreads) {
         const int i = e / KP, c = e - (e / KP) * KP;
         const int f = i * K + c;                          // the start's entry (i, c)
         uint32_t hsh = (uint32_t)f * 2654435761u + 0x9e3779b9u;
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
         if (it > 0) {
             // Z = S Q: thread (i, half) forms row i over half of the l range for
             // every column (each S entry read once), the halves meet by a lane swap
-            constexpr int TPR = kPrThreads / D;          // threads per row: 2 (D = 128) or 4 (D = 64)
+            constexpr int TPR = kFitThreads / D;         // threads per row (a power of two)
             const int i = threadIdx.x / TPR, part = threadIdx.x % TPR;
             f32x4 z[kPrMaxRank / 4];
 #pragma unroll
@@ -321,7 +322,8 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
                     for (int u = 0; u < 4; ++u) {
                         float v = z[g][u];
                         v += __shfl_xor(v, 1, kWave);
-                        if constexpr (TPR == 4) v += __shfl_xor(v, 2, kWave);
+#pragma unroll
+                        for (int sh = 2; sh < TPR; sh <<= 1) v += __shfl_xor(v, sh, kWave);
                         z[g][u] = v;
                     }
                 }
@@ -373,13 +375,13 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
 
     // G + lam I, packed over S (no longer needed)
 #pragma unroll 16
-    for (int e = threadIdx.x; e < D * D; e += kPrThreads) {
+    for (int e = threadIdx.x; e < D * D; e += kFitThreads) {
         const int i = e / D, j = e - (e / D) * D;
         if (j <= i) L[tri(i, j)] = Gm[e] + (i == j ? lam : 0.f);
     }
     // right-hand sides T = H Q (columns c < K of the 32-column region, the rest zero)
     float *T = reg;                                       // T[i * 32 + c]
-    for (int e = threadIdx.x; e < D * 32; e += kPrThreads) {
+    for (int e = threadIdx.x; e < D * 32; e += kFitThreads) {
         const int i = e / 32, c = e - (e / 32) * 32;
         float v = 0.f;
         if (c < K) {
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
         }
         __syncthreads();
         const float djj = L[tri(j, j)];
-        for (int t = threadIdx.x; t < 2 * (D - 1 - j); t += kPrThreads) {
+        for (int t = threadIdx.x; t < 2 * (D - 1 - j); t += kFitThreads) {
             const int i = j + 1 + (t >> 1), half = t & 1;
             const float *Li = L + tri(i, 0);
             float p[4] = {0.f, 0.f, 0.f, 0.f};
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(kPrThreads) void pr_fit_kernel(PrArgs a) {
     }
     __syncthreads();
     // the map's factors for the apply: W = B Q, then Q, both D x KP (zero past K)
-    for (int e = threadIdx.x; e < D * KP; e += kPrThreads) {
+    for (int e = threadIdx.x; e < D * KP; e += kFitThreads) {
         const int i = e / KP, c = e - (e / KP) * KP;
         Bm[e] = c < K ? T[i * 32 + c] : 0.f;
         Bm[D * KP + e] = Qs[e];
@@ -637,7 +639,7 @@ static hipError_t launch_pr_d(int dtype, const void *q, void *qp, void *o, const
         hipLaunchKernelGGL(pr_gram_kernel<D>, dim3(a.n_chunks, BH), dim3(kPrThreads), 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(pr_fit_kernel<D>, dim3(BH), dim3(kPrThreads), 0, st, a);
+        hipLaunchKernelGGL(pr_fit_kernel<D>, dim3(BH), dim3(kFitThreads), 0, st, a);
     } else if (step == 3) {
         const int rows = BH * a.M;
         constexpr int RPB = kPrThreads / kWave;
