@@ -940,8 +940,9 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
     FlashArgs a) {
     using C = FC<D, BQ>;
     const int p = grid_position(blockIdx.x, a.n_items);
-    // fused routing has no work order (no costs before the pass): plain order
-    const int item = kSparse && !kFused ? __builtin_amdgcn_readfirstlane(a.work_order[p]) : p;
+    // sparse paths take the route's cost-ordered work list (under fused routing
+    // the pre-pass costs the decisions the forward takes)
+    const int item = kSparse ? __builtin_amdgcn_readfirstlane(a.work_order[p]) : p;
     __shared__ __attribute__((aligned(1024))) unsigned char K0[C::TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char K1[C::TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char V0[C::TILE];

@@ -433,10 +433,36 @@ __device__ __forceinline__ void row_stats_only(const float *S, int bh, int I, co
     float z = 0.f;
     for (int J = lane; J < n; J += kWave) z += fast_exp(S[J] - m);
     z = wave_sum(z);
+    const float lse = m + fast_log(z);
+    // The work order's cost of the row under the decisions the fused forward
+    // will take (the same threshold test; a block within the rounding band may
+    // be decided the other way there, which only moves the estimate by a tile):
+    // exact tiles of the kept blocks plus one residual tile per mask word that
+    // holds a dropped block.
+    const float thr = fmaxf((a.tau_mode == SA_TAU_ABSOLUTE ? lse : m) + a.ln_tau, -3.40282347e38f);
+    const bool dense_row = (int64_t)I * a.block_q < a.n_prefix;
+    const int rows = a.exact_tile_rows;
+    const int t_full = (a.block_k + rows - 1) / rows;
+    const int t_last = (a.N - (n - 1) * a.block_k + rows - 1) / rows;
+    int tiles = 0;
+    for (int base = 0; base < n; base += kWave) {
+        const int J = base + lane;
+        const bool keep = J < n && (S[J] >= thr || dense_row || (int64_t)J * a.block_k < a.n_prefix);
+        tiles += keep ? (J == n - 1 ? t_last : t_full) : 0;
+        const uint64_t kb = __ballot(keep);
+        // the chunk's two mask words: residual tile if a valid block is dropped
+        const int lim0 = min(32, n - base), lim1 = min(32, max(0, n - base - 32));
+        const uint32_t v0 = lim0 >= 32 ? ~0u : ((1u << lim0) - 1u);
+        const uint32_t v1 = lim1 >= 32 ? ~0u : ((1u << lim1) - 1u);
+        if (lane == 0) tiles += (~(uint32_t)kb & v0) != 0u;
+        if (lane == 1 && lim1 > 0) tiles += (~(uint32_t)(kb >> 32) & v1) != 0u;
+    }
+    tiles = wave_count(tiles);
     if (lane == 0) {
         const size_t row = (size_t)bh * a.n_qb + I;
         a.row_stats[row * 2 + 0] = m;
-        a.row_stats[row * 2 + 1] = m + fast_log(z);
+        a.row_stats[row * 2 + 1] = lse;
+        a.cost[row] = tiles;
     }
 }
 
@@ -945,7 +971,8 @@ hipError_t launch_select(int D, const SelectArgs &a, int BH, hipStream_t st, int
         e = D == 64 ? launch_select_d<64>(a, G, BH, st) : launch_select_d<128>(a, G, BH, st);
     }
     if (e != hipSuccess) return e;
-    if (a.stats_only) return hipSuccess;            // fused routing: no lists, no work order
+    // (fused routing too: its pre-pass writes the costs of the decisions the
+    // forward will take)
     hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, st, (const int32_t *)a.cost, a.work_order,
                        BH * a.n_qb);
     return hipGetLastError();

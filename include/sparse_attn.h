@@ -33,10 +33,11 @@
  *     (block_q / 32 + 1) * n_kb + block_q floats fit in 64 KB.
  *     With SA_FLAG_FUSED (pass it to both calls) routing is fused into the
  *     attention pass, the Sol-Attn abstract's single pass: sparse_attn_route
- *     only pools and writes the proxy rows' maximum and log-sum-exp (no lists,
- *     no work order), and sparse_attn_forward takes each query block's
- *     decisions at the start of its work item from s_IJ and those statistics,
- *     writes them to kv_mask and kv_count, and attends in plain order.  The
+ *     only pools and writes the proxy rows' maximum and log-sum-exp, and the
+ *     cost and work order of the decisions to come (no lists), and
+ *     sparse_attn_forward takes each query block's decisions at the start of
+ *     its work item from s_IJ and those statistics, writes them to kv_mask and
+ *     kv_count, and attends in the work order.  The
  *     decisions are the τ test of RELATIVE or ABSOLUTE; max_keep must be 0,
  *     min_keep 0 (or 1 for RELATIVE with tau <= 1, where the argmax clears τ),
  *     no PAMA, n_kb <= 16384.  The dense prefix applies as above.
