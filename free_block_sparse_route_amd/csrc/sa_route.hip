@@ -835,14 +835,17 @@ __device__ __forceinline__ int cost_band(int32_t c) { return c > 1 ? 31 - __clz(
 // order is therefore by row, then by item: a stable sort.
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *cost, int32_t *work_order, int W) {
     constexpr int NW = kOrderThreads / kWave;
-    constexpr int kCells = kBands * kOrderTiles;
-    constexpr int kPer = kCells / kOrderThreads;
-    static_assert(kCells % kOrderThreads == 0, "scan split");
-    __shared__ int32_t cnt[kCells];                       // [row][tile]
+    static_assert(kBands * 32 % kOrderThreads == 0, "scan split");
+    __shared__ int32_t cnt[kBands * kOrderTiles];         // [row][tile]
     __shared__ int32_t part[NW];
     if (W <= 0) return;
+    // tiles in use: one per 64 items, a multiple of 32 (so that the scan splits
+    // evenly over the threads), at most kOrderTiles
+    const int T = min(kOrderTiles, ((W + kWave - 1) / kWave + 31) / 32 * 32);
+    const int kCells = kBands * T;
+    const int kPer = kCells / kOrderThreads;
     const int t = threadIdx.x, lane = lane_id(), wave = t / kWave;
-    const int m = (W + kWave * kOrderTiles - 1) / (kWave * kOrderTiles);   // 64-item chunks per tile
+    const int m = (W + kWave * T - 1) / (kWave * T);      // 64-item chunks per tile
     const int span = kWave * m;
     const int n_tiles = (W + span - 1) / span;
     for (int e = t; e < kCells; e += kOrderThreads) cnt[e] = 0;
@@ -855,7 +858,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *cos
             while (left) {
                 const int r = __builtin_amdgcn_readlane(row, __builtin_ctzll(left));
                 const uint64_t mr = __ballot(row == r);
-                if (lane == 0) cnt[r * kOrderTiles + tile] += __popcll(mr);
+                if (lane == 0) cnt[r * T + tile] += __popcll(mr);
                 left &= ~mr;
             }
         }
@@ -890,9 +893,9 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *cos
             while (left) {
                 const int r = __builtin_amdgcn_readlane(row, __builtin_ctzll(left));
                 const uint64_t mr = __ballot(row == r);
-                const int base = cnt[r * kOrderTiles + tile];
+                const int base = cnt[r * T + tile];
                 if (row == r) work_order[base + __popcll(mr & lanes_below())] = i;
-                if (lane == 0) cnt[r * kOrderTiles + tile] = base + __popcll(mr);
+                if (lane == 0) cnt[r * T + tile] = base + __popcll(mr);
                 left &= ~mr;
             }
         }
