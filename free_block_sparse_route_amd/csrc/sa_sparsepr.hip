@@ -28,7 +28,9 @@
 namespace sa {
 
 constexpr int kPrThreads = 256;
-constexpr int kPrIters = 40;             // subspace iterations
+constexpr int kPrIters = 40;             // subspace iterations on k columns (no room to double them)
+constexpr int kPrItersOver = 6;          // subspace iterations on 2k columns
+constexpr int kPrJacobiSweeps = 6;       // Jacobi sweeps of the Rayleigh-Ritz step
 constexpr int kFitThreads = 512;         // the fit: two waves per SIMD hide its LDS latencies (1024 is slower)
 
 __device__ __forceinline__ int probe_row(int j, const PrArgs &a) {
@@ -188,6 +190,8 @@ struct FitLds {
     static constexpr int kTri = D * (D + 1) / 2;
     static constexpr int kRegion = 32 * D > 2 * 16 * D ? 32 * D : 2 * 16 * D;   // >= D * kPrMaxRank too
     static_assert(kRegion >= D * kPrMaxRank, "basis fits the region");
+    static_assert(kRegion >= D * kPrMaxRank + 2 * kPrMaxRank * kPrMaxRank + kPrMaxRank,
+                  "Rayleigh-Ritz: S Q, the small matrix, its rotations and their order fit the region");
     static constexpr int kFloats = kTri + 2 * D + 64 + kRegion + D * kPrMaxRank;
 };
 
@@ -276,65 +280,73 @@ __global__ __launch_bounds__(kFitThreads) void pr_fit_kernel(PrArgs a) {
     // B Q = (G + lam I)^-1 (H Q): the subspace comes first, then a solve with k
     // right-hand sides instead of D.
 
-    // leading eigenvectors of S = R^T R by subspace iteration from a fixed start;
-    // S (symmetric) packed into LDS
+    // Leading eigenvectors of S = R^T R: subspace iteration on K2 = min(2k, 16)
+    // columns from a fixed start (S packed into LDS), then Rayleigh-Ritz: the
+    // k leading eigenvectors of the K2 x K2 matrix Q^T S Q (Jacobi rotations)
+    // carried back, Q_k = Q U_k.  With twice the columns the k-th direction
+    // separates at the rate lambda_{2k+1} / lambda_k per step instead of
+    // lambda_{k+1} / lambda_k; without room for them (k > 8) more steps are taken.
     float *Sp = L;
     const int K = a.rank;
-    const int KP = (K + 3) & ~3;                          // row stride of the basis (zero columns past K)
+    const int K2 = min(2 * K, kPrMaxRank);
+    const int KI = (K2 + 3) & ~3;                         // row stride of the iterated basis
+    const int KP = (K + 3) & ~3;                          // row stride of the final basis (zero past K)
+    const int n_iter = K2 >= 2 * K ? kPrItersOver : kPrIters;
 #pragma unroll 16
     for (int e = threadIdx.x; e < D * D; e += kFitThreads) {
         const int i = e / D, j = e - (e / D) * D;
         if (j <= i) Sp[tri(i, j)] = Sm[e];
     }
-    for (int e = threadIdx.x; e < D * KP; e += kFitThreads) {
-        const int i = e / KP, c = e - (e / KP) * KP;
-        const int f = i * K + c;                          // the start's entry (i, c)
+    for (int e = threadIdx.x; e < D * KI; e += kFitThreads) {
+        const int i = e / KI, c = e - (e / KI) * KI;
+        const int f = i * K2 + c;                         // the start's entry (i, c)
         uint32_t hsh = (uint32_t)f * 2654435761u + 0x9e3779b9u;
         hsh ^= hsh >> 15;
         hsh *= 2246822519u;
         hsh ^= hsh >> 13;
-        Qs[e] = c < K ? (float)(hsh & 0xffff) / 32768.f - 1.f : 0.f;
+        Qs[e] = c < K2 ? (float)(hsh & 0xffff) / 32768.f - 1.f : 0.f;
     }
     __syncthreads();
-    for (int it = 0; it <= kPrIters; ++it) {
-        if (it > 0) {
-            // Z = S Q: thread (i, half) forms row i over half of the l range for
-            // every column (each S entry read once), the halves meet by a lane swap
-            constexpr int TPR = kFitThreads / D;         // threads per row (a power of two)
-            const int i = threadIdx.x / TPR, part = threadIdx.x % TPR;
-            f32x4 z[kPrMaxRank / 4];
+    // Z = S Q into dst (stride KI): thread (i, part) forms row i over a part of
+    // the l range for every column (each S entry read once), the parts meet by
+    // lane swaps.  Ends with a barrier.
+    auto s_times_q = [&](float *dst) {
+        constexpr int TPR = kFitThreads / D;             // threads per row (a power of two)
+        const int i = threadIdx.x / TPR, part = threadIdx.x % TPR;
+        f32x4 z[kPrMaxRank / 4];
 #pragma unroll
-            for (int g = 0; g < kPrMaxRank / 4; ++g) z[g] = f32x4{};
-            const int l0 = part * (D / TPR), l1 = l0 + D / TPR;
-            const int G4 = KP / 4;
+        for (int g = 0; g < kPrMaxRank / 4; ++g) z[g] = f32x4{};
+        const int l0 = part * (D / TPR), l1 = l0 + D / TPR;
+        const int G4 = KI / 4;
 #pragma unroll 8
-            for (int l = l0; l < l1; ++l) {
-                const float sv = l <= i ? Sp[tri(i, l)] : Sp[tri(l, i)];
-                const f32x4 *ql = reinterpret_cast<const f32x4 *>(Qs + l * KP);
+        for (int l = l0; l < l1; ++l) {
+            const float sv = l <= i ? Sp[tri(i, l)] : Sp[tri(l, i)];
+            const f32x4 *ql = reinterpret_cast<const f32x4 *>(Qs + l * KI);
 #pragma unroll
-                for (int g = 0; g < kPrMaxRank / 4; ++g)
-                    if (g < G4) z[g] += sv * ql[g];
-            }
+            for (int g = 0; g < kPrMaxRank / 4; ++g)
+                if (g < G4) z[g] += sv * ql[g];
+        }
 #pragma unroll
-            for (int g = 0; g < kPrMaxRank / 4; ++g) {
-                if (g < G4) {
+        for (int g = 0; g < kPrMaxRank / 4; ++g) {
+            if (g < G4) {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        float v = z[g][u];
-                        v += __shfl_xor(v, 1, kWave);
+                for (int u = 0; u < 4; ++u) {
+                    float v = z[g][u];
 #pragma unroll
-                        for (int sh = 2; sh < TPR; sh <<= 1) v += __shfl_xor(v, sh, kWave);
-                        z[g][u] = v;
-                    }
+                    for (int sh = 1; sh < TPR; sh <<= 1) v += __shfl_xor(v, sh, kWave);
+                    z[g][u] = v;
                 }
             }
-            __syncthreads();
-            if (part == 0)
-#pragma unroll
-                for (int g = 0; g < kPrMaxRank / 4; ++g)
-                    if (g < G4) *reinterpret_cast<f32x4 *>(Qs + i * KP + 4 * g) = z[g];
-            __syncthreads();
         }
+        __syncthreads();
+        if (part == 0)
+#pragma unroll
+            for (int g = 0; g < kPrMaxRank / 4; ++g)
+                if (g < G4) *reinterpret_cast<f32x4 *>(dst + i * KI + 4 * g) = z[g];
+        __syncthreads();
+    };
+    for (int it = 0; it <= n_iter; ++it) {
+        if (it > 0) s_times_q(Qs);
         // modified Gram-Schmidt on the columns, by one wave, in registers: lane
         // l holds rows l, l + 64, ..
         if (wave == 0) {
@@ -343,10 +355,10 @@ __global__ __launch_bounds__(kFitThreads) void pr_fit_kernel(PrArgs a) {
 #pragma unroll
             for (int r = 0; r < RL; ++r)
 #pragma unroll
-                for (int c = 0; c < kPrMaxRank; ++c) qv[r][c] = c < K ? Qs[(lane + r * kWave) * KP + c] : 0.f;
+                for (int c = 0; c < kPrMaxRank; ++c) qv[r][c] = c < K2 ? Qs[(lane + r * kWave) * KI + c] : 0.f;
 #pragma unroll
             for (int c = 0; c < kPrMaxRank; ++c) {
-                if (c >= K) break;
+                if (c >= K2) break;
 #pragma unroll
                 for (int pcol = 0; pcol < c; ++pcol) {
                     float dp = 0.f;
@@ -368,8 +380,103 @@ __global__ __launch_bounds__(kFitThreads) void pr_fit_kernel(PrArgs a) {
             for (int r = 0; r < RL; ++r)
 #pragma unroll
                 for (int c = 0; c < kPrMaxRank; ++c)
-                    if (c < K) Qs[(lane + r * kWave) * KP + c] = qv[r][c];
+                    if (c < K2) Qs[(lane + r * kWave) * KI + c] = qv[r][c];
         }
+        __syncthreads();
+    }
+    // Rayleigh-Ritz.  The T region holds Z = S Q, then Hr = Q^T Z (K2 x K2,
+    // stride 16), Ur (the rotations, K2 x K2, stride 16) and the order of the
+    // Ritz values.
+    {
+        float *Z = reg;
+        float *Hr = reg + D * kPrMaxRank;
+        float *Ur = Hr + kPrMaxRank * kPrMaxRank;
+        int *sel = reinterpret_cast<int *>(Ur + kPrMaxRank * kPrMaxRank);
+        s_times_q(Z);
+        for (int e = threadIdx.x; e < K2 * K2; e += kFitThreads) {
+            const int r = e / K2, c = e - (e / K2) * K2;
+            float h = 0.f;
+#pragma unroll 8
+            for (int l = 0; l < D; ++l) h = fmaf(Qs[l * KI + r], Z[l * KI + c], h);
+            Hr[r * kPrMaxRank + c] = h;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // symmetrise (rounding), then cyclic Jacobi: lane j < K2 updates
+            // entries (j, p), (j, q) and their mirrors, and row j of U
+            if (lane < K2)
+                for (int c = 0; c < lane; ++c) {
+                    const float m = 0.5f * (Hr[lane * kPrMaxRank + c] + Hr[c * kPrMaxRank + lane]);
+                    Hr[lane * kPrMaxRank + c] = m;
+                    Hr[c * kPrMaxRank + lane] = m;
+                }
+            float u[kPrMaxRank];
+#pragma unroll
+            for (int c = 0; c < kPrMaxRank; ++c) u[c] = c == lane ? 1.f : 0.f;
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            for (int sweep = 0; sweep < kPrJacobiSweeps; ++sweep) {
+#pragma unroll
+                for (int pp = 0; pp < kPrMaxRank - 1; ++pp) {
+#pragma unroll
+                    for (int qq = pp + 1; qq < kPrMaxRank; ++qq) {
+                        if (qq >= K2) break;
+                        const float hpq = Hr[pp * kPrMaxRank + qq];
+                        const float hpp = Hr[pp * kPrMaxRank + pp], hqq = Hr[qq * kPrMaxRank + qq];
+                        // converged pairs (off-diagonal below fp32 resolution of the diagonal) are skipped
+                        if (!(fabsf(hpq) > 1e-7f * (fabsf(hpp) + fabsf(hqq)))) continue;
+                        const float theta = (hqq - hpp) / (2.f * hpq);
+                        const float t = (theta >= 0.f ? 1.f : -1.f) / (fabsf(theta) + sqrtf(theta * theta + 1.f));
+                        const float c = 1.f / sqrtf(t * t + 1.f), sn = t * c;
+                        if (lane < K2 && lane != pp && lane != qq) {
+                            const float hjp = Hr[lane * kPrMaxRank + pp], hjq = Hr[lane * kPrMaxRank + qq];
+                            const float np = c * hjp - sn * hjq, nq = sn * hjp + c * hjq;
+                            Hr[lane * kPrMaxRank + pp] = np;
+                            Hr[lane * kPrMaxRank + qq] = nq;
+                            Hr[pp * kPrMaxRank + lane] = np;
+                            Hr[qq * kPrMaxRank + lane] = nq;
+                        }
+                        if (lane == 0) {
+                            Hr[pp * kPrMaxRank + pp] = hpp - t * hpq;
+                            Hr[qq * kPrMaxRank + qq] = hqq + t * hpq;
+                            Hr[pp * kPrMaxRank + qq] = 0.f;
+                            Hr[qq * kPrMaxRank + pp] = 0.f;
+                        }
+                        const float up = u[pp], uq = u[qq];
+                        u[pp] = c * up - sn * uq;
+                        u[qq] = sn * up + c * uq;
+                        __builtin_amdgcn_s_waitcnt(0xc07f);
+                        __builtin_amdgcn_wave_barrier();
+                    }
+                }
+            }
+            // lane j: row j of U; rank of the Ritz value j (largest first, ties by index)
+            if (lane < K2) {
+#pragma unroll
+                for (int c = 0; c < kPrMaxRank; ++c)
+                    if (c < K2) Ur[lane * kPrMaxRank + c] = u[c];
+                const float dj = Hr[lane * kPrMaxRank + lane];
+                int rank = 0;
+                for (int m = 0; m < K2; ++m) {
+                    const float dm = Hr[m * kPrMaxRank + m];
+                    rank += dm > dj || (dm == dj && m < lane);
+                }
+                if (rank < K) sel[rank] = lane;
+            }
+        }
+        __syncthreads();
+        // Q_k = Q U_k into Z (stride KP), then back into Qs
+        for (int e = threadIdx.x; e < D * KP; e += kFitThreads) {
+            const int i = e / KP, r = e - (e / KP) * KP;
+            float v = 0.f;
+            if (r < K) {
+                const int j = sel[r];
+                for (int m = 0; m < K2; ++m) v = fmaf(Qs[i * KI + m], Ur[m * kPrMaxRank + j], v);
+            }
+            Z[e] = v;
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < D * KP; e += kFitThreads) Qs[e] = Z[e];
         __syncthreads();
     }
 
