@@ -30,7 +30,7 @@ namespace sa {
 constexpr int kPrThreads = 256;
 constexpr int kPrIters = 40;             // subspace iterations on k columns (no room to double them)
 constexpr int kPrItersOver = 6;          // subspace iterations on 2k columns
-constexpr int kPrJacobiSweeps = 6;       // Jacobi sweeps of the Rayleigh-Ritz step
+constexpr int kPrJacobiSweeps = 4;       // Jacobi sweeps of the Rayleigh-Ritz step
 constexpr int kFitThreads = 512;         // the fit: two waves per SIMD hide its LDS latencies (1024 is slower)
 
 __device__ __forceinline__ int probe_row(int j, const PrArgs &a) {
