@@ -28,7 +28,7 @@
 namespace sa {
 
 constexpr int kPoolThreads = 256;
-constexpr int kSelectThreads = 256;
+constexpr int kSelectThreads = 512;       // 8 waves: a row per wave in flight on more SIMD slots
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderTiles = 448;         // 32 x 448 counters: 56 KB of LDS
 constexpr int kBands = 32;               // floor(log2(cost)) of a non-negative int32
