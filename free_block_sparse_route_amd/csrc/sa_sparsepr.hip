@@ -4,19 +4,21 @@
 //   1. the sparse output O_s over the kept tokens only, in fp32 (forward kernel,
 //      no block residual);
 //   2. probe rows, P per query block evenly spread (row I*bq + floor((j+1/2) m_I / P)),
-//      gathered and attended densely (forward kernel, dense path), in fp32;
+//      gathered and attended densely (forward kernel, dense path, the key tiles
+//      split into ranges whose rows merge by their log-sum-exp), in fp32;
 //   3. per (b, h) and chunk of kPrChunk probes, one workgroup forms the chunk's
 //      means and centred Gram matrices; then per (b, h) one workgroup combines
 //      the chunks (the centred scatter of a union is the sum of the chunks'
 //      plus n_c (m_c - m)(m_c - m)^T per chunk, which keeps the centring exact
-//      in fp32) and fits R = O_d - O_s at the probes as an affine
-//      map of x = O_s, B = (G + lam I)^-1 H with a ridge lam = ridge * trace / d
-//      and the intercept b = rm - xm B, projected on the k leading eigenvectors
-//      Q of R^T R (the right singular vectors of R, by subspace iteration),
-//      Pk = Q Q^T.  Only B Q is formed: a Cholesky solve with the k columns of
-//      H Q; then C_B = (B Q) Q^T and C_b = (rm Q - xm B Q) Q^T;
-//   4. every row not probed takes O_s + C_b + (O_s W) Q^T, W = B Q (the same as
-//      O_s C_B), probed rows take O_d.
+//      in fp32) and fits R = O_d - O_s at the probes as an affine map of
+//      x = O_s, B = (G + lam I)^-1 H with a ridge lam = ridge * trace / d and
+//      the intercept b = rm - xm B, projected on the k leading eigenvectors Q
+//      of R^T R (the right singular vectors of R; subspace iteration on 2k
+//      columns, then Rayleigh-Ritz), Pk = Q Q^T.  Only W = B Q is formed, by
+//      a Cholesky solve with the k columns of H Q; the fit leaves W, Q and
+//      C_b = (rm Q - xm W) Q^T;
+//   4. every row not probed takes O_s + C_b + (O_s W) Q^T (= O_s B Pk + b Pk
+//      + O_s), probed rows take O_d.
 //
 // Steps 3 and 4 are small: d x d matrices per head and one d x d product per row.
 #include <math.h>
