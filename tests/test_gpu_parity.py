@@ -143,6 +143,14 @@ def test_fused_parity(case):
     say(f"  rows with identical decisions {int(same.sum())} / {same.size}")
     rows = torch.from_numpy(np.repeat(same, w.block_q, axis=-1)[..., :w.N])
     assert torch.equal(O.cpu()[rows], O2.cpu()[rows]) and torch.equal(L.cpu()[rows], L2.cpu()[rows])
+    # the pre-pass costs each row under the same decisions: equal costs on those
+    # rows, and a work order sorted by cost band
+    cost, cost2 = rt.cost.cpu().numpy(), rt2.cost.cpu().numpy()
+    if not cfg.no_residual:
+        assert np.array_equal(cost[same], cost2[same])
+    c = cost.ravel().astype(np.int64)
+    band = np.floor(np.log2(np.maximum(c, 1))).astype(np.int64)
+    assert np.array_equal(rt.work_order.cpu().numpy(), np.lexsort((np.arange(c.size), -band)))
 
 
 def test_fused_rejects_what_it_cannot_decide_alone():
