@@ -97,8 +97,16 @@ int32_t min_cap(const sa_params *p) {
     return lim < d.n_kb ? lim : d.n_kb;
 }
 
+// Host pointers (the route descriptor): not NULL.
+sa_status check_host_ptr(const void *ptr, const char *name) {
+    if (!ptr) return fail(SA_ERR_INVALID_ARG, "%s is NULL", name);
+    return SA_OK;
+}
+
+// Device pointers: not NULL, 16-byte aligned (the kernels move 16-byte vectors).
 sa_status check_ptr(const void *ptr, const char *name) {
     if (!ptr) return fail(SA_ERR_INVALID_ARG, "%s is NULL", name);
+    if ((uintptr_t)ptr % 16 != 0) return fail(SA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
     return SA_OK;
 }
 
@@ -138,7 +146,7 @@ sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, co
     sa_status s = check_params(p, true);
     if (s != SA_OK) return s;
     if ((s = check_ptr(q, "q")) || (s = check_ptr(k, "k")) || (s = check_ptr(v, "v")) ||
-        (s = check_ptr(r, "route")))
+        (s = check_host_ptr(r, "route")))
         return s;
     if ((s = check_ptr(r->kv_count, "route.kv_count")) || (s = check_ptr(r->kv_idx, "route.kv_idx")) ||
         (s = check_ptr(r->kv_mask, "route.kv_mask")) || (s = check_ptr(r->q_mean, "route.q_mean")) ||
@@ -219,7 +227,7 @@ sa_status sparse_attn_forward(const sa_params *p, const void *q, const void *k, 
     sa_status s = check_params(p, true);
     if (s != SA_OK) return s;
     if ((s = check_ptr(q, "q")) || (s = check_ptr(k, "k")) || (s = check_ptr(v, "v")) ||
-        (s = check_ptr(o, "o")) || (s = check_ptr(r, "route")))
+        (s = check_ptr(o, "o")) || (s = check_host_ptr(r, "route")))
         return s;
     if ((s = check_ptr(r->kv_count, "route.kv_count")) || (s = check_ptr(r->kv_idx, "route.kv_idx")) ||
         (s = check_ptr(r->kv_mask, "route.kv_mask")) ||
@@ -267,7 +275,8 @@ sa_status sparse_attn_permute_tokens(int32_t B, int32_t H, int32_t N, int32_t d,
     if (n0 < 0 || n_perm < 0 || (int64_t)n0 + n_perm > N)
         return fail(SA_ERR_INVALID_ARG, "rows [%d, %d + %d) outside [0, %d)", n0, n0, n_perm, N);
     if (inverse != 0 && inverse != 1) return fail(SA_ERR_INVALID_ARG, "inverse must be 0 or 1");
-    if (!in || !out) return fail(SA_ERR_INVALID_ARG, "in or out is NULL");
+    sa_status s;
+    if ((s = check_ptr(in, "in")) || (s = check_ptr(out, "out"))) return s;
     if (in == out) return fail(SA_ERR_INVALID_ARG, "in and out must not be the same buffer");
     if (n_perm > 0 && !perm) return fail(SA_ERR_INVALID_ARG, "perm is NULL");
     if ((int64_t)B * H * N * d > ((int64_t)1 << 40)) return fail(SA_ERR_INVALID_ARG, "tensor too large");
@@ -354,7 +363,7 @@ sa_status sparse_attn_forward_sparsepr(const sa_params *p, const void *q, const 
     if (s != SA_OK) return s;
     if ((s = check_pr(p, probes_per_block, rank, ridge)) != SA_OK) return s;
     if ((s = check_ptr(q, "q")) || (s = check_ptr(k, "k")) || (s = check_ptr(v, "v")) ||
-        (s = check_ptr(o, "o")) || (s = check_ptr(r, "route")) || (s = check_ptr(workspace, "workspace")))
+        (s = check_ptr(o, "o")) || (s = check_host_ptr(r, "route")) || (s = check_ptr(workspace, "workspace")))
         return s;
     if ((s = check_ptr(r->kv_count, "route.kv_count")) || (s = check_ptr(r->kv_idx, "route.kv_idx")) ||
         (s = check_ptr(r->kv_mask, "route.kv_mask")) || (s = check_ptr(r->kv_split, "route.kv_split")) ||

@@ -64,8 +64,11 @@
  *    value and its remainder), the softmax weights as bf16.  Routing
  *    (pooling, proxy, threshold) is fp32 throughout.
  *  - Every tensor pointer is a DEVICE pointer (hipMalloc or equivalent) of the
- *    current HIP device.  The caller owns and frees all memory; the library
- *    allocates nothing, frees nothing and never synchronises.
+ *    current HIP device, 16-byte aligned (hipMalloc and torch allocations are;
+ *    the kernels move 16-byte vectors; lse and perm need 4 bytes).  A
+ *    misaligned pointer is SA_ERR_INVALID_ARG.  The caller owns and frees all
+ *    memory; the library allocates nothing, frees nothing and never
+ *    synchronises.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *    work is enqueued asynchronously on it; results are ready once the caller
  *    synchronises that stream.

@@ -143,26 +143,43 @@ def test_route_sizes_wan13b():
 def test_null_pointers_rejected_before_launch():
     p = params()
     r = B.SaRoute()
-    st = B.lib.sparse_attn_route(ctypes.byref(p), None, 1, 1, ctypes.byref(r), None)
+    A = 0x1000                     # a stand-in device address (16-byte aligned), never dereferenced
+    st = B.lib.sparse_attn_route(ctypes.byref(p), None, A, A, ctypes.byref(r), None)
     assert st == B.SA_ERR_INVALID_ARG and "q is NULL" in B.last_error()
-    st = B.lib.sparse_attn_route(ctypes.byref(p), 1, 1, 1, ctypes.byref(r), None)
+    st = B.lib.sparse_attn_route(ctypes.byref(p), A, A, A, ctypes.byref(r), None)
     assert st == B.SA_ERR_INVALID_ARG and "route.kv_count" in B.last_error()
-    st = B.lib.sparse_attn_forward(ctypes.byref(p), 1, 1, 1, None, 1, None, None)
+    st = B.lib.sparse_attn_forward(ctypes.byref(p), A, A, A, None, A, None, None)
     assert st == B.SA_ERR_INVALID_ARG and "route is NULL" in B.last_error()
-    st = B.lib.sparse_attn_dense_ref_gpu(ctypes.byref(p), 1, 1, 1, None, None, None)
+    st = B.lib.sparse_attn_dense_ref_gpu(ctypes.byref(p), A, A, A, None, None, None)
     assert st == B.SA_ERR_INVALID_ARG and "o is NULL" in B.last_error()
-    st = B.lib.sparse_attn_route(None, 1, 1, 1, ctypes.byref(r), None)
+    st = B.lib.sparse_attn_route(None, A, A, A, ctypes.byref(r), None)
     assert st == B.SA_ERR_INVALID_ARG
 
 
 def test_capacity_checked_before_launch():
     p = params(max_keep=4)
-    r = B.SaRoute(*([1] * len(B.BUFFERS)), 3)
-    assert B.lib.sparse_attn_route(ctypes.byref(p), 1, 1, 1, ctypes.byref(r), None) == B.SA_ERR_CAPACITY
-    assert B.lib.sparse_attn_forward(ctypes.byref(p), 1, 1, 1, ctypes.byref(r), 1, None, None) == B.SA_ERR_CAPACITY
+    A = 0x1000                     # a stand-in device address (16-byte aligned), never dereferenced
+    r = B.SaRoute(*([A] * len(B.BUFFERS)), 3)
+    assert B.lib.sparse_attn_route(ctypes.byref(p), A, A, A, ctypes.byref(r), None) == B.SA_ERR_CAPACITY
+    assert B.lib.sparse_attn_forward(ctypes.byref(p), A, A, A, ctypes.byref(r), A, None, None) == B.SA_ERR_CAPACITY
 
 
 def test_status_strings():
     assert B.status_string(0) == "ok"
     assert "capacity" in B.status_string(B.SA_ERR_CAPACITY)
     assert B.status_string(-99) == "unknown status"
+
+
+def test_misaligned_device_pointers_rejected_before_launch():
+    """Device pointers must be 16-byte aligned (the kernels move 16-byte vectors);
+    a misaligned one is an argument error, and nothing is launched."""
+    p = params()
+    good, bad = 0x1000, 0x1008
+    r = B.SaRoute(*([good] * len(B.BUFFERS)), 1 << 10)
+    assert B.lib.sparse_attn_forward(ctypes.byref(p), bad, good, good, ctypes.byref(r), good, None, None) == \
+        B.SA_ERR_INVALID_ARG
+    assert b"aligned" in B.lib.sparse_attn_last_error()
+    r_bad = B.SaRoute(*([good] * (len(B.BUFFERS) - 1) + [bad]), 1 << 10)      # work_order misaligned
+    assert B.lib.sparse_attn_route(ctypes.byref(p), good, good, good, ctypes.byref(r_bad), None) == \
+        B.SA_ERR_INVALID_ARG
+    assert B.lib.sparse_attn_permute_tokens(1, 1, 64, 64, 0, 0, 0, None, 0, bad, good, None) == B.SA_ERR_INVALID_ARG
