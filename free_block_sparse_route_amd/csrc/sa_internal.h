@@ -8,8 +8,8 @@ namespace sa {
 
 typedef __bf16 bf16;
 
-constexpr size_t kSelectLdsBudget = 64 * 1024;   // proxy rows of one select workgroup
-constexpr int kMaxKeyBlocks = 16384 - 16;       // n_kb limit implied by that budget at G = 1
+constexpr size_t kSelectLdsBudget = 80 * 1024;   // proxy rows of one select workgroup (gfx950: up to 160 KB per workgroup)
+constexpr int kMaxKeyBlocks = 16384 - 16;       // n_kb limit: one proxy row at G = 1 stays within 64 KB
 
 struct PoolArgs {
     int N, block_q, block_k, n_qb, n_kb, words;

@@ -940,6 +940,11 @@ template <int D, int G, int R>
 static hipError_t launch_select_t(const SelectArgs &a, int BH, hipStream_t st) {
     const size_t lds = select_lds_bytes(G, a.n_kb, D);
     dim3 grid((a.n_qb + G - 1) / G * BH);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)select_kernel<D, G, R>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((select_kernel<D, G, R>), grid, dim3(kSelectThreads), lds, st, a);
     return hipGetLastError();
 }
