@@ -82,7 +82,7 @@ sa_status check_params(const sa_params *p, bool routing) {
         if (!floor_free) return fail(SA_ERR_UNSUPPORTED, "fused routing with a min_keep floor that can bind");
         if (d.words > sa::kFusedMaxWords) return fail(SA_ERR_UNSUPPORTED, "fused routing: n_kb = %d too large", d.n_kb);
     }
-    if (routing && (p->flags & SA_FLAG_PAMA) && sa::pama_lds_bytes(d.n_kb, p->block_q) > sa::kPamaLdsBudget)
+    if (routing && (p->flags & SA_FLAG_PAMA) && sa::pama_lds_bytes(d.n_kb, p->block_q, p->dtype) > sa::kPamaLdsBudget)
         return fail(SA_ERR_UNSUPPORTED, "PAMA proxy: n_kb = %d too large for block_q = %d", d.n_kb, p->block_q);
     if (d.BH * d.n_qb > INT32_MAX / 2) return fail(SA_ERR_UNSUPPORTED, "too many work items");
     return SA_OK;

@@ -68,8 +68,8 @@ hipError_t launch_pool(int dtype, int D, const void *q, const void *k, const voi
 // otherwise the PAMA proxy from the queries q (dtype an sa_dtype).
 hipError_t launch_select(int D, const SelectArgs &a, int BH, hipStream_t st, int dtype = 0,
                          const void *q = nullptr);
-size_t pama_lds_bytes(int n_kb, int BQ);
-constexpr size_t kPamaLdsBudget = 64 * 1024;
+size_t pama_lds_bytes(int n_kb, int BQ, int dtype);
+constexpr size_t kPamaLdsBudget = 128 * 1024;
 constexpr int kFusedMaxWords = 512;              // decision words a fused work item holds in LDS
 int select_group(int n_kb, int D, int n_qb);
 size_t select_lds_bytes(int G, int n_kb, int D);

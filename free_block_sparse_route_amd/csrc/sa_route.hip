@@ -613,15 +613,25 @@ __device__ __forceinline__ void split8(const float *x, bf16x8 (&p)[NP]) {
     }
 }
 
+constexpr int kPamaThreads = 256;       // 4 waves
+
+// Query sets of 32 per wave: two for bf16 queries (the key operands read from
+// LDS serve both sets' products), one for fp32 queries (their three bf16 parts
+// fill the registers).
+template <typename T> struct PamaShape {
+    static constexpr int QS = QSplit<T>::N == 1 ? 2 : 1;
+    static constexpr int QW = 32 * QS;                    // queries per wave
+    static constexpr int QWG = (kPamaThreads / kWave) * QW;   // queries per workgroup
+};
+
 // Staging of one tile of 32 key-block means, split into three bf16 parts, in
 // LDS: part p, row r at p * 32 * RS + r * RS bytes, RS = 2 D + 16 (the pad puts
 // the 16 rows read by one ds_read_b128 quarter on distinct banks).  Every
 // thread loads, splits and writes FPT consecutive features of one row; the
 // waves then read their MFMA operands from the one staged copy.
-template <int D, int BQ>
+template <int D>
 struct PamaStage {
-    static constexpr int THREADS = BQ * 2;
-    static constexpr int FPT = 32 * D / THREADS;        // features per thread
+    static constexpr int FPT = 32 * D / kPamaThreads;   // features per thread
     static constexpr int TPR = D / FPT;                 // threads per row
     static constexpr int RS = 2 * D + 16;
     static constexpr int BYTES = 3 * 32 * RS;
@@ -659,48 +669,58 @@ struct PamaStage {
     }
 };
 
+// One workgroup per NB = QWG / BQ consecutive query blocks of a head; wave w
+// holds the QW queries w QW .. of the group (all in one block, since QW <= BQ).
 template <typename T, int D, int BQ, int R>
-__global__ __launch_bounds__(BQ * 2) void pama_kernel(const T *__restrict__ q, SelectArgs a) {
-    constexpr int WAVES = BQ / 32;
+__global__ __launch_bounds__(kPamaThreads) void pama_kernel(const T *__restrict__ q, SelectArgs a) {
+    using Sh = PamaShape<T>;
+    constexpr int QS = Sh::QS, QW = Sh::QW, NB = Sh::QWG / BQ;
+    constexpr int WAVES = kPamaThreads / kWave, WPB = BQ / QW;   // waves per query block
+    static_assert(QW <= BQ && Sh::QWG % BQ == 0, "a wave's queries lie in one block");
     constexpr int NQ = QSplit<T>::N;
     constexpr int NS = D / 16;
-    using St = PamaStage<D, BQ>;
+    using St = PamaStage<D>;
     extern __shared__ __attribute__((aligned(16))) float smem[];
     const int n = a.n_kb;
     unsigned char *tile = reinterpret_cast<unsigned char *>(smem);
     float *part = smem + St::BYTES / 4;          // [WAVES][n]
-    float *row = part + WAVES * n;               // [n]: ln A
-    float *cq = row + n;                         // [BQ]: per-query log2 normaliser
-    const int task = die_task(blockIdx.x, (int)gridDim.x, a.n_qb);   // one head per die, as in select
-    const int bh = task / a.n_qb, I = task - bh * a.n_qb;
+    float *rows = part + WAVES * n;              // [NB][n]: ln A per block
+    float *cq = rows + NB * n;                   // [QWG]: per-query log2 normaliser
+    const int n_grp = (a.n_qb + NB - 1) / NB;
+    const int task = die_task(blockIdx.x, (int)gridDim.x, n_grp);   // the groups of a head on one die
+    const int bh = task / n_grp, I0 = (task - bh * n_grp) * NB;
     const int lane = lane_id(), h = lane >> 5, l32 = lane & 31;
     const int wave = threadIdx.x / kWave;
-    const int q0 = I * a.block_q;
-    const int m_I = min(a.block_q, a.N - q0);
-    const int qrow = q0 + wave * 32 + l32;
-    const bool row_ok = wave * 32 + l32 < m_I;
+    const int wb = wave / WPB;                   // the wave's block within the group
+    const int Iw = I0 + wb;
+    const int q0 = Iw * a.block_q;
+    const int m_w = Iw < a.n_qb ? min(a.block_q, a.N - q0) : 0;   // the block's actual rows
     const float c2 = a.scale * 1.44269504088896341f;          // logits in log2 units
 
-    bf16x8 qf[NS][NQ];           // lane (h, l32): query l32 of the wave, features 16c + 8h..
-    {
-        const T *src = q + ((size_t)bh * a.N + (row_ok ? qrow : q0)) * D + 8 * h;
+    bf16x8 qf[QS][NS][NQ];       // lane (h, l32): query l32 of set s, features 16c + 8h..
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+        const int rb = (wave % WPB) * QW + s * 32 + l32;       // row within the block
+        const bool ok = rb < m_w;
+        const T *src = q + ((size_t)bh * a.N + (ok ? q0 + rb : 0)) * D + 8 * h;
 #pragma unroll
         for (int c = 0; c < NS; ++c) {
             float x[8];
             Ld8<T>::load_f32(src + 16 * c, x);
-            if (!row_ok)
+            if (!ok)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = 0.f;
-            split8<NQ>(x, qf[c]);
+            split8<NQ>(x, qf[s][c]);
         }
     }
     const float *kb = a.k_mean + (size_t)bh * n * D;
     const int n_jt = (n + 31) / 32;
 
-    // One pass over the key-block tiles.  kSwap = false: S^T (lane: query l32,
-    // key blocks 8(r/4) + 4h + r%4); true: S (lane: key block l32, queries
-    // 8(r/4) + 4h + r%4).  Products of parts with orders a + b <= 2, smallest
-    // first.  The next tile's means are loaded while this one is multiplied.
+    // One pass over the key-block tiles.  kSwap = false: S^T (lane: query l32
+    // of set s, key blocks 8(r/4) + 4h + r%4); true: S (lane: key block l32,
+    // queries 8(r/4) + 4h + r%4 of set s).  Products of parts with orders
+    // a + b <= 2, smallest first.  The next tile's means are loaded while this
+    // one is multiplied.
     auto pass = [&](auto swap, auto &&post) {
         constexpr bool kSwap = decltype(swap)::value;
         St st;
@@ -709,7 +729,9 @@ __global__ __launch_bounds__(BQ * 2) void pama_kernel(const T *__restrict__ q, S
             st.store(tile);
             __syncthreads();
             if (jt + 1 < n_jt) st.load(kb, n, jt + 1);
-            f32x16 acc = {};
+            f32x16 acc[QS];
+#pragma unroll
+            for (int s = 0; s < QS; ++s) acc[s] = f32x16{};
 #pragma unroll
             for (int c = 0; c < NS; ++c) {
                 bf16x8 kp[3];
@@ -721,10 +743,13 @@ __global__ __launch_bounds__(BQ * 2) void pama_kernel(const T *__restrict__ q, S
                     for (int qa = 0; qa < NQ; ++qa) {
                         const int kb_ = ord - qa;
                         if (kb_ < 0 || kb_ > 2) continue;
-                        if constexpr (kSwap)
-                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[c][qa], kp[kb_], acc, 0, 0, 0);
-                        else
-                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kp[kb_], qf[c][qa], acc, 0, 0, 0);
+#pragma unroll
+                        for (int s = 0; s < QS; ++s) {
+                            if constexpr (kSwap)
+                                acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s][c][qa], kp[kb_], acc[s], 0, 0, 0);
+                            else
+                                acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kp[kb_], qf[s][c][qa], acc[s], 0, 0, 0);
+                        }
                     }
                 }
             }
@@ -733,75 +758,104 @@ __global__ __launch_bounds__(BQ * 2) void pama_kernel(const T *__restrict__ q, S
         }
     };
 
-    // pass 1: per lane, running max and sum of 2^logit over its key blocks, for query l32
-    float m = -INFINITY, z = 0.f;
-    pass(std::false_type{}, [&](int jt, const f32x16 &st) {
-        float x[16];
-        float mt = -INFINITY;
+    // pass 1: per lane and set, running max and sum of 2^logit over its key blocks
+    float m[QS], z[QS];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int J = jt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            x[r] = J < n ? st[r] * c2 : -INFINITY;
-            mt = fmaxf(mt, x[r]);
-        }
-        if (mt > -INFINITY) {
-            const float mn = fmaxf(m, mt);
-            float zt = 0.f;
+    for (int s = 0; s < QS; ++s) m[s] = -INFINITY, z[s] = 0.f;
+    pass(std::false_type{}, [&](int jt, const f32x16 (&acc)[QS]) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) zt += __builtin_amdgcn_exp2f(x[r] - mn);
-            z = z * __builtin_amdgcn_exp2f(m - mn) + zt;       // m = -inf: z = 0
-            m = mn;
+        for (int s = 0; s < QS; ++s) {
+            float x[16];
+            float mt = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int J = jt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                x[r] = J < n ? acc[s][r] * c2 : -INFINITY;
+                mt = fmaxf(mt, x[r]);
+            }
+            if (mt > -INFINITY) {
+                const float mn = fmaxf(m[s], mt);
+                float zt = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) zt += __builtin_amdgcn_exp2f(x[r] - mn);
+                z[s] = z[s] * __builtin_amdgcn_exp2f(m[s] - mn) + zt;       // m = -inf: z = 0
+                m[s] = mn;
+            }
         }
     });
-    {
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
         // combine the two lanes of each query: c = log2 of its normaliser
-        const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-        const auto pz = __builtin_amdgcn_permlane32_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+        const auto pm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m[s]), __float_as_uint(m[s]), false, false);
+        const auto pz = __builtin_amdgcn_permlane32_swap(__float_as_uint(z[s]), __float_as_uint(z[s]), false, false);
         const float m0 = __uint_as_float(pm[0]), m1 = __uint_as_float(pm[1]);
         const float z0 = __uint_as_float(pz[0]), z1 = __uint_as_float(pz[1]);
         const float M = fmaxf(m0, m1);
         const float Z = (m0 > -INFINITY ? z0 * __builtin_amdgcn_exp2f(m0 - M) : 0.f) +
                         (m1 > -INFINITY ? z1 * __builtin_amdgcn_exp2f(m1 - M) : 0.f);
-        if (h == 0) cq[wave * 32 + l32] = row_ok ? M + __builtin_amdgcn_logf(Z) : INFINITY;
+        const bool ok = (wave % WPB) * QW + s * 32 + l32 < m_w;
+        if (h == 0) cq[wave * QW + s * 32 + l32] = ok ? M + __builtin_amdgcn_logf(Z) : INFINITY;
     }
     __syncthreads();
     // pass 2: normalised weights of each key block summed over the wave's queries
-    float cr[16];
+    float cr[QS][16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) cr[r] = cq[wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
-    pass(std::true_type{}, [&](int jt, const f32x16 &st) {
+    for (int s = 0; s < QS; ++s)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cr[s][r] = cq[wave * QW + s * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
+    pass(std::true_type{}, [&](int jt, const f32x16 (&acc)[QS]) {
         float w = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) w += __builtin_amdgcn_exp2f(st[r] * c2 - cr[r]);   // invalid rows: 0
+        for (int s = 0; s < QS; ++s)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) w += __builtin_amdgcn_exp2f(acc[s][r] * c2 - cr[s][r]);   // invalid rows: 0
         const auto pw = __builtin_amdgcn_permlane32_swap(__float_as_uint(w), __float_as_uint(w), false, false);
         const float ws = __uint_as_float(pw[0]) + __uint_as_float(pw[1]);
         const int J = jt * 32 + l32;
         if (h == 0 && J < n) part[wave * n + J] = ws;
     });
     __syncthreads();
-    const float inv_m = 1.f / (float)m_I;
-    for (int J = threadIdx.x; J < n; J += BQ * 2) {
-        float A = 0.f;
+    for (int b = 0; b < NB; ++b) {
+        const int I = I0 + b;
+        if (I >= a.n_qb) break;
+        const float inv_m = 1.f / (float)min(a.block_q, a.N - I * a.block_q);
+        for (int J = threadIdx.x; J < n; J += kPamaThreads) {
+            float A = 0.f;
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) A += part[w * n + J];
-        A *= inv_m;
-        row[J] = A > 0.f ? fast_log(A) : -1e30f;     // an underflowed importance stays a real, finite score
+            for (int w = 0; w < WPB; ++w) A += part[(b * WPB + w) * n + J];
+            A *= inv_m;
+            rows[b * n + J] = A > 0.f ? fast_log(A) : -1e30f;     // an underflowed importance stays a real, finite score
+        }
     }
     __syncthreads();
-    if (wave == 0) {
-        if constexpr (R > 0) select_row<R>(row, bh, I, a);
-        else select_row_lds(row, bh, I, a);
+    if (wave < NB && I0 + wave < a.n_qb) {
+        if constexpr (R > 0) select_row<R>(rows + wave * n, bh, I0 + wave, a);
+        else select_row_lds(rows + wave * n, bh, I0 + wave, a);
     }
 }
 
-size_t pama_lds_bytes(int n_kb, int BQ) {
-    const size_t stage = BQ == 128 ? PamaStage<128, 128>::BYTES : PamaStage<128, 64>::BYTES;   // d = 128 bound
-    return stage + ((size_t)(BQ / 32 + 1) * n_kb + BQ) * sizeof(float);
+template <typename T, int BQ>
+static size_t pama_lds_bytes_t(int n_kb) {
+    constexpr int NB = PamaShape<T>::QWG / BQ;
+    return PamaStage<128>::BYTES + ((size_t)(kPamaThreads / kWave + NB) * n_kb + PamaShape<T>::QWG) * sizeof(float);
+}
+
+// d = 128 bound (the staging tile of d = 64 is smaller)
+size_t pama_lds_bytes(int n_kb, int BQ, int dtype) {
+    if (dtype == SA_BF16) return BQ == 128 ? pama_lds_bytes_t<bf16, 128>(n_kb) : pama_lds_bytes_t<bf16, 64>(n_kb);
+    return BQ == 128 ? pama_lds_bytes_t<float, 128>(n_kb) : pama_lds_bytes_t<float, 64>(n_kb);
 }
 
 template <typename T, int D, int BQ, int R>
 static hipError_t launch_pama_t(const void *q, const SelectArgs &a, int BH, hipStream_t st) {
-    hipLaunchKernelGGL((pama_kernel<T, D, BQ, R>), dim3(a.n_qb * BH), dim3(BQ * 2), pama_lds_bytes(a.n_kb, BQ), st,
+    constexpr int NB = PamaShape<T>::QWG / BQ;
+    const size_t lds = pama_lds_bytes_t<T, BQ>(a.n_kb);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)pama_kernel<T, D, BQ, R>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((pama_kernel<T, D, BQ, R>), dim3((a.n_qb + NB - 1) / NB * BH), dim3(kPamaThreads), lds, st,
                        (const T *)q, a);
     return hipGetLastError();
 }

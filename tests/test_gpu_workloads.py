@@ -59,6 +59,22 @@ def test_wan13b_full_pama(mode):
     check_workload(w, [cfg], heads=[(0, h) for h in range(w.H)])
 
 
+def test_wan14b_pama():
+    """PAMA on the full Wan-14B shape in the benchmark's setting (TOPP at tau 0.1,
+    cap of 295 blocks): 1182 key blocks per row, two query blocks per workgroup."""
+    w = S.WORKLOADS["wan14b"]
+    cfg = cfg_for(w, mode=R.TOPP, tau=0.1, proxy=R.PAMA)
+    check_workload(w, [cfg], [(0, 0), (0, 39)], blocks_per_head=3)
+
+
+def test_pama_rows_past_64k_of_lds():
+    """PAMA with 1700 key blocks per row (block_k = 64): its workgroup takes
+    more than 64 KB of LDS, which the launch must request explicitly."""
+    w = S.small("pama_1700", 1, 1, 128, (17, 80, 80), 128, 64, 0.1, qscale=6.0)
+    cfg = cfg_for(w, mode=R.TOPP, tau=0.1, proxy=R.PAMA)
+    check_workload(w, [cfg], [(0, 0)], blocks_per_head=3)
+
+
 def test_wan13b_full_fused():
     """Fused routing (decisions inside the forward) on the full Wan-1.3B shape."""
     w = S.WORKLOADS["wan1.3b"]
