@@ -84,6 +84,18 @@ def test_fused_floor_free_configurations_accepted():
         assert B.lib.sparse_attn_kv_idx_cap(ctypes.byref(params(**kw))) > 0, kw
 
 
+@pytest.mark.parametrize("block_q,dtype,n_max", [(64, 0, 3248), (128, 0, 4330), (64, 1, 4352), (128, 1, 5222)])
+def test_pama_key_block_limit(block_q, dtype, n_max):
+    """The PAMA workgroup keeps per-wave partial rows, the group's ln A rows and
+    the queries' normalisers beside a 26 KB staging tile in at most 128 KB of
+    LDS: the largest n_kb is accepted, one more is rejected before any launch."""
+    ok = params(flags=2, block_q=block_q, block_k=64, dtype=dtype, N=n_max * 64)
+    assert B.lib.sparse_attn_kv_idx_cap(ctypes.byref(ok)) > 0, B.lib.sparse_attn_last_error().decode()
+    over = params(flags=2, block_q=block_q, block_k=64, dtype=dtype, N=(n_max + 1) * 64)
+    assert B.lib.sparse_attn_kv_idx_cap(ctypes.byref(over)) == B.SA_ERR_UNSUPPORTED
+    assert "PAMA" in B.lib.sparse_attn_last_error().decode()
+
+
 @pytest.mark.parametrize("per,rank,ridge,flags,status", [
     (0, 4, 1e-3, 0, B.SA_ERR_INVALID_ARG), (17, 4, 1e-3, 0, B.SA_ERR_INVALID_ARG),
     (2, 0, 1e-3, 0, B.SA_ERR_INVALID_ARG), (2, 17, 1e-3, 0, B.SA_ERR_INVALID_ARG),
