@@ -617,13 +617,14 @@ template <> struct Store4<float> {
 // groups of four, group g of thread p at columns 4 (p + 4 g) .. (the four
 // threads of a row read 64 contiguous bytes per load; the k partial sums of y
 // meet by lane swaps).  HBM-bound: one read of O_s and one write of O.
-template <typename T, int D>
+// G4: groups of four rank columns, (k + 3) / 4.
+template <typename T, int D, int G4>
 __global__ __launch_bounds__(kPrThreads) void pr_apply_kernel(T *__restrict__ o, PrArgs a) {
     constexpr int TPR = 4;                    // threads per row
     constexpr int CPT = D / TPR;              // columns per thread
     constexpr int RPB = kPrThreads / TPR;     // rows per workgroup
     const int bh = blockIdx.y;
-    const int K = a.rank, KP = (K + 3) & ~3;
+    constexpr int KP = 4 * G4;
     __shared__ __attribute__((aligned(16))) float Ws[D * kPrMaxRank];
     __shared__ __attribute__((aligned(16))) float Qs[D * kPrMaxRank];
     __shared__ float Cbs[D];
@@ -653,26 +654,22 @@ __global__ __launch_bounds__(kPrThreads) void pr_apply_kernel(T *__restrict__ o,
 #pragma unroll
         for (int w = 0; w < 4; ++w) x[q + w] = v[w];
     }
-    // W and Q rows in groups of four (KP is a multiple of 4; columns past K are zero)
-    const int G4 = KP / 4;
-    f32x4 y[kPrMaxRank / 4];
+    // W and Q rows in groups of four (KP = 4 G4; columns past K are zero)
+    f32x4 y[G4];
 #pragma unroll
-    for (int g = 0; g < kPrMaxRank / 4; ++g) y[g] = f32x4{};
+    for (int g = 0; g < G4; ++g) y[g] = f32x4{};
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
         const f32x4 *wr = reinterpret_cast<const f32x4 *>(Ws + col(c) * KP);
 #pragma unroll
-        for (int g = 0; g < kPrMaxRank / 4; ++g)
-            if (g < G4) y[g] += x[c] * wr[g];
+        for (int g = 0; g < G4; ++g) y[g] += x[c] * wr[g];
     }
 #pragma unroll
-    for (int g = 0; g < kPrMaxRank / 4; ++g) {
-        if (g < G4) {
+    for (int g = 0; g < G4; ++g) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                y[g][u] += __shfl_xor(y[g][u], 1, kWave);
-                y[g][u] += __shfl_xor(y[g][u], 2, kWave);
-            }
+        for (int u = 0; u < 4; ++u) {
+            y[g][u] += __shfl_xor(y[g][u], 1, kWave);
+            y[g][u] += __shfl_xor(y[g][u], 2, kWave);
         }
     }
     // probed rows take their dense values (the rows of a workgroup meet at most
@@ -694,8 +691,7 @@ __global__ __launch_bounds__(kPrThreads) void pr_apply_kernel(T *__restrict__ o,
             const f32x4 *qr = reinterpret_cast<const f32x4 *>(Qs + col(c) * KP);
             f32x4 t = f32x4{};
 #pragma unroll
-            for (int g = 0; g < kPrMaxRank / 4; ++g)
-                if (g < G4) t += y[g] * qr[g];
+            for (int g = 0; g < G4; ++g) t += y[g] * qr[g];
             out[c] = x[c] + Cbs[col(c)] + ((t[0] + t[1]) + (t[2] + t[3]));
         }
     }
@@ -755,10 +751,19 @@ static hipError_t launch_pr_d(int dtype, const void *q, void *qp, void *o, const
         hipLaunchKernelGGL(pr_merge_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(kPrThreads), 0, st, a, rows);
     } else {
         dim3 grid((a.N + kPrThreads / 4 - 1) / (kPrThreads / 4), BH);
-        if (dtype == SA_BF16)
-            hipLaunchKernelGGL((pr_apply_kernel<bf16, D>), grid, dim3(kPrThreads), 0, st, (bf16 *)o, a);
-        else
-            hipLaunchKernelGGL((pr_apply_kernel<float, D>), grid, dim3(kPrThreads), 0, st, (float *)o, a);
+        auto go = [&](auto g4) {
+            constexpr int G4 = decltype(g4)::value;
+            if (dtype == SA_BF16)
+                hipLaunchKernelGGL((pr_apply_kernel<bf16, D, G4>), grid, dim3(kPrThreads), 0, st, (bf16 *)o, a);
+            else
+                hipLaunchKernelGGL((pr_apply_kernel<float, D, G4>), grid, dim3(kPrThreads), 0, st, (float *)o, a);
+        };
+        switch ((a.rank + 3) / 4) {       // the rank is 1 .. 16
+            case 1: go(std::integral_constant<int, 1>{}); break;
+            case 2: go(std::integral_constant<int, 2>{}); break;
+            case 3: go(std::integral_constant<int, 3>{}); break;
+            default: go(std::integral_constant<int, 4>{}); break;
+        }
     }
     return hipGetLastError();
 }
