@@ -53,9 +53,11 @@ struct FC {
 // Waves per SIMD the register budget targets.  bf16, 128-row workgroups: three
 // share a CU (48 KB of LDS each: K double-buffered, V single-buffered).  fp32
 // rows need more registers: two 128-row workgroups (64 KB of LDS each).  A
-// 64-row workgroup (2 waves) gets the full register file.
+// 64-row workgroup (2 waves): two waves per SIMD for bf16, so that the three
+// workgroups the LDS admits can share a CU (with the whole register file one
+// wave per SIMD left room for two); fp32 rows keep the whole file.
 template <typename T, int BQ>
-constexpr int kWavesPerEU = BQ == 128 ? (sizeof(T) == 2 ? 3 : 2) : 1;
+constexpr int kWavesPerEU = BQ == 128 ? (sizeof(T) == 2 ? 3 : 2) : (sizeof(T) == 2 ? 2 : 1);
 
 // chunk position = logical chunk ^ swizzle(row)
 template <int D> __device__ __forceinline__ int swz_k(int r) { return r & (D / 8 - 1); }
