@@ -6,12 +6,19 @@ select, schedule) followed by the sparse forward with the dropped-block
 residual.  Inputs are seeded synthetic Q/K/V with the token-grid shape of the
 workload, resident in HBM before the timed region.
 
-    python bench.py [--steps K] [--warmup W] [--workload wan1.3b] [--tau-mode relative]
+    python bench.py [--steps K] [--warmup W] [--workload stress] [--tau-mode relative]
+
+The default workload is the largest single-GPU layer shape: the stress case,
+B = 2, H = 24, N = 118800 (a 33 x 45 x 80 token grid), d = 128, bf16, 128 x 128
+blocks, tau = 0.05 relative, per-head query scales drawn from [1, 12].
 
 Prints one JSON line.  value = dense-equivalent TFLOP/s = 4 B H N^2 d / step
 time.  roofline: the forward kernel's algorithmic flops per launch (exact
 kept tiles + one residual column per dropped block) over its average launch
 time measured with HIP events on its stream, against the bf16 dense MFMA peak.
+route: the routing kernels' algorithmic bytes (q, k, v read once; pooled key
+and value means written in fp32 and bf16; kept-block indices and the bit mask
+written) over their time, against the HBM peak.
 cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
 workload and extrapolated in executed query-key pairs.
 """
@@ -38,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="wan1.3b")
+    ap.add_argument("--workload", default="stress")
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--tau-mode", choices=("relative", "absolute", "topp"), default="relative")
     ap.add_argument("--sparsepr", type=int, default=0, metavar="P",
@@ -57,7 +64,19 @@ def parse():
                     help="write profiles/flash_<workload>_<tau-mode>_traffic.{json,md} from the counter "
                          "collections of two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of this "
                          "script with --with-copy, then exit")
+    ap.add_argument("--mfma-summary", metavar="CSV",
+                    help="write profiles/flash_<workload>_<tau-mode>_mfma.{json,md} from the counter collection "
+                         "of a rocprofv3 --pmc run of this script (SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+                         "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE) and its kernel trace "
+                         "(KERNEL_TRACE_CSV, for the durations), then exit")
+    ap.add_argument("--trace-csv", metavar="KERNEL_TRACE_CSV", help="kernel trace of the --mfma-summary run")
+    ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
+                    help="write profiles/flash_<workload>_<tau-mode>_kernel_stats.md from the kernel_stats.csv of a "
+                         "rocprofv3 --kernel-trace --stats run of this script (the library's kernels under the "
+                         "profiler's own names), then exit")
     ap.add_argument("--pmc-command", default="", help="the command the counter runs used (recorded)")
+    ap.add_argument("--no-residual-timing", action="store_true",
+                    help="skip timing the forward without the residual fold (its share of the forward)")
     ap.add_argument("--cold-calls", type=int, default=20,
                     help="calls timed one by one after flushing the caches with a 512 MiB write (0: skip)")
     return ap.parse_args()
@@ -134,6 +153,15 @@ def pmc_summary(args):
            "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
            "copy_fetch_kib": copy_f, "copy_write_kib": copy_w, "fetch_scale": scale_f, "write_scale": scale_w,
            "command": args.pmc_command}
+    # every kernel of the run, by the same scales (the routing kernels among them)
+    per_kernel = []
+    for name in sorted({r["Kernel_Name"] for r in fetch_rows} | {r["Kernel_Name"] for r in write_rows}):
+        fk, n1 = _mean_kib(fetch_rows, lambda r, n=name: r["Kernel_Name"] == n)
+        wk, n2 = _mean_kib(write_rows, lambda r, n=name: r["Kernel_Name"] == n)
+        per_kernel.append({"kernel": _short_kernel(name), "kernel_name": name, "dispatches": [n1, n2],
+                           "read_bytes_per_launch": None if fk is None else fk * 1024.0 * scale_f,
+                           "write_bytes_per_launch": None if wk is None else wk * 1024.0 * scale_w})
+    rec["all_kernels"] = per_kernel
     base = os.path.join(ROOT, "profiles", f"flash_{args.workload}_{args.tau_mode}_traffic")
     with open(base + ".json", "w") as f:
         json.dump(rec, f, indent=1)
@@ -150,7 +178,135 @@ def pmc_summary(args):
         f.write(f"| read bytes per launch (scaled) | {rd / 1e9:.3f} GB |\n")
         f.write(f"| written bytes per launch (scaled) | {wr / 1e9:.3f} GB |\n")
         f.write(f"| kernel source sha256[:16] | {rec['flash_source_sha256_16']} |\n")
+        f.write("\nEvery kernel of the run, by the same scales (bytes per launch):\n\n")
+        f.write("| kernel | dispatches | read MB | written MB |\n|---|---|---|---|\n")
+        mb = lambda x: "-" if x is None else f"{x / 1e6:,.1f}"
+        for r in per_kernel:
+            f.write(f"| {r['kernel']} | {r['dispatches'][0]} | {mb(r['read_bytes_per_launch'])} | "
+                    f"{mb(r['write_bytes_per_launch'])} |\n")
     print(json.dumps(rec))
+
+
+def _short_kernel(name: str) -> str:
+    """Readable label of a rocprof kernel name (the full name is kept beside it)."""
+    if "flash_kernel" in name:
+        dt = "bf16" if "DF16b" in name else "f32"
+        kind = "fused" if "Lb1ELb1E" in name else ("sparse" if "Lb1ELb0E" in name else "dense")
+        return f"flash_kernel {dt} {kind}"
+    for k in ("pool_kernel", "select_kernel", "order_kernel", "pama_kernel", "permute_kernel"):
+        if k in name:
+            return k
+    return name[:60]
+
+
+def mfma_summary(args):
+    """Matrix-core counters per kernel from one rocprofv3 --pmc pass
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES,
+    GRBM_GUI_ACTIVE) with the kernel trace of the same run (durations):
+      MFMA flops per launch = MOPS_BF16 x 512 (the counter's unit),
+      MFMA busy = sum of SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs),
+      shader clock = GRBM_GUI_ACTIVE / kernel duration."""
+    import csv
+    rows = list(csv.DictReader(open(args.mfma_summary)))
+    # the profiler reports GRBM_GUI_ACTIVE summed over the dies (one GRBM each)
+    # and SQ counters summed over every SIMD; the agent table gives both counts
+    n_xcc, simds = 8, 256 * 4
+    info = os.path.join(os.path.dirname(args.mfma_summary), os.path.basename(args.mfma_summary).replace(
+        "counter_collection", "agent_info"))
+    if os.path.exists(info):
+        for r in csv.DictReader(open(info)):
+            if r.get("Name", "").startswith("gfx"):
+                n_xcc, simds = int(r["Num_Xcc"]), int(r["Simd_Count"])
+    dur = {}
+    if args.trace_csv:
+        for r in csv.DictReader(open(args.trace_csv)):
+            dur[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    per = {}
+    for r in rows:
+        d = per.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    kernels = {}
+    for did, d in per.items():
+        k = kernels.setdefault(d["name"], [])
+        d["dur_s"] = dur.get(did)
+        k.append(d)
+    out = []
+    for name, ds in kernels.items():
+        mean = lambda key: sum(x.get(key, 0.0) for x in ds) / len(ds)
+        flops = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512.0
+        grbm = mean("GRBM_GUI_ACTIVE") / n_xcc        # busy cycles of the GPU clock
+        busy = mean("SQ_VALU_MFMA_BUSY_CYCLES")
+        durs = [x["dur_s"] for x in ds if x["dur_s"]]
+        t = sum(durs) / len(durs) if durs else None
+        rec = {"kernel": _short_kernel(name), "kernel_name": name, "dispatches": len(ds),
+               "mfma_bf16_flops_per_launch": flops, "mfma_busy_frac": busy / (grbm * simds) if grbm else None,
+               "grbm_gui_active": grbm, "sq_busy_cycles": mean("SQ_BUSY_CYCLES"),
+               "avg_duration_ms": t * 1e3 if t else None,
+               "clock_ghz": grbm / t / 1e9 if t and grbm else None,
+               "mfma_bf16_tflops": flops / t / 1e12 if t else None,
+               "mfma_bf16_frac_of_peak": flops / t / 1e12 / PEAK_BF16_TFLOPS if t else None}
+        out.append(rec)
+    out.sort(key=lambda r: -(r["avg_duration_ms"] or 0) * r["dispatches"])
+    rec = {"workload": args.workload, "tau_mode": args.tau_mode, "flash_source_sha256_16": source_hash(),
+           "kernels": out, "command": args.pmc_command}
+    base = os.path.join(ROOT, "profiles", f"flash_{args.workload}_{args.tau_mode}_mfma")
+    with open(base + ".json", "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    with open(base + ".md", "w") as f:
+        f.write(f"# Matrix-core counters: {args.workload}, {args.tau_mode} tau\n\n")
+        f.write("One rocprofv3 counter pass with the kernel trace (durations), then the summary:\n\n")
+        f.write(f"    {args.pmc_command}\n\n")
+        f.write("MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; GPU cycles = GRBM_GUI_ACTIVE / 8 (the "
+                "profiler sums it over the 8 dies); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GPU cycles x 1024 "
+                "SIMDs); clock = GPU cycles / duration (the kernel runs alone under counter collection).\n\n")
+        f.write("| kernel | dispatches | avg ms | MFMA bf16 GFLOP per launch | MFMA TFLOP/s | frac of 2500 | "
+                "MFMA busy | clock GHz |\n|---|---|---|---|---|---|---|---|\n")
+        fmt = lambda x, spec: "-" if x is None else format(x, spec)
+        for r in out:
+            f.write(f"| {r['kernel']} | {r['dispatches']} | {fmt(r['avg_duration_ms'], '.3f')} | "
+                    f"{r['mfma_bf16_flops_per_launch'] / 1e9:,.1f} | {fmt(r['mfma_bf16_tflops'], ',.0f')} | "
+                    f"{fmt(r['mfma_bf16_frac_of_peak'], '.3f')} | {fmt(r['mfma_busy_frac'], '.3f')} | "
+                    f"{fmt(r['clock_ghz'], '.2f')} |\n")
+        f.write(f"\nKernel source sha256[:16] (sa_flash.hip): {rec['flash_source_sha256_16']}\n")
+    print(json.dumps(rec))
+
+
+def stats_summary(args):
+    """The library's kernels from a rocprofv3 --kernel-trace --stats table, under
+    the names the profiler prints."""
+    import csv
+    rows = [r for r in csv.DictReader(open(args.stats_summary))
+            if any(k in r["Name"] for k in ("flash_kernel", "pool_kernel", "select_kernel", "order_kernel",
+                                             "pama_kernel", "permute_kernel", "pr_", "probe_gather"))]
+    path = os.path.join(ROOT, "profiles", f"flash_{args.workload}_{args.tau_mode}_kernel_stats.md")
+    with open(path, "w") as f:
+        f.write(f"# Kernel times: {args.workload}, {args.tau_mode} tau\n\n")
+        f.write("rocprofv3 kernel trace with per-kernel statistics (kernel_stats.csv, the library's rows):\n\n")
+        f.write(f"    {args.pmc_command}\n\n")
+        f.write("| kernel (as rocprofv3 names it) | calls | avg us | min us | max us | % of GPU time |\n"
+                "|---|---|---|---|---|---|\n")
+        for r in rows:
+            f.write(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:,.1f} | "
+                    f"{float(r['MinNs']) / 1e3:,.1f} | {float(r['MaxNs']) / 1e3:,.1f} | {float(r['Percentage']):.2f} |\n")
+        f.write(f"\nKernel source sha256[:16] (sa_flash.hip): {source_hash()}\n")
+    print(path)
+
+
+def load_mfma(workload: str, tau_mode: str):
+    """The sparse forward's matrix-core counters from the committed summary, if taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"flash_{workload}_{tau_mode}_mfma.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("flash_source_sha256_16") != source_hash():
+        return None
+    for r in rec["kernels"]:
+        if r["kernel"].startswith("flash_kernel") and r["kernel"].endswith("sparse"):
+            return {k: r[k] for k in ("mfma_bf16_flops_per_launch", "mfma_busy_frac", "clock_ghz",
+                                      "mfma_bf16_frac_of_peak", "avg_duration_ms")}
+    return None
 
 
 def cpu_baseline(w, cfg, Qc, Kc, Vc, budget_s: float = 12.0):
@@ -336,6 +492,12 @@ def main():
     if args.pmc_summary:
         pmc_summary(args)
         return
+    if args.mfma_summary:
+        mfma_summary(args)
+        return
+    if args.stats_summary:
+        stats_summary(args)
+        return
 
     import torch
 
@@ -393,8 +555,35 @@ def main():
     fwd_tflops = (exact_flops + resid_flops) / (fwd_ms * 1e-3) / 1e12
 
     es = 2 if w.dtype == "bf16" else 4
-    route_bytes = 3.0 * w.B * w.H * w.N * w.d * es
+    words = -(-rt.n_kb // 32)
+    route_read = 3.0 * w.B * w.H * w.N * w.d * es
+    route_written = (2.0 * w.B * w.H * rt.n_kb * w.d * (4 + 2)       # key and value means, fp32 and bf16
+                     + 4.0 * float(mask.sum())                       # kept-block indices
+                     + 4.0 * w.B * w.H * rt.n_qb * words)            # bit mask
+    route_bytes = route_read + route_written
     route_gbs = route_bytes / (route_ms * 1e-3) / 1e9
+
+    # the forward without the residual fold, on the same route: the residual's share
+    noresid = None
+    if not args.no_residual_timing:
+        import dataclasses
+        cfg_nr = dataclasses.replace(cfg, no_residual=True)
+        On = torch.empty_like(O)
+        sa.forward(Q, K, V, rt, cfg_nr, out=On)
+        ts = []
+        for _ in range(max(3, args.steps // 2)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            sa.forward(Q, K, V, rt, cfg_nr, out=On)
+            e1.record()
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        nr_ms = median([a.elapsed_time(b) for a, b in ts])
+        del On
+        noresid = {"forward_ms_median": nr_ms, "forward_with_residual_ms_median": warm["forward_ms_median"],
+                   "residual_share_of_forward": 1.0 - nr_ms / warm["forward_ms_median"],
+                   "exact_tflops": exact_flops / (nr_ms * 1e-3) / 1e12,
+                   "exact_frac_of_peak": exact_flops / (nr_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
     dense_ms = None
     if not args.no_dense:
@@ -431,12 +620,17 @@ def main():
                      "frac": fwd_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "kernel": "flash_kernel (sparse forward with residual)",
                      "flops_per_launch": exact_flops + resid_flops, "avg_launch_ms": fwd_ms},
-        "route": {"ms": route_ms, "bytes_read": route_bytes, "GB/s": route_gbs,
-                  "frac_hbm": route_gbs / PEAK_HBM_GBS},
+        "route": {"ms": route_ms, "bytes": route_bytes, "bytes_read": route_read, "bytes_written": route_written,
+                  "GB/s": route_gbs, "frac_hbm": route_gbs / PEAK_HBM_GBS},
         "forward_ms": fwd_ms,
         "dense_ms": dense_ms,
         "speedup_vs_dense": (dense_ms / (route_ms + fwd_ms)) if dense_ms else None,
         "inverse_kept_fraction": 1.0 / kept_frac,
+        # 1 / (kept + residual share of the dense flops): the speedup the algorithmic work allows
+        "inverse_algorithmic_fraction": dense_flops / (exact_flops + resid_flops),
+        "residual_flops_per_forward": resid_flops,
+        "no_residual": noresid,
+        "mfma_counters": load_mfma(w.name, args.tau_mode),
         "issued_mfma_flops_per_forward": issued,
         "issued_mfma_frac": issued / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "timing_warm": warm,

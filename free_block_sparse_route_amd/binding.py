@@ -138,6 +138,30 @@ def kv_idx_cap(p: SaParams) -> int:
     return c
 
 
+# sa_params fields a route is built for.  A forward must use the route with the
+# same values (the header's contract); only SA_FLAG_NO_RESIDUAL, a forward-only
+# switch, may differ.
+_ROUTE_FIELDS = ("B", "H", "N", "d", "block_q", "block_k", "tau", "tau_mode", "max_keep", "min_keep",
+                 "n_dense_prefix", "scale", "dtype")
+_SHAPE_FIELDS = ("B", "H", "N", "d", "block_q", "block_k", "dtype")
+
+
+def _params_diff(a: SaParams, b: SaParams, fields) -> list:
+    diff = [f"{f} {getattr(a, f)} != {getattr(b, f)}" for f in fields if getattr(a, f) != getattr(b, f)]
+    fa, fb = a.flags & ~FLAG_NO_RESIDUAL, b.flags & ~FLAG_NO_RESIDUAL
+    if fa != fb:
+        diff.append(f"routing flags 0x{fa:x} != 0x{fb:x}")
+    return diff
+
+
+def _check_out(name: str, t: torch.Tensor, like: torch.Tensor, dtype=None):
+    """An out= tensor: same device and shape as `like`, contiguous, of `like`'s dtype (or `dtype`)."""
+    want = like.dtype if dtype is None else dtype
+    if not isinstance(t, torch.Tensor) or t.device != like.device or tuple(t.shape) != tuple(like.shape) \
+            or t.dtype != want or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {want} tensor of shape {tuple(like.shape)} on {like.device}")
+
+
 def route_sizes(p: SaParams, cap: int) -> list:
     arr = (ctypes.c_size_t * len(BUFFERS))()
     _check(lib.sparse_attn_route_sizes(ctypes.byref(p), cap, arr))
@@ -172,6 +196,14 @@ class Route:
                 raise RuntimeError(f"route buffer {name}: {t.numel() * t.element_size()} bytes, library wants {nbytes}")
         self.c = SaRoute(*[getattr(self, n).data_ptr() for n in BUFFERS], self.cap)
 
+    def check(self, p: SaParams, who: str, fields=_ROUTE_FIELDS):
+        """ValueError unless this route was built for p (before anything is enqueued)."""
+        diff = _params_diff(self.params, p, fields)
+        if diff:
+            raise ValueError(f"{who}: the route was built for other parameters ({'; '.join(diff)})")
+        if self.cap < kv_idx_cap(p):
+            raise ValueError(f"{who}: route kv_idx capacity {self.cap} < {kv_idx_cap(p)} needed")
+
     def mask(self) -> torch.Tensor:
         """Keep mask as bool [B, H, n_qb, n_kb] (unpacked from the bit words, on device)."""
         w = self.kv_mask.to(torch.int64) & 0xFFFFFFFF
@@ -184,7 +216,13 @@ def route(q, k, v, cfg: Config, out: Route | None = None) -> Route:
     """sparse_attn_route: block routing; returns the route buffers."""
     _check_qkv(q, k, v)
     p = make_params(q, cfg)
+    if out is not None:
+        # reusable for new routing fields (tau, budget, mode) at the same shapes
+        out.check(p, "route(out=...)", _SHAPE_FIELDS)
+        if out.kv_count.device != q.device:
+            raise ValueError("route(out=...): the route's buffers are on another device")
     rt = out if out is not None else Route(p, q.device)
+    rt.params = SaParams.from_buffer_copy(p)
     _check(lib.sparse_attn_route(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(rt.c),
                                  _stream(q.device)))
     return rt
@@ -194,6 +232,9 @@ def forward(q, k, v, rt: Route, cfg: Config, out: torch.Tensor | None = None, ls
     """sparse_attn_forward: exact kept tiles plus dropped-block residual. Returns o or (o, lse)."""
     _check_qkv(q, k, v)
     p = make_params(q, cfg)
+    rt.check(p, "forward")
+    if out is not None:
+        _check_out("out", out, q)
     o = out if out is not None else torch.empty_like(q)
     L = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse else None
     _check(lib.sparse_attn_forward(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(rt.c),
@@ -206,6 +247,8 @@ def dense_ref_gpu(q, k, v, block_q: int = 128, scale: float = 0.0, out: torch.Te
     """sparse_attn_dense_ref_gpu: dense softmax attention with the same kernels."""
     _check_qkv(q, k, v)
     p = make_params(q, Config(block_q=block_q, block_k=128, scale=scale))
+    if out is not None:
+        _check_out("out", out, q)
     o = out if out is not None else torch.empty_like(q)
     L = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse else None
     _check(lib.sparse_attn_dense_ref_gpu(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
@@ -228,7 +271,13 @@ def forward_sparsepr(q, k, v, rt: Route, cfg: Config, probes_per_block: int = 2,
     affine map fitted on exact probe rows (in place of the block residual)."""
     _check_qkv(q, k, v)
     p = make_params(q, cfg)
+    rt.check(p, "forward_sparsepr")
     n = sparsepr_workspace_size(q, cfg, probes_per_block)
+    if workspace is not None and (workspace.device != q.device or workspace.dtype != torch.uint8
+                                  or not workspace.is_contiguous() or workspace.numel() < n):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor of at least {n} bytes on {q.device}")
+    if out is not None:
+        _check_out("out", out, q)
     ws = workspace if workspace is not None else torch.empty(n, dtype=torch.uint8, device=q.device)
     o = out if out is not None else torch.empty_like(q)
     _check(lib.sparse_attn_forward_sparsepr(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),

@@ -69,17 +69,23 @@ sa_status check_params(const sa_params *p, bool routing) {
     if ((p->block_q != 64 && p->block_q != 128) || (p->block_k != 64 && p->block_k != 128))
         return fail(SA_ERR_UNSUPPORTED, "block sizes %d x %d (supported: 64 or 128 each)", p->block_q,
                     p->block_k);
+    // the attention kernels address one head's keys and values through a buffer
+    // resource whose byte range is 32 bits wide
+    const int64_t head_bytes = (int64_t)p->N * p->d * (p->dtype == SA_BF16 ? 2 : 4);
+    if (head_bytes > (int64_t)UINT32_MAX)
+        return fail(SA_ERR_UNSUPPORTED, "N * d * element size = %lld bytes per head exceeds 2^32 - 1",
+                    (long long)head_bytes);
     const Dims d = dims_of(p);
     if (routing && d.n_kb > sa::kMaxKeyBlocks)
         return fail(SA_ERR_UNSUPPORTED, "n_kb = %d exceeds %d", d.n_kb, sa::kMaxKeyBlocks);
     if (routing && (p->flags & SA_FLAG_FUSED)) {
         // the decision of a block depends only on its own proxy and the row's
-        // statistics: no cap, no ranking-based mode, no floor that can bind
+        // statistics (plus, for a floor of one block, the row's best block):
+        // no cap, no ranking-based mode, no floor above one block
         if (p->flags & SA_FLAG_PAMA) return fail(SA_ERR_UNSUPPORTED, "fused routing with the PAMA proxy");
         if (p->tau_mode == SA_TAU_TOPP) return fail(SA_ERR_UNSUPPORTED, "fused routing with SA_TAU_TOPP");
         if (p->max_keep != 0) return fail(SA_ERR_UNSUPPORTED, "fused routing with max_keep");
-        const bool floor_free = p->min_keep == 0 || (p->min_keep == 1 && p->tau_mode == SA_TAU_RELATIVE && p->tau <= 1.f);
-        if (!floor_free) return fail(SA_ERR_UNSUPPORTED, "fused routing with a min_keep floor that can bind");
+        if (p->min_keep > 1) return fail(SA_ERR_UNSUPPORTED, "fused routing with min_keep = %d (at most 1)", p->min_keep);
         if (d.words > sa::kFusedMaxWords) return fail(SA_ERR_UNSUPPORTED, "fused routing: n_kb = %d too large", d.n_kb);
     }
     if (routing && (p->flags & SA_FLAG_PAMA) && sa::pama_lds_bytes(d.n_kb, p->block_q, p->dtype) > sa::kPamaLdsBudget)
@@ -212,6 +218,7 @@ static sa_status run_flash(const sa_params *p, const void *q, const void *k, con
             fa.row_stats = r->row_stats;
             fa.tau_mode = p->tau_mode;
             fa.n_prefix = p->n_dense_prefix;
+            fa.min_keep = p->min_keep;
             fa.scale = (float)scale;
             fa.ln_tau = p->tau > 0.f ? (float)log((double)p->tau) : -INFINITY;
         }
@@ -298,7 +305,9 @@ struct PrLayout {
     size_t qp, od32, o32, scratch, part, cmean, cb_mat, cb_vec, osplit, lsplit, total;
     int M, n_chunks, kv_splits;
 };
-PrLayout pr_layout(const sa_params *p, int per_block) {
+// limit_bytes > 0: fewer key ranges for the probe pass (down to one) while the
+// workspace would exceed limit_bytes; the caller checks L.total against it.
+PrLayout pr_layout(const sa_params *p, int per_block, size_t limit_bytes = 0) {
     const Dims d = dims_of(p);
     const size_t es = p->dtype == SA_BF16 ? 2 : 4;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -326,11 +335,17 @@ PrLayout pr_layout(const sa_params *p, int per_block) {
         S = S < tiles / 8 ? S : tiles / 8;
         L.kv_splits = S > 1 ? (int)S : 1;
     }
-    L.osplit = off;
-    if (L.kv_splits > 1) off += up((size_t)L.kv_splits * BH * L.M * D * 4);
-    L.lsplit = off;
-    if (L.kv_splits > 1) off += up((size_t)L.kv_splits * BH * L.M * 4);
-    L.total = off;
+    const size_t fixed = off;
+    for (;;) {
+        off = fixed;
+        L.osplit = off;
+        if (L.kv_splits > 1) off += up((size_t)L.kv_splits * BH * L.M * D * 4);
+        L.lsplit = off;
+        if (L.kv_splits > 1) off += up((size_t)L.kv_splits * BH * L.M * 4);
+        L.total = off;
+        if (limit_bytes == 0 || L.total <= limit_bytes || L.kv_splits == 1) break;
+        --L.kv_splits;
+    }
     return L;
 }
 
@@ -356,14 +371,15 @@ sa_status sparse_attn_sparsepr_workspace_size(const sa_params *p, int32_t probes
     return SA_OK;
 }
 
-sa_status sparse_attn_forward_sparsepr(const sa_params *p, const void *q, const void *k, const void *v,
-                                       const sa_route *r, int32_t probes_per_block, int32_t rank, float ridge,
-                                       void *workspace, size_t workspace_bytes, void *o, void *stream) {
+namespace {
+// Argument checks of the probe-fitted residual entry points (the workspace aside).
+sa_status check_sparsepr_call(const sa_params *p, const void *q, const void *k, const void *v, const sa_route *r,
+                              int32_t probes_per_block, int32_t rank, float ridge, const void *o) {
     sa_status s = check_params(p, true);
     if (s != SA_OK) return s;
     if ((s = check_pr(p, probes_per_block, rank, ridge)) != SA_OK) return s;
     if ((s = check_ptr(q, "q")) || (s = check_ptr(k, "k")) || (s = check_ptr(v, "v")) ||
-        (s = check_ptr(o, "o")) || (s = check_host_ptr(r, "route")) || (s = check_ptr(workspace, "workspace")))
+        (s = check_ptr(o, "o")) || (s = check_host_ptr(r, "route")))
         return s;
     if ((s = check_ptr(r->kv_count, "route.kv_count")) || (s = check_ptr(r->kv_idx, "route.kv_idx")) ||
         (s = check_ptr(r->kv_mask, "route.kv_mask")) || (s = check_ptr(r->kv_split, "route.kv_split")) ||
@@ -371,9 +387,14 @@ sa_status sparse_attn_forward_sparsepr(const sa_params *p, const void *q, const 
         return s;
     if (r->kv_idx_cap < min_cap(p))
         return fail(SA_ERR_CAPACITY, "route.kv_idx_cap %d < required %d", r->kv_idx_cap, min_cap(p));
-    const PrLayout L = pr_layout(p, probes_per_block);
-    if (workspace_bytes < L.total)
-        return fail(SA_ERR_CAPACITY, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
+    return SA_OK;
+}
+
+// The probe-fitted residual's launches on a workspace laid out as L.
+sa_status run_sparsepr(const sa_params *p, const void *q, const void *k, const void *v, const sa_route *r,
+                       int32_t probes_per_block, int32_t rank, float ridge, const PrLayout &L, void *workspace,
+                       void *o, void *stream) {
+    sa_status s;
     const Dims d = dims_of(p);
     hipStream_t st = (hipStream_t)stream;
     unsigned char *ws = (unsigned char *)workspace;
@@ -424,6 +445,20 @@ sa_status sparse_attn_forward_sparsepr(const sa_params *p, const void *q, const 
     e = sa::launch_sparsepr_step(2, p->dtype, p->d, nullptr, nullptr, o, a, (int)d.BH, st);
     if (e != hipSuccess) return hip_fail(e, "sparsepr: apply launch");
     return SA_OK;
+}
+
+}  // namespace
+
+sa_status sparse_attn_forward_sparsepr(const sa_params *p, const void *q, const void *k, const void *v,
+                                       const sa_route *r, int32_t probes_per_block, int32_t rank, float ridge,
+                                       void *workspace, size_t workspace_bytes, void *o, void *stream) {
+    sa_status s = check_sparsepr_call(p, q, k, v, r, probes_per_block, rank, ridge, o);
+    if (s != SA_OK) return s;
+    if ((s = check_ptr(workspace, "workspace")) != SA_OK) return s;
+    const PrLayout L = pr_layout(p, probes_per_block);
+    if (workspace_bytes < L.total)
+        return fail(SA_ERR_CAPACITY, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
+    return run_sparsepr(p, q, k, v, r, probes_per_block, rank, ridge, L, workspace, o, stream);
 }
 
 const char *sparse_attn_status_string(sa_status s) {

@@ -94,9 +94,13 @@ struct TileStream {
     int J_cur, J_pf;          // kept blocks li and li + 1
     uint32_t w_cur, w_pf;     // mask words rt and rt + 1
 
-    __device__ void prime() {
-        J_cur = cnt > 0 ? list[0] : 0;
-        J_pf = cnt > 1 ? list[1] : 0;
+    // A list entry outside [0, n_kb) (a route that does not belong to this
+    // call) is clamped, so that no tile is read outside the head.
+    static __device__ __forceinline__ int clampJ(int J, int n_kb) { return min(max(J, 0), n_kb - 1); }
+
+    __device__ void prime(const FlashArgs &a) {
+        J_cur = cnt > 0 ? clampJ(list[0], a.n_kb) : 0;
+        J_pf = cnt > 1 ? clampJ(list[1], a.n_kb) : 0;
         w_cur = n_rt > 0 ? mask[0] : 0u;
         w_pf = n_rt > 1 ? mask[1] : 0u;
     }
@@ -121,7 +125,7 @@ struct TileStream {
                 ++li;
                 sub = 0;
                 J_cur = J_pf;
-                J_pf = list[min(li + 1, cnt - 1)];   // unconditional: the load lands in J_pf's register
+                J_pf = clampJ(list[min(li + 1, cnt - 1)], a.n_kb);   // unconditional: the load lands in J_pf's register
             }
             if (tok0 < b1) {
                 o.kind = exact_kind;
@@ -160,7 +164,7 @@ struct BitStream {
 
     __device__ uint32_t word(int w) const { return (uint32_t)__builtin_amdgcn_readfirstlane((int)lw[w]); }
 
-    __device__ void prime() {
+    __device__ void prime(const FlashArgs &) {
         wi = 0;
         sub = 0;
         rt = 0;
@@ -212,8 +216,11 @@ struct BitStream {
 // and log-sum-exp).  Every thread scores key blocks J = t, t + THREADS, ...:
 // s = scale * qbar_I . kbar_J in fp32 (the query mean through the scalar cache),
 // kept when s clears the threshold the route's row statistics give, or when
-// the dense prefix covers it.  Writes the words to LDS and to the route's mask,
-// the count to the route; returns the count (uniform).
+// the dense prefix covers it.  With a floor of one block (min_keep = 1) and no
+// block clearing the threshold, the block of largest s (lowest J among equal
+// ones) is kept as well: the first block of the ranking, as in the unfused
+// route.  Writes the words to LDS and to the route's mask, the count to the
+// route; returns the count (uniform).
 constexpr int kFusedWords = 512;           // n_kb <= 16368
 template <int D, int BQ>
 __device__ __forceinline__ int fused_route(int bh, int I, const FlashArgs &a, uint32_t *fw) {
@@ -225,6 +232,9 @@ __device__ __forceinline__ int fused_route(int bh, int I, const FlashArgs &a, ui
     const bool dense_row = (int64_t)I * a.block_q < a.n_prefix;
     const kconst<float> *qb = (const kconst<float> *)(a.q_mean + row * D);
     const float *kb = a.k_mean + (size_t)bh * n * D;
+    float best = -INFINITY;                // this thread's largest score and its block
+    int best_j = n;
+    int npass = 0;                         // blocks that clear the threshold
     for (int base = 0; base < n; base += C::THREADS) {
         const int J = base + (int)threadIdx.x;
         bool keep = false;
@@ -238,14 +248,51 @@ __device__ __forceinline__ int fused_route(int bh, int I, const FlashArgs &a, ui
                 for (int e = 0; e < 4; ++e) s4[e] = fmaf(qb[c + e], x[e], s4[e]);
             }
             const float sc = ((s4[0] + s4[1]) + (s4[2] + s4[3])) * a.scale;
-            keep = sc >= thr || dense_row || (int64_t)J * a.block_k < a.n_prefix;
+            const bool pass = sc >= thr;
+            npass += pass ? 1 : 0;
+            if (sc > best || best_j == n) {   // J rises along the loop: ties keep the lower J
+                best = sc;
+                best_j = J;
+            }
+            keep = pass || dense_row || (int64_t)J * a.block_k < a.n_prefix;
         }
         const uint64_t b = __ballot(keep);
         const int w = (base + wave * kWave) / 32;
         if (lane == 0 && w < words) fw[w] = (uint32_t)b;
         if (lane == 1 && w + 1 < words) fw[w + 1] = (uint32_t)(b >> 32);
     }
+    uint32_t *part = fw + kFusedWords;     // per-wave partial results: [4][WAVES]
+    npass = (int)wave_sum((float)npass);
+    if (lane == 0) part[C::WAVES + wave] = (uint32_t)npass;
     __syncthreads();
+    int total_pass = 0;
+#pragma unroll
+    for (int w = 0; w < C::WAVES; ++w) total_pass += (int)part[C::WAVES + w];
+    total_pass = __builtin_amdgcn_readfirstlane(total_pass);
+    if (a.min_keep > 0 && total_pass == 0) {
+        // the floor: the block of largest score, lowest index among equal ones
+        const float m = wave_max(best);
+        const float jm = wave_reduce(best == m ? (float)best_j : (float)n, [](float x, float y) { return fminf(x, y); });
+        if (lane == 0) {
+            part[2 * C::WAVES + wave] = __float_as_uint(m);
+            part[3 * C::WAVES + wave] = (uint32_t)(int)jm;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float bm = -INFINITY;
+            int bj = n;
+            for (int w = 0; w < C::WAVES; ++w) {
+                const float mw = __uint_as_float(part[2 * C::WAVES + w]);
+                const int jw = (int)part[3 * C::WAVES + w];
+                if (jw < n && (bj == n || mw > bm || (mw == bm && jw < bj))) {
+                    bm = mw;
+                    bj = jw;
+                }
+            }
+            if (bj < n) fw[bj / 32] |= 1u << (bj % 32);
+        }
+        __syncthreads();
+    }
     int cnt = 0;
     for (int w = threadIdx.x; w < words; w += C::THREADS) {
         const uint32_t x = fw[w];
@@ -253,11 +300,11 @@ __device__ __forceinline__ int fused_route(int bh, int I, const FlashArgs &a, ui
         cnt += __popc(x);
     }
     cnt = (int)wave_sum((float)cnt);
-    if (lane == 0) fw[kFusedWords + wave] = (uint32_t)cnt;
+    if (lane == 0) part[wave] = (uint32_t)cnt;
     __syncthreads();
     int total = 0;
 #pragma unroll
-    for (int w = 0; w < C::WAVES; ++w) total += (int)fw[kFusedWords + w];
+    for (int w = 0; w < C::WAVES; ++w) total += (int)part[w];
     if (threadIdx.x == 0) a.kv_count_out[row] = total;
     return __builtin_amdgcn_readfirstlane(total);
 }
@@ -768,7 +815,9 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
         }
         if constexpr (kSparse) {
             ts.list = (const kconst<int32_t> *)(a.kv_idx + row_id * a.kv_idx_cap);
-            ts.cnt = __builtin_amdgcn_readfirstlane(a.kv_count[row_id]);
+            // at most the list's capacity and n_kb: a count beyond them (a route
+            // that does not belong to this call) cannot run the stream off the list
+            ts.cnt = min(max(__builtin_amdgcn_readfirstlane(a.kv_count[row_id]), 0), min(a.kv_idx_cap, a.n_kb));
             ts.mask = (const kconst<uint32_t> *)(a.kv_mask + row_id * a.mask_words);
             ts.n_rt = (a.residual && ts.cnt < a.n_kb) ? a.mask_words : 0;   // all kept: no residual
         } else {
@@ -778,7 +827,7 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
             ts.n_rt = 0;
         }
     }
-    ts.prime();
+    ts.prime(a);
     HeadSrc<T> hs;
     hs.k = k + head;
     hs.v = v + head;
@@ -944,13 +993,15 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
     const int p = grid_position(blockIdx.x, a.n_items);
     // sparse paths take the route's cost-ordered work list (under fused routing
     // the pre-pass costs the decisions the forward takes)
-    const int item = kSparse ? __builtin_amdgcn_readfirstlane(a.work_order[p]) : p;
+    // (an entry outside [0, n_items) is clamped: a route that does not belong to
+    // this call gives a wrong result, never a read outside the tensors)
+    const int item = kSparse ? min(max(__builtin_amdgcn_readfirstlane(a.work_order[p]), 0), a.n_items - 1) : p;
     __shared__ __attribute__((aligned(1024))) unsigned char K0[C::TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char K1[C::TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char V0[C::TILE];
     uint32_t *fw = nullptr;
     if constexpr (kFused) {
-        __shared__ uint32_t FW[kFusedWords + C::WAVES];
+        __shared__ uint32_t FW[kFusedWords + 4 * C::WAVES];
         fw = FW;
     }
     if constexpr (sizeof(T) == 2) {

@@ -52,6 +52,7 @@ struct FlashArgs {
     uint32_t *kv_mask_out;
     int32_t *kv_count_out;
     int tau_mode, n_prefix;
+    int min_keep;                        // 0 or 1: the floor of one block
     float scale, ln_tau;
 };
 

@@ -444,10 +444,22 @@ __device__ __forceinline__ void row_stats_only(const float *S, int bh, int I, co
     const int rows = a.exact_tile_rows;
     const int t_full = (a.block_k + rows - 1) / rows;
     const int t_last = (a.N - (n - 1) * a.block_k + rows - 1) / rows;
+    // a floor of one block: when no block clears the threshold the forward keeps
+    // the row's best block (the largest score, lowest J among equal ones)
+    int floor_j = -1;
+    if (a.min_keep > 0) {
+        int npass = 0;
+        for (int J = lane; J < n; J += kWave) npass += S[J] >= thr ? 1 : 0;
+        if (wave_count(npass) == 0) {
+            int jm = n;
+            for (int J = lane; J < n; J += kWave) jm = (S[J] == m && J < jm) ? J : jm;
+            floor_j = (int)wave_reduce((float)jm, [](float x, float y) { return fminf(x, y); });
+        }
+    }
     int tiles = 0;
     for (int base = 0; base < n; base += kWave) {
         const int J = base + lane;
-        const bool keep = J < n && (S[J] >= thr || dense_row || (int64_t)J * a.block_k < a.n_prefix);
+        const bool keep = J < n && (S[J] >= thr || J == floor_j || dense_row || (int64_t)J * a.block_k < a.n_prefix);
         tiles += keep ? (J == n - 1 ? t_last : t_full) : 0;
         const uint64_t kb = __ballot(keep);
         // the chunk's two mask words: residual tile if a valid block is dropped

@@ -350,7 +350,11 @@ __global__ __launch_bounds__(kFitThreads) void pr_fit_kernel(PrArgs a) {
     for (int it = 0; it <= n_iter; ++it) {
         if (it > 0) s_times_q(Qs);
         // modified Gram-Schmidt on the columns, by one wave, in registers: lane
-        // l holds rows l, l + 64, ..
+        // l holds rows l, l + 64, ..  In fp32 one pass leaves the basis
+        // orthogonal only to about eps times the spread of the column norms
+        // (up to 1e-3 here), which would carry into Pk = Q Q^T; the last
+        // iteration, whose basis the Rayleigh-Ritz step uses, orthogonalises
+        // twice (a second pass restores orthogonality to rounding).
         if (wave == 0) {
             constexpr int RL = D / kWave;                 // rows per lane
             float qv[RL][kPrMaxRank];
@@ -358,6 +362,8 @@ __global__ __launch_bounds__(kFitThreads) void pr_fit_kernel(PrArgs a) {
             for (int r = 0; r < RL; ++r)
 #pragma unroll
                 for (int c = 0; c < kPrMaxRank; ++c) qv[r][c] = c < K2 ? Qs[(lane + r * kWave) * KI + c] : 0.f;
+            const int passes = it == n_iter ? 2 : 1;
+            for (int pass = 0; pass < passes; ++pass)
 #pragma unroll
             for (int c = 0; c < kPrMaxRank; ++c) {
                 if (c >= K2) break;

@@ -29,8 +29,11 @@
  *     the key-block means on its own before the average; the scores compared
  *     are then s_IJ = ln A_IJ (so the softmax of a row is A itself, and
  *     SA_TAU_TOPP retains PARK's cumulative importance).  Its logits carry
- *     fp32-level error (split bf16 products).  Supported while
- *     (block_q / 32 + 1) * n_kb + block_q floats fit in 64 KB.
+ *     fp32-level error (split bf16 products).  A PAMA workgroup takes
+ *     Q = 256 (bf16) or 128 (fp32) queries, G = Q / block_q query blocks;
+ *     supported while (4 + G) * n_kb + Q floats plus a 26 KB staging tile fit
+ *     in 128 KB of LDS (n_kb <= 3248 for bf16 at block_q = 64, 4330 at 128;
+ *     4352 and 5222 for fp32).
  *     With SA_FLAG_FUSED (pass it to both calls) routing is fused into the
  *     attention pass, the Sol-Attn abstract's single pass: sparse_attn_route
  *     only pools and writes the proxy rows' maximum and log-sum-exp, and the
@@ -39,8 +42,9 @@
  *     its work item from s_IJ and those statistics, writes them to kv_mask and
  *     kv_count, and attends in the work order.  The
  *     decisions are the τ test of RELATIVE or ABSOLUTE; max_keep must be 0,
- *     min_keep 0 (or 1 for RELATIVE with tau <= 1, where the argmax clears τ),
- *     no PAMA, n_kb <= 16384.  The dense prefix applies as above.
+ *     min_keep 0 or 1 (with 1, a row where no block clears tau keeps its block
+ *     of largest proxy score, lowest J among equal ones), no PAMA,
+ *     n_kb <= 16384.  The dense prefix applies as above.
  *
  *  2. Exact pass.  One online-softmax pass over the kept key blocks:
  *     logits scale * q_i . k_t for every token t of a kept block (Sol-Attn
@@ -63,6 +67,8 @@
  *    fp32 accumulation; fp32 inputs enter them as bf16 pairs (the rounded
  *    value and its remainder), the softmax weights as bf16.  Routing
  *    (pooling, proxy, threshold) is fp32 throughout.
+ *  - One head's keys (N * d elements) must span at most 2^32 - 1 bytes; larger
+ *    is SA_ERR_UNSUPPORTED.
  *  - Every tensor pointer is a DEVICE pointer (hipMalloc or equivalent) of the
  *    current HIP device, 16-byte aligned (hipMalloc and torch allocations are;
  *    the kernels move 16-byte vectors; lse and perm need 4 bytes).  A
@@ -189,7 +195,11 @@ sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, co
 
 /* Steps 2 and 3.  Writes o [B,H,N,d] (dtype of p) and, when lse is not NULL,
  * lse [B,H,N] fp32 (natural log).  r must come from sparse_attn_route with
- * the same p (tau and budget fields may not differ) on the same k and v. */
+ * the same p (only SA_FLAG_NO_RESIDUAL may differ) on the same k and v.  The
+ * route buffers are not validated on the device: entries of another route
+ * (out-of-range counts, block indices or work items) are clamped to the
+ * buffers' ranges, so that such a misuse reads nothing outside q, k, v and the
+ * route, but its output is meaningless. */
 sa_status sparse_attn_forward(const sa_params *p, const void *q, const void *k, const void *v,
                               const sa_route *r, void *o, float *lse, void *stream);
 
@@ -211,10 +221,13 @@ sa_status sparse_attn_dense_ref_gpu(const sa_params *p, const void *q, const voi
  *   4. o = O_s + (b + O_s B) Pk on every row that is not a probe, O_dense on
  *      probe rows.
  * Intermediates live in the caller's workspace, of the size
- * sparse_attn_sparsepr_workspace_size() gives (host only, no HIP calls): the
- * gathered probe queries in q's dtype; O_s, the probes' dense outputs (per key
- * range, then merged), the Gram matrices and the fitted map (b Pk and the
- * factors B Q and Q of B Pk) in fp32.
+ * sparse_attn_sparsepr_workspace_size() gives (host only, no HIP calls).  It
+ * starts with, each piece padded to a multiple of 256 bytes: the gathered
+ * probe queries [B,H,M,d] in q's dtype (M = n_qb * probes_per_block), the
+ * probes' dense outputs [B,H,M,d] fp32, then O_s [B,H,N,d] fp32 (readable
+ * after the call, for inspection); then the Gram matrices, the fitted map (b Pk
+ * and the factors B Q and Q of B Pk) and the probe pass's per-key-range
+ * outputs, in fp32.
  * probes_per_block in [1, 16], rank in [1, min(16, d)], ridge >= 0; the route
  * must not be fused.  o has the layout and dtype of q.  The workspace must not
  * be shared by concurrent calls. */

@@ -84,6 +84,13 @@ def check_mask_head(gpu_mask: np.ndarray, q: np.ndarray, k: np.ndarray, cfg, row
     return rt, int(diff.sum()), int(rt.exempt.sum())
 
 
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half the spacing of bf16 numbers at |x| (8 significant bits): the most that
+    rounding a result to a bf16 output moves it."""
+    _, e = np.frexp(np.abs(np.asarray(x, dtype=np.float64)))   # |x| in [2^(e-1), 2^e)
+    return np.ldexp(1.0, e - 9)
+
+
 def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 

@@ -65,10 +65,12 @@ def params(**kw):
     (dict(scale=-1.0), B.SA_ERR_INVALID_ARG), (dict(d=96), B.SA_ERR_UNSUPPORTED),
     (dict(block_q=32), B.SA_ERR_UNSUPPORTED), (dict(block_k=256), B.SA_ERR_UNSUPPORTED),
     (dict(N=2_000_000, block_k=64), B.SA_ERR_UNSUPPORTED),
-    # fused routing decides each block alone: no cap, no top-p, no PAMA, no binding floor
+    # fused routing decides each block alone: no cap, no top-p, no PAMA, no floor above one block
     (dict(flags=4, max_keep=3), B.SA_ERR_UNSUPPORTED), (dict(flags=4, tau_mode=2), B.SA_ERR_UNSUPPORTED),
-    (dict(flags=6), B.SA_ERR_UNSUPPORTED), (dict(flags=4, tau_mode=1, min_keep=1), B.SA_ERR_UNSUPPORTED),
-    (dict(flags=4, tau=1.5), B.SA_ERR_UNSUPPORTED),
+    (dict(flags=6), B.SA_ERR_UNSUPPORTED), (dict(flags=4, min_keep=2), B.SA_ERR_UNSUPPORTED),
+    (dict(flags=4, tau_mode=1, min_keep=3), B.SA_ERR_UNSUPPORTED),
+    # one head's keys beyond the 32-bit byte range of the kernels' buffer resources
+    (dict(N=8_388_608, d=128, dtype=1, block_k=128), B.SA_ERR_UNSUPPORTED),
 ])
 def test_invalid_params_rejected(kw, status):
     p = params(**kw)
@@ -78,10 +80,44 @@ def test_invalid_params_rejected(kw, status):
     assert B.lib.sparse_attn_last_error().decode() != ""
 
 
-def test_fused_floor_free_configurations_accepted():
+def test_fused_floor_configurations_accepted():
+    """Fused routing takes a floor of at most one block (the row's best block when
+    nothing clears tau), in either tau mode and at any tau."""
     for kw in (dict(flags=4), dict(flags=4, tau_mode=1, min_keep=0), dict(flags=4, tau=1.0),
-               dict(flags=5, min_keep=0, tau=3.0)):
+               dict(flags=5, min_keep=0, tau=3.0), dict(flags=4, tau_mode=1, min_keep=1),
+               dict(flags=4, tau=1.5)):
         assert B.lib.sparse_attn_kv_idx_cap(ctypes.byref(params(**kw))) > 0, kw
+
+
+def test_head_byte_range_limit():
+    """The largest head the kernels address (N * d * element size <= 2^32 - 1 bytes)
+    is accepted; one token more is rejected before any launch, for the dense path too."""
+    A = 0x1000                     # a stand-in device address (16-byte aligned), never dereferenced
+    n_ok = (2 ** 32 - 1) // (128 * 4)
+    ok = params(N=n_ok, d=128, dtype=1, block_q=128, block_k=128, tau=0.0)
+    over = params(N=n_ok + 1, d=128, dtype=1, block_q=128, block_k=128, tau=0.0)
+    st = B.lib.sparse_attn_dense_ref_gpu(ctypes.byref(over), A, A, A, A, None, None)
+    assert st == B.SA_ERR_UNSUPPORTED and "bytes per head" in B.last_error()
+    # the accepted size stops at a later check (no pointers), not at the byte range
+    st = B.lib.sparse_attn_dense_ref_gpu(ctypes.byref(ok), A, A, A, None, None, None)
+    assert st == B.SA_ERR_INVALID_ARG and "o is NULL" in B.last_error()
+
+
+def test_route_parameters_checked_by_the_binding():
+    """A route remembers the parameters it was built for; a forward with other
+    shapes, routing fields or routing flags is refused before anything is
+    enqueued (only the forward-only no-residual switch may differ)."""
+    p = params(B=1, H=2, N=1000, d=64, block_q=64, block_k=64, flags=B.FLAG_FUSED)
+    rt = B.Route(p, "cpu")
+    rt.check(p, "forward")
+    rt.check(B.SaParams.from_buffer_copy(params(B=1, H=2, N=1000, d=64, block_q=64, block_k=64,
+                                                flags=B.FLAG_FUSED | B.FLAG_NO_RESIDUAL)), "forward")
+    for kw in (dict(flags=0), dict(N=999), dict(block_k=128), dict(tau=0.02), dict(dtype=1), dict(H=3),
+               dict(flags=B.FLAG_FUSED | B.FLAG_PAMA)):
+        base = dict(B=1, H=2, N=1000, d=64, block_q=64, block_k=64, flags=B.FLAG_FUSED)
+        base.update(kw)
+        with pytest.raises(ValueError, match="other parameters"):
+            rt.check(params(**base), "forward")
 
 
 @pytest.mark.parametrize("block_q,dtype,n_max", [(64, 0, 3248), (128, 0, 4330), (64, 1, 4352), (128, 1, 5222)])

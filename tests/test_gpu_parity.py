@@ -124,6 +124,12 @@ FUSED_SMALL = [
     ("fused_f32", (4, 8, 16), 64, 64, 64, "f32", 0.02, R.RELATIVE, 1, 0, False, 1, 2),
     ("fused_all_dropped", (3, 8, 27), 128, 128, 128, "bf16", 2.0, R.RELATIVE, 0, 0, False, 1, 1),
     ("fused_n130", (1, 10, 13), 128, 128, 64, "bf16", 0.05, R.ABSOLUTE, 0, 0, False, 1, 1),
+    # a floor of one block: at tau = 1 only the row maximum clears tau, and the
+    # fused score of the argmax may round below the pre-pass maximum; with a high
+    # ABSOLUTE tau or tau > 1 nothing clears it; the row keeps its best block
+    ("fused_rel_tau1_floor", (4, 8, 32), 128, 128, 128, "bf16", 1.0, R.RELATIVE, 1, 0, False, 1, 2),
+    ("fused_abs_floor_k64", (5, 8, 25), 128, 128, 64, "bf16", 0.5, R.ABSOLUTE, 1, 0, False, 1, 2),
+    ("fused_floor_prefix", (4, 8, 30), 128, 128, 128, "bf16", 2.0, R.RELATIVE, 1, 100, True, 1, 1),
 ]
 
 
@@ -133,6 +139,8 @@ def test_fused_parity(case):
     w = S.small(name, B, H, d, grid, bq, bk, tau, dtype=dt, qscale=6.0, n_text=n_text, hilbert=hil)
     cfg = cfg_for(w, mode=mode, max_keep=0, min_keep=mn, fused=True)
     rt, O, L, mask = full_check(w, cfg, label="fused")
+    if mn >= 1:
+        assert (rt.kv_count.cpu().numpy() >= 1).all(), "a row kept no block under a floor of one"
     # the two-kernel route on the same inputs: the same decisions outside the
     # band, and then the same tiles in the same order, so the same bits
     Qc, Kc, Vc, Q, K, V = make(w)
@@ -157,13 +165,45 @@ def test_fused_rejects_what_it_cannot_decide_alone():
     m = sa()
     w = S.small("fr", 1, 1, 128, (2, 8, 16), 128, 128, 0.01)
     Qc, Kc, Vc, Q, K, V = make(w)
-    for kw in (dict(max_keep=3), dict(tau_mode=R.TOPP), dict(tau_mode=R.ABSOLUTE, min_keep=1),
-               dict(proxy=R.PAMA), dict(tau=1.5, min_keep=1)):
+    for kw in (dict(max_keep=3), dict(tau_mode=R.TOPP), dict(tau_mode=R.ABSOLUTE, min_keep=2),
+               dict(proxy=R.PAMA), dict(tau=1.5, min_keep=2)):
         base = dict(block_q=128, block_k=128, tau=0.01, fused=True, min_keep=0)
         base.update(kw)
         with pytest.raises(m.SparseAttnError) as ei:
             m.route(Q, K, V, m.Config(**base))
         assert ei.value.status == m.binding.SA_ERR_UNSUPPORTED
+
+
+def test_route_of_other_parameters_refused():
+    """A route serves forwards of its own parameters only: a fused route (no lists)
+    under a two-kernel forward, or a route of another shape, tau or block size,
+    is refused before anything is enqueued; so are out= tensors of another shape."""
+    m = sa()
+    w = S.small("rp", 1, 2, 128, (2, 8, 16), 128, 128, 0.01)
+    Qc, Kc, Vc, Q, K, V = make(w)
+    cfg = cfg_for(w)
+    fused = cfg_for(w, fused=True)
+    rt_f = m.route(Q, K, V, fused)
+    with pytest.raises(ValueError, match="other parameters"):
+        m.forward(Q, K, V, rt_f, cfg)
+    rt = m.route(Q, K, V, cfg)
+    for bad in (cfg_for(w, tau=0.02), m.Config(block_q=128, block_k=64, tau=0.01)):
+        with pytest.raises(ValueError, match="other parameters"):
+            m.forward(Q, K, V, rt, bad)
+    with pytest.raises(ValueError):
+        m.forward(Q[:, :1].contiguous(), K[:, :1].contiguous(), V[:, :1].contiguous(), rt, cfg)
+    with pytest.raises(ValueError, match="out"):
+        m.forward(Q, K, V, rt, cfg, out=torch.empty_like(Q[:, :1]))
+    with pytest.raises(ValueError, match="other parameters"):
+        m.route(Q, K, V, m.Config(block_q=128, block_k=64, tau=0.01), out=rt)
+    torch.cuda.synchronize()
+    # re-routing into the same buffers with a new tau is allowed, and the route
+    # then serves forwards of that tau
+    cfg2 = cfg_for(w, tau=0.05)
+    m.route(Q, K, V, cfg2, out=rt)
+    O = m.forward(Q, K, V, rt, cfg2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(O.float()).all()
 
 
 @pytest.mark.parametrize("mode", [R.RELATIVE, R.ABSOLUTE])

@@ -383,6 +383,35 @@ def test_recall_is_one_when_all_kept():
     assert abs(R.attention_recall(q, k, rt.mask, p) - 1.0) < 1e-12
 
 
+def test_recall_hand_worked_partial_mask():
+    """Attention recall (PARK page, section 3.2: the share of the dense softmax
+    weight that lands in retained blocks, averaged over queries) worked by hand
+    on d = 1, N = 4 with a logit scale of 1/2 and block 0 dropped for both
+    query blocks.
+
+    q = (1, 1, 0, 0), k = (-1, 1, 2, 0): the rows with q = 1 have logits
+    (-1/2, 1/2, 1, 0) and keep tokens 2, 3, so their recall is
+    (e + 1) / (e^(-1/2) + e^(1/2) + e + 1); the rows with q = 0 weigh all four
+    keys equally and keep two of them, recall 1/2.  A dropped scale (logits
+    -1, 1, 2, 0) or a mask indexed [key block, query block] (which would drop
+    tokens 2, 3 of the first rows and keep all of the last) give other values;
+    block_q = 4 (one query block) with block_k = 2 gives the same value."""
+    q = np.array([[1.0], [1.0], [0.0], [0.0]])
+    k = np.array([[-1.0], [1.0], [2.0], [0.0]])
+    e = math.e
+    first = (e + 1.0) / (math.exp(-0.5) + math.exp(0.5) + e + 1.0)
+    want = (2.0 * first + 2.0 * 0.5) / 4.0
+    p = R.RouteParams(2, 2, 0.0, scale=0.5)
+    mask = np.array([[False, True], [False, True]])
+    assert abs(R.attention_recall(q, k, mask, p) - want) < 1e-12
+    p1 = R.RouteParams(4, 2, 0.0, scale=0.5)
+    assert abs(R.attention_recall(q, k, np.array([[False, True]]), p1) - want) < 1e-12
+    # the two plausible mistakes give different numbers
+    unscaled = (2.0 * (e * e + 1.0) / (math.exp(-1.0) + e + e * e + 1.0) + 1.0) / 4.0
+    transposed = (2.0 * 0.0 + 2.0 * 1.0) / 4.0
+    assert abs(want - unscaled) > 1e-2 and abs(want - transposed) > 1e-2
+
+
 # ----------------------------------------------------------------------------- PAMA proxy
 # Per-query attention-mass aggregation (PARK page, section 5.1): each query's
 # softmax over the key-block means, averaged within its query block.
