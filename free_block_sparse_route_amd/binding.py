@@ -73,6 +73,8 @@ def _load():
     lib.sparse_attn_forward_sparsepr.argtypes = [P, vp, vp, vp, R, i32, i32, ctypes.c_float, vp, ctypes.c_size_t,
                                                  vp, vp]
     lib.sparse_attn_forward_sparsepr.restype = ctypes.c_int
+    lib.sparse_attn_forward_sparsepr_static.argtypes = [P, vp, vp, vp, R, i32, i32, ctypes.c_float, vp, vp]
+    lib.sparse_attn_forward_sparsepr_static.restype = ctypes.c_int
     lib.sparse_attn_status_string.argtypes = [ctypes.c_int]
     lib.sparse_attn_status_string.restype = ctypes.c_char_p
     lib.sparse_attn_last_error.argtypes = []
@@ -283,6 +285,23 @@ def forward_sparsepr(q, k, v, rt: Route, cfg: Config, probes_per_block: int = 2,
     _check(lib.sparse_attn_forward_sparsepr(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                             ctypes.byref(rt.c), probes_per_block, rank, ridge, ws.data_ptr(),
                                             ws.numel(), o.data_ptr(), _stream(q.device)))
+    return o
+
+
+def forward_sparsepr_static(q, k, v, rt: Route, cfg: Config, probes_per_block: int = 2, rank: int = 8,
+                            ridge: float = 1e-3, out: torch.Tensor | None = None) -> torch.Tensor:
+    """sparse_attn_forward_sparsepr_static: forward_sparsepr with its intermediates in
+    the library's static per-GPU array (no workspace; the library allocates nothing).
+    Calls that overlap on one GPU race; out= lets the caller allocate nothing either."""
+    _check_qkv(q, k, v)
+    p = make_params(q, cfg)
+    rt.check(p, "forward_sparsepr_static")
+    if out is not None:
+        _check_out("out", out, q)
+    o = out if out is not None else torch.empty_like(q)
+    _check(lib.sparse_attn_forward_sparsepr_static(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                   ctypes.byref(rt.c), probes_per_block, rank, ridge,
+                                                   o.data_ptr(), _stream(q.device)))
     return o
 
 

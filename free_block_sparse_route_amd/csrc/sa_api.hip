@@ -5,8 +5,16 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "sa_internal.h"
 #include "sparse_attn.h"
+
+// Workspace of the allocation-free probe-fitted entry point
+// (sparse_attn_forward_sparsepr_static): one array per device, held until the
+// process ends.  In host code its name is only a handle for the runtime; the
+// device address of each GPU's copy comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[SA_SPARSEPR_STATIC_WORKSPACE_BYTES];
 
 namespace {
 
@@ -447,6 +455,29 @@ sa_status run_sparsepr(const sa_params *p, const void *q, const void *k, const v
     return SA_OK;
 }
 
+constexpr size_t kStaticScratchBytes = SA_SPARSEPR_STATIC_WORKSPACE_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up once per
+// device, with that device current).
+sa_status scratch_of_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "sparsepr (static workspace): hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(SA_ERR_UNSUPPORTED, "device ordinal %d >= %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "sparsepr (static workspace): hipGetSymbolAddress");
+        if (!ptr || (uintptr_t)ptr % 256 != 0) return fail(SA_ERR_HIP, "sparsepr (static workspace): bad address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SA_OK;
+}
 }  // namespace
 
 sa_status sparse_attn_forward_sparsepr(const sa_params *p, const void *q, const void *k, const void *v,
@@ -459,6 +490,22 @@ sa_status sparse_attn_forward_sparsepr(const sa_params *p, const void *q, const 
     if (workspace_bytes < L.total)
         return fail(SA_ERR_CAPACITY, "workspace %zu bytes < required %zu", workspace_bytes, L.total);
     return run_sparsepr(p, q, k, v, r, probes_per_block, rank, ridge, L, workspace, o, stream);
+}
+
+sa_status sparse_attn_forward_sparsepr_static(const sa_params *p, const void *q, const void *k, const void *v,
+                                              const sa_route *r, int32_t probes_per_block, int32_t rank,
+                                              float ridge, void *o, void *stream) {
+    sa_status s = check_sparsepr_call(p, q, k, v, r, probes_per_block, rank, ridge, o);
+    if (s != SA_OK) return s;
+    const PrLayout L = pr_layout(p, probes_per_block, kStaticScratchBytes);
+    if (L.total > kStaticScratchBytes)
+        return fail(SA_ERR_CAPACITY,
+                    "sparsepr (static workspace): this call needs %zu bytes of workspace, more than the %zu "
+                    "bytes of the library's static array; use sparse_attn_forward_sparsepr with a workspace",
+                    L.total, kStaticScratchBytes);
+    void *ws = nullptr;
+    if ((s = scratch_of_current_device(&ws)) != SA_OK) return s;
+    return run_sparsepr(p, q, k, v, r, probes_per_block, rank, ridge, L, ws, o, stream);
 }
 
 const char *sparse_attn_status_string(sa_status s) {

@@ -236,6 +236,27 @@ sa_status sparse_attn_forward_sparsepr(const sa_params *p, const void *q, const 
                                        const sa_route *r, int32_t probes_per_block, int32_t rank, float ridge,
                                        void *workspace, size_t workspace_bytes, void *o, void *stream);
 
+/* sparse_attn_forward_sparsepr without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * that must not call hipMalloc, harnesses that forbid it).  It allocates
+ * nothing: the intermediates live in a static device array of
+ * SA_SPARSEPR_STATIC_WORKSPACE_BYTES per GPU, which the library holds from its
+ * first use on that GPU until the process ends.  The computation is
+ * sparse_attn_forward_sparsepr's (the same kernels); when the layout that call
+ * would use does not fit, the probe pass takes fewer key ranges (a different
+ * summation order of the probes' dense outputs, nothing else).  A call that
+ * does not fit even then returns SA_ERR_CAPACITY before any launch (for
+ * Wan-1.3B-sized heads, N = 32760 and d = 128, about 12 heads at
+ * probes_per_block = 4).  Every call on one GPU uses that GPU's one array:
+ * calls that overlap on one GPU (concurrent streams, or threads) race and must
+ * be serialised by the caller; no part of the array needs to start at zero,
+ * and what an earlier call left in it does not matter.  Arguments, errors and
+ * o as for sparse_attn_forward_sparsepr. */
+#define SA_SPARSEPR_STATIC_WORKSPACE_BYTES ((size_t)256 << 20)
+sa_status sparse_attn_forward_sparsepr_static(const sa_params *p, const void *q, const void *k, const void *v,
+                                              const sa_route *r, int32_t probes_per_block, int32_t rank,
+                                              float ridge, void *o, void *stream);
+
 /* Token reordering (DFSAttn abstract: tokens reordered along a 3D Hilbert curve
  * before blocking, so that a block of consecutive tokens is compact in space
  * and time).  The library orders a T x Hh x W video token grid and permutes
