@@ -542,23 +542,23 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
         const float *kb = a.k_mean + (size_t)bh * n * D;
         const int n_sl = (n + 15) / 16;
         constexpr int kStride = kSelectThreads / kWave;
+        // A slice past the last key block reads block 0 instead (in bounds): its
+        // rows only form the scores of blocks J >= n_kb, which are never stored,
+        // so the loaded values go to the products untouched (no select on them,
+        // which would make the compiler wait for the loads where they are issued).
         auto load_slice = [&](int sl, float (&kv)[KS]) {
             const int J = sl * 16 + i16;
             const float *src = kb + (size_t)(J < n ? J : 0) * D + kg * KS;
 #pragma unroll
             for (int e = 0; e < KS; e += 4) {
-                const f32x4 y = *reinterpret_cast<const f32x4 *>(src + e);   // block clamped: in bounds
-                const f32x4 x = J < n ? y : f32x4{};
-                kv[e] = x[0];
-                kv[e + 1] = x[1];
-                kv[e + 2] = x[2];
-                kv[e + 3] = x[3];
+                const f32x4 y = *reinterpret_cast<const f32x4 *>(src + e);
+                kv[e] = y[0];
+                kv[e + 1] = y[1];
+                kv[e + 2] = y[2];
+                kv[e + 3] = y[3];
             }
         };
-        float kv[KS], kn[KS];
-        if (wave0 < n_sl) load_slice(wave0, kv);
-        for (int sl = wave0; sl < n_sl; sl += kStride) {
-            if (sl + kStride < n_sl) load_slice(sl + kStride, kn);     // the next slice's keys in flight
+        auto scores = [&](int sl, const float (&kv)[KS]) {
             f32x4 acc0 = {}, acc1 = {};
 #pragma unroll
             for (int e = 0; e < KS; e += 2) {
@@ -572,8 +572,22 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
                     if (Jr < n) S[i16 * n + Jr] = (acc0[r] + acc1[r]) * a.scale;
                 }
             }
-#pragma unroll
-            for (int e = 0; e < KS; ++e) kv[e] = kn[e];
+        };
+        // two slice buffers in turn: the next slice's keys are in flight while
+        // the current one's products run (with a single buffer copied at the end
+        // of each step the compiler waited for the next slice before the products)
+        // The loads are unconditional (a slice past the last one reloads the last,
+        // whose scores are not stored twice): a load under a branch makes the
+        // compiler wait for every load in flight at the join.
+        float ka[KS], kb2[KS];
+        const int last = n_sl - 1;
+        load_slice(min(wave0, last), ka);
+        for (int sl = wave0; sl < n_sl; sl += 2 * kStride) {
+            load_slice(min(sl + kStride, last), kb2);
+            scores(sl, ka);
+            if (sl + kStride >= n_sl) break;
+            load_slice(min(sl + 2 * kStride, last), ka);
+            scores(sl + kStride, kb2);
         }
     }
     __syncthreads();
@@ -968,6 +982,107 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *cos
     }
 }
 
+// Head-major work order, for long work lists: heads by total cost (highest
+// first, lower index on ties), within a head by cost band (highest first) and
+// then by query block.  A head's neighbouring query blocks, which keep mostly the
+// same key blocks, then run together and share the key and value tiles in the
+// dies' L2 and the Infinity Cache, while the heads' order keeps the most
+// expensive work first.  One workgroup of 16 waves; a wave places whole heads,
+// holding a head's costs in registers (n_qb <= kHeadChunks * 64).
+constexpr int kHeadChunks = 32;
+constexpr int kHeadMaxBH = 1024;
+
+__global__ __launch_bounds__(kOrderThreads) void order_head_kernel(const int32_t *cost, int32_t *work_order, int BH,
+                                                                   int n_qb) {
+    constexpr int NW = kOrderThreads / kWave;
+    __shared__ int32_t hcost[kHeadMaxBH];
+    __shared__ int32_t hrank[kHeadMaxBH];
+    __shared__ int32_t hist[NW][kBands];
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int chunks = (n_qb + kWave - 1) / kWave;
+    // costs of head h into registers, every load issued before the first use
+    auto load = [&](int h, int (&c)[kHeadChunks]) {
+#pragma unroll
+        for (int r = 0; r < kHeadChunks; ++r) {
+            const int I = r * kWave + lane;
+            c[r] = (r < chunks && I < n_qb) ? cost[(size_t)h * n_qb + I] : -1;
+        }
+    };
+    int c[kHeadChunks];
+    for (int h = wave; h < BH; h += NW) {
+        load(h, c);
+        int sum = 0;
+#pragma unroll
+        for (int r = 0; r < kHeadChunks; ++r) sum += max(c[r], 0);
+        sum = wave_count(sum);
+        if (lane == 0) hcost[h] = sum;
+    }
+    __syncthreads();
+    for (int h = threadIdx.x; h < BH; h += kOrderThreads) {
+        const int ch = hcost[h];
+        int rk = 0;
+        for (int g = 0; g < BH; ++g) {
+            const int cg = hcost[g];
+            rk += (cg > ch || (cg == ch && g < h)) ? 1 : 0;
+        }
+        hrank[h] = rk;
+    }
+    __syncthreads();
+    for (int h = wave; h < BH; h += NW) {
+        load(h, c);
+        if (lane < kBands) hist[wave][lane] = 0;
+        __builtin_amdgcn_wave_barrier();
+        // band histogram of the head (row 0: highest band)
+#pragma unroll
+        for (int r = 0; r < kHeadChunks; ++r) {
+            if (r >= chunks) break;
+            const int row = c[r] >= 0 ? kBands - 1 - cost_band(c[r]) : -1;
+            uint64_t left = __ballot(row >= 0);
+            while (left) {
+                const int rr = __builtin_amdgcn_readlane(row, __builtin_ctzll(left));
+                const uint64_t mr = __ballot(row == rr);
+                if (lane == 0) hist[wave][rr] += __popcll(mr);
+                left &= ~mr;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        // exclusive prefix over the rows: where the head's items of each band start
+        if (lane == 0) {
+            int run = hrank[h] * n_qb;
+            for (int rr = 0; rr < kBands; ++rr) {
+                const int n = hist[wave][rr];
+                hist[wave][rr] = run;
+                run += n;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int r = 0; r < kHeadChunks; ++r) {
+            if (r >= chunks) break;
+            const int row = c[r] >= 0 ? kBands - 1 - cost_band(c[r]) : -1;
+            uint64_t left = __ballot(row >= 0);
+            while (left) {
+                const int rr = __builtin_amdgcn_readlane(row, __builtin_ctzll(left));
+                const uint64_t mr = __ballot(row == rr);
+                const int base = hist[wave][rr];
+                if (row == rr) work_order[base + __popcll(mr & lanes_below())] = h * n_qb + r * kWave + lane;
+                if (lane == 0) hist[wave][rr] = base + __popcll(mr);
+                left &= ~mr;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// The head-major order serves long work lists (many items per workgroup slot of
+// the attention kernel); shorter lists keep the global cost-band order, whose
+// tail balances better.
+constexpr int kHeadOrderMinItems = 16 * 768;
+
+bool head_major_order(int BH, int n_qb) {
+    return (int64_t)BH * n_qb >= kHeadOrderMinItems && n_qb <= kHeadChunks * kWave && BH <= kHeadMaxBH;
+}
+
 // --------------------------------------------------------------------- launch
 template <typename T, int D>
 static hipError_t launch_pool_t(const void *q, const void *k, const void *v, const PoolArgs &a,
@@ -1047,8 +1162,12 @@ hipError_t launch_select(int D, const SelectArgs &a, int BH, hipStream_t st, int
     if (e != hipSuccess) return e;
     // (fused routing too: its pre-pass writes the costs of the decisions the
     // forward will take)
-    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, st, (const int32_t *)a.cost, a.work_order,
-                       BH * a.n_qb);
+    if (head_major_order(BH, a.n_qb))
+        hipLaunchKernelGGL(order_head_kernel, dim3(1), dim3(kOrderThreads), 0, st, (const int32_t *)a.cost,
+                           a.work_order, BH, a.n_qb);
+    else
+        hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, st, (const int32_t *)a.cost, a.work_order,
+                           BH * a.n_qb);
     return hipGetLastError();
 }
 

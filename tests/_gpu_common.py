@@ -84,6 +84,35 @@ def check_mask_head(gpu_mask: np.ndarray, q: np.ndarray, k: np.ndarray, cfg, row
     return rt, int(diff.sum()), int(rt.exempt.sum())
 
 
+HEAD_ORDER_MIN_ITEMS = 16 * 768     # work lists at least this long are ordered head-major
+HEAD_ORDER_MAX_NQB = 32 * 64
+HEAD_ORDER_MAX_BH = 1024
+
+
+def expected_work_order(cost: np.ndarray, BH: int, n_qb: int) -> np.ndarray:
+    """The forward's work order as the route defines it from the costs: items by cost
+    band floor(log2 cost), highest band first, then ascending item; a long list
+    (at least HEAD_ORDER_MIN_ITEMS items) head-major instead: heads by total cost
+    (highest first, lower head on ties), then band (highest first), then query block."""
+    cost = np.asarray(cost).ravel().astype(np.int64)
+    item = np.arange(cost.size)
+    band = np.floor(np.log2(np.maximum(cost, 1))).astype(np.int64)
+    if cost.size >= HEAD_ORDER_MIN_ITEMS and n_qb <= HEAD_ORDER_MAX_NQB and BH <= HEAD_ORDER_MAX_BH:
+        hcost = cost.reshape(BH, n_qb).sum(axis=1)
+        hrank = np.empty(BH, dtype=np.int64)
+        hrank[np.lexsort((np.arange(BH), -hcost))] = np.arange(BH)
+        return np.lexsort((item, -band, hrank[item // n_qb]))
+    return np.lexsort((item, -band))
+
+
+def check_work_order(rt):
+    """The route's work order equals the one its costs define."""
+    cost = rt.cost.cpu().numpy()
+    B, H, n_qb = cost.shape
+    want = expected_work_order(cost, B * H, n_qb)
+    assert np.array_equal(rt.work_order.cpu().numpy(), want), "work order differs from the cost-defined order"
+
+
 def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
     """Half the spacing of bf16 numbers at |x| (8 significant bits): the most that
     rounding a result to a bf16 output moves it."""

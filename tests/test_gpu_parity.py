@@ -12,8 +12,8 @@ import torch
 from oracle import sparse_attn_ref as R
 from workloads import synth as S
 
-from _gpu_common import (check_lists, check_mask_head, check_out_head, cfg_for, head_np, run_gpu, sa,
-                         sample_blocks, say)
+from _gpu_common import (check_lists, check_mask_head, check_out_head, check_work_order, cfg_for,
+                         expected_work_order, head_np, run_gpu, sa, sample_blocks, say)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -156,9 +156,7 @@ def test_fused_parity(case):
     cost, cost2 = rt.cost.cpu().numpy(), rt2.cost.cpu().numpy()
     if not cfg.no_residual:
         assert np.array_equal(cost[same], cost2[same])
-    c = cost.ravel().astype(np.int64)
-    band = np.floor(np.log2(np.maximum(c, 1))).astype(np.int64)
-    assert np.array_equal(rt.work_order.cpu().numpy(), np.lexsort((np.arange(c.size), -band)))
+    check_work_order(rt)
 
 
 def test_fused_rejects_what_it_cannot_decide_alone():
@@ -378,14 +376,8 @@ def test_work_order_by_cost_band():
     assert torch.equal(rt2.work_order, rt.work_order)
 
 
-def test_work_order_large():
-    """Enough items that the ordering workgroup cuts them into two-chunk tiles and
-    each wave loads its chunks in several batches; per-head query scales spread
-    the costs over many bands."""
-    m = sa()
-    B, H, N, d = 1, 240, 8192, 64
-    say(f"[case] schedule large B{B} H{H} N{N} d{d}")
-    g = torch.Generator(device="cuda").manual_seed(7)
+def _spread_heads(B, H, N, d, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
     # a random direction per 64-token block, shared by its queries and keys, so
     # that block means are informative; query scales from flat to peaked heads
     E = torch.randn(B, H, N // 64, 1, d, device="cuda", generator=g).expand(B, H, N // 64, 64, d).reshape(B, H, N, d)
@@ -393,13 +385,49 @@ def test_work_order_large():
     Q = (s * (E + 0.5 * torch.randn(B, H, N, d, device="cuda", generator=g))).to(torch.bfloat16)
     K = (E + 0.5 * torch.randn(B, H, N, d, device="cuda", generator=g)).to(torch.bfloat16)
     V = torch.randn(B, H, N, d, device="cuda", generator=g).to(torch.bfloat16)
+    return Q, K, V
+
+
+def test_work_order_large():
+    """A long work list (30720 items, past the head-major threshold): heads by total
+    cost, then cost band, then query block.  Head 1 repeats head 0, so two heads
+    tie on total cost (the lower head goes first); per-head query scales spread the
+    costs over many bands."""
+    m = sa()
+    B, H, N, d = 1, 240, 8192, 64
+    say(f"[case] schedule large B{B} H{H} N{N} d{d}")
+    Q, K, V = _spread_heads(B, H, N, d, 7)
+    for T in (Q, K, V):
+        T[:, 1] = T[:, 0]
     rt = m.route(Q, K, V, m.Config(block_q=64, block_k=64, tau=0.02))
     torch.cuda.synchronize()
-    cost = rt.cost.cpu().numpy().ravel().astype(np.int64)
-    assert cost.size == B * H * (N // 64) and cost.size > 64 * 448
+    cost = rt.cost.cpu().numpy()
+    assert cost.size == B * H * (N // 64) and cost.size >= 16 * 768
+    assert np.array_equal(cost[0, 0], cost[0, 1])
     band = np.floor(np.log2(np.maximum(cost, 1))).astype(np.int64)
     assert len(np.unique(band)) > 3
-    assert np.array_equal(rt.work_order.cpu().numpy(), np.lexsort((np.arange(cost.size), -band)))
+    check_work_order(rt)
+    wo = rt.work_order.cpu().numpy()
+    n_qb = cost.shape[-1]
+    heads_in_order = wo[::n_qb] // n_qb
+    assert np.all(wo.reshape(B * H, n_qb) // n_qb == heads_in_order[:, None])   # each head contiguous
+    assert list(heads_in_order).index(0) < list(heads_in_order).index(1)
+
+
+def test_work_order_band_tiles():
+    """A long work list with more heads than the head-major order takes (1100 >
+    1024): the global cost-band order, with more items than the ordering
+    workgroup's 448 tiles of 64 hold (two-chunk tiles, chunks loaded in several
+    batches)."""
+    m = sa()
+    B, H, N, d = 1, 1100, 2048, 64
+    say(f"[case] schedule band tiles B{B} H{H} N{N} d{d}")
+    Q, K, V = _spread_heads(B, H, N, d, 11)
+    rt = m.route(Q, K, V, m.Config(block_q=64, block_k=64, tau=0.02))
+    torch.cuda.synchronize()
+    cost = rt.cost.cpu().numpy()
+    assert cost.size > 64 * 448
+    check_work_order(rt)
 
 
 def test_work_order_many_items():
@@ -410,5 +438,4 @@ def test_work_order_many_items():
     rt, _, _ = run_gpu(Q, K, V, cfg_for(w))
     cost = rt.cost.cpu().numpy().ravel().astype(np.int64)
     assert cost.size > 512 and cost.size % 512
-    band = np.floor(np.log2(np.maximum(cost, 1))).astype(np.int64)
-    assert np.array_equal(rt.work_order.cpu().numpy(), np.lexsort((np.arange(cost.size), -band)))
+    check_work_order(rt)

@@ -10,7 +10,8 @@ import torch
 from oracle import sparse_attn_ref as R
 from workloads import synth as S
 
-from _gpu_common import check_lists, check_mask_head, check_out_head, cfg_for, head_np, run_gpu, sample_blocks, say
+from _gpu_common import (check_lists, check_mask_head, check_out_head, check_work_order, cfg_for, head_np, run_gpu,
+                         sample_blocks, say)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -24,6 +25,7 @@ def check_workload(w, cfgs, heads, blocks_per_head=6, lists=True):
         say(f"[case] {w.name} tau={cfg.tau} mode={cfg.tau_mode} cap={cfg.max_keep} prefix={cfg.n_dense_prefix}")
         rt, O, L = run_gpu(Q, K, V, cfg)
         mask = check_lists(rt, lists=lists)
+        check_work_order(rt)
         stats = rt.row_stats.cpu().numpy()
         assert torch.isfinite(O).all().item() and torch.isfinite(L).all().item()
         nd_tot = 0
