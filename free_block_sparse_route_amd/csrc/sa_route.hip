@@ -61,47 +61,100 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const T *__restrict_
         for (int i = 0; i < 8; ++i) acc[b][i] = 0.f;
     // every load is issued before the first sum (a load under a branch would
     // wait for the one before it); rows past the span re-read the span's last
-    // row and add nothing
+    // row and add nothing.  The loaded words stay raw until they are summed
+    // (bf16: 4 registers per 8 elements instead of 8), so that more workgroups
+    // fit a CU and more loads are in flight.
     constexpr int IT = 128 / RG;
-    float x[IT][8];
+    constexpr int WPL = 8 * sizeof(T) / 4;    // 32-bit words per 8-element load
+    uint32_t x[IT][WPL];
 #pragma unroll
-    for (int it = 0; it < IT; ++it)
-        Ld8<T>::load_f32(X + (size_t)(r0 + min(g + it * RG, span - 1)) * D + c * 8, x[it]);
+    for (int it = 0; it < IT; ++it) {
+        const T *src = X + (size_t)(r0 + min(g + it * RG, span - 1)) * D + c * 8;
+#pragma unroll
+        for (int h = 0; h < WPL / 4; ++h) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint32_t *>(src) + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[it][4 * h + e] = w[e];
+        }
+    }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int r = g + it * RG;
         const bool in = r < span;
         const int b = r >= bs;                 // RG divides bs: uniform per iteration
+        float y[8];
+        if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[b][i] += in ? x[it][i] : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                y[2 * i] = __uint_as_float(x[it][i] << 16);
+                y[2 * i + 1] = __uint_as_float(x[it][i] & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[i] = __uint_as_float(x[it][i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[b][i] += in ? y[i] : 0.f;
     }
-    __shared__ float part[2][RG * D];
+    // Row groups of one wave are combined with lane swaps (the lanes of a
+    // feature chunk sit CH apart), the kernel's four waves through 4 KB of LDS;
+    // then a thread finishes four consecutive features of a block and stores
+    // them at once (16 bytes of fp32 means, 8 bytes each of the bf16 rows).
+    static_assert(kPoolThreads == 4 * kWave && (CH == 16 || CH == 8), "lane layout");
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) part[b][g * D + c * 8 + i] = acc[b][i];
+        for (int i = 0; i < 8; ++i) {
+            float x = acc[b][i];
+            const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            x = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+            const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+            if constexpr (CH == 8)        // lanes 8 apart within a row of 16: rotate by 8
+                x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+            acc[b][i] = x;
+        }
+    __shared__ __attribute__((aligned(16))) float part[4][2][D];
+    const int wave = threadIdx.x / kWave, lane = lane_id();
+    if (lane < CH) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) part[wave][b][lane * 8 + i] = acc[b][i];
+    }
     __syncthreads();
     const int nblk = (span + bs - 1) / bs;
-    if (threadIdx.x < nblk * D) {
-        const int b = threadIdx.x / D, col = threadIdx.x % D;
+    constexpr int Q4 = D / 4;                   // threads per block, four features each
+    if ((int)threadIdx.x < nblk * Q4) {
+        const int b = threadIdx.x / Q4, f = 4 * (threadIdx.x % Q4);
         const int J = (r0 + b * bs) / bs;
-        const int cnt = min(bs, a.N - J * bs);
-        float s = 0.f;                    // other blocks' rows left zeros here
-        for (int gg = 0; gg < RG; ++gg) s += part[b][gg * D + col];
-        const float m = s / (float)cnt;
+        const float inv = 1.f / (float)min(bs, a.N - J * bs);
+        f32x4 m = *reinterpret_cast<const f32x4 *>(&part[0][b][f]);
+#pragma unroll
+        for (int w = 1; w < 4; ++w) m += *reinterpret_cast<const f32x4 *>(&part[w][b][f]);
+        // (other blocks' rows left zeros in the sums)
+        f32x4 mean;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mean[e] = m[e] * inv;
         float *dst = which == 0 ? a.q_mean : which == 1 ? a.k_mean : a.v_mean;
-        dst[((size_t)bh * nb + J) * D + col] = m;
+        *reinterpret_cast<f32x4 *>(dst + ((size_t)bh * nb + J) * D + f) = mean;
         if (which != 0) {
             // residual tile rows: block J -> group J/32, row J%32 (bf16 of the mean)
             // and row 32 + J%32 (bf16 of what that rounding left)
             bf16 *sp = a.kv_split + (((size_t)bh * 2 + (which - 1)) * a.words + J / 32) * 64 * D;
-            const bf16 hi = (bf16)m;
-            sp[(size_t)(J % 32) * D + col] = hi;
-            sp[(size_t)(32 + J % 32) * D + col] = (bf16)(m - (float)hi);
+            bf16x4 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hi[e] = (bf16)mean[e];
+                lo[e] = (bf16)(mean[e] - (float)hi[e]);
+            }
+            *reinterpret_cast<bf16x4 *>(sp + (size_t)(J % 32) * D + f) = hi;
+            *reinterpret_cast<bf16x4 *>(sp + (size_t)(32 + J % 32) * D + f) = lo;
             if (J == nb - 1) {
+                const bf16x4 z = {};
                 for (int r = J % 32 + 1; r < 32; ++r) {
-                    sp[(size_t)r * D + col] = (bf16)0.f;
-                    sp[(size_t)(32 + r) * D + col] = (bf16)0.f;
+                    *reinterpret_cast<bf16x4 *>(sp + (size_t)r * D + f) = z;
+                    *reinterpret_cast<bf16x4 *>(sp + (size_t)(32 + r) * D + f) = z;
                 }
             }
         }
@@ -987,38 +1040,94 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *cos
 // then by query block.  A head's neighbouring query blocks, which keep mostly the
 // same key blocks, then run together and share the key and value tiles in the
 // dies' L2 and the Infinity Cache, while the heads' order keeps the most
-// expensive work first.  One workgroup of 16 waves; a wave places whole heads,
-// holding a head's costs in registers (n_qb <= kHeadChunks * 64).
+// expensive work first.  Two launches:
+//   order_head_local  one wave per head: the head's items sorted stably by band
+//                     into the head's own slot of work_order (its costs held in
+//                     registers, n_qb <= kHeadChunks * 64; band counts and
+//                     running offsets in lane registers, lane r for band row r)
+//   order_head_place  one workgroup: the heads' total costs, their ranks, and each
+//                     head's sorted items moved to slot rank * n_qb (the whole
+//                     list read into registers before any write, W <= 48 * 1024)
 constexpr int kHeadChunks = 32;
-constexpr int kHeadMaxBH = 1024;
+constexpr int kHeadPerThread = 48;
 
-__global__ __launch_bounds__(kOrderThreads) void order_head_kernel(const int32_t *cost, int32_t *work_order, int BH,
-                                                                   int n_qb) {
-    constexpr int NW = kOrderThreads / kWave;
-    __shared__ int32_t hcost[kHeadMaxBH];
-    __shared__ int32_t hrank[kHeadMaxBH];
-    __shared__ int32_t hist[NW][kBands];
-    const int lane = lane_id(), wave = threadIdx.x / kWave;
+__global__ __launch_bounds__(kWave) void order_head_local(const int32_t *cost, int32_t *work_order, int n_qb) {
+    const int h = blockIdx.x, lane = lane_id();
     const int chunks = (n_qb + kWave - 1) / kWave;
-    // costs of head h into registers, every load issued before the first use
-    auto load = [&](int h, int (&c)[kHeadChunks]) {
+    int row[kHeadChunks];
+#pragma unroll
+    for (int r = 0; r < kHeadChunks; ++r) {
+        const int I = r * kWave + lane;
+        row[r] = (r < chunks && I < n_qb) ? cost[(size_t)h * n_qb + I] : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < kHeadChunks; ++r) row[r] = row[r] >= 0 ? kBands - 1 - cost_band(row[r]) : -1;
+    int cnt = 0;                                    // lane r < kBands: items of band row r
+#pragma unroll
+    for (int r = 0; r < kHeadChunks; ++r) {
+        if (r >= chunks) break;
+        uint64_t left = __ballot(row[r] >= 0);
+        while (left) {
+            const int rr = __builtin_amdgcn_readlane(row[r], __builtin_ctzll(left));
+            const uint64_t mr = __ballot(row[r] == rr);
+            cnt += lane == rr ? __popcll(mr) : 0;
+            left &= ~mr;
+        }
+    }
+    // exclusive prefix over the band rows (lanes 0..kBands-1)
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < kBands; o <<= 1) {
+        const int y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
+    }
+    int next = h * n_qb + incl - cnt;               // lane r: where band row r's next item goes
+#pragma unroll
+    for (int r = 0; r < kHeadChunks; ++r) {
+        if (r >= chunks) break;
+        uint64_t left = __ballot(row[r] >= 0);
+        while (left) {
+            const int rr = __builtin_amdgcn_readlane(row[r], __builtin_ctzll(left));
+            const uint64_t mr = __ballot(row[r] == rr);
+            const int base = __builtin_amdgcn_readlane(next, rr);
+            if (row[r] == rr) work_order[base + __popcll(mr & lanes_below())] = h * n_qb + r * kWave + lane;
+            next += lane == rr ? __popcll(mr) : 0;
+            left &= ~mr;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kOrderThreads) void order_head_place(const int32_t *cost, int32_t *work_order, int BH,
+                                                                  int n_qb) {
+    __shared__ int32_t hcost[kOrderThreads];
+    __shared__ int32_t hrank[kOrderThreads];
+    const int t = threadIdx.x, lane = lane_id(), wave = t / kWave;
+    const int W = BH * n_qb;
+    // total cost of each head (exact int32 sums): a wave sums whole heads, its
+    // loads all issued first
+    const int chunks = (n_qb + kWave - 1) / kWave;
+    for (int h = wave; h < BH; h += kOrderThreads / kWave) {
+        int c[kHeadChunks];
 #pragma unroll
         for (int r = 0; r < kHeadChunks; ++r) {
             const int I = r * kWave + lane;
-            c[r] = (r < chunks && I < n_qb) ? cost[(size_t)h * n_qb + I] : -1;
+            c[r] = (r < chunks && I < n_qb) ? cost[(size_t)h * n_qb + I] : 0;
         }
-    };
-    int c[kHeadChunks];
-    for (int h = wave; h < BH; h += NW) {
-        load(h, c);
         int sum = 0;
 #pragma unroll
-        for (int r = 0; r < kHeadChunks; ++r) sum += max(c[r], 0);
-        sum = wave_count(sum);
+        for (int r = 0; r < kHeadChunks; ++r) sum += c[r];
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) sum += __shfl_xor(sum, o, kWave);
         if (lane == 0) hcost[h] = sum;
     }
+    int v[kHeadPerThread];
+#pragma unroll
+    for (int k = 0; k < kHeadPerThread; ++k) {
+        const int i = t + k * kOrderThreads;
+        v[k] = i < W ? work_order[i] : 0;
+    }
     __syncthreads();
-    for (int h = threadIdx.x; h < BH; h += kOrderThreads) {
+    for (int h = t; h < BH; h += kOrderThreads) {
         const int ch = hcost[h];
         int rk = 0;
         for (int g = 0; g < BH; ++g) {
@@ -1028,49 +1137,13 @@ __global__ __launch_bounds__(kOrderThreads) void order_head_kernel(const int32_t
         hrank[h] = rk;
     }
     __syncthreads();
-    for (int h = wave; h < BH; h += NW) {
-        load(h, c);
-        if (lane < kBands) hist[wave][lane] = 0;
-        __builtin_amdgcn_wave_barrier();
-        // band histogram of the head (row 0: highest band)
 #pragma unroll
-        for (int r = 0; r < kHeadChunks; ++r) {
-            if (r >= chunks) break;
-            const int row = c[r] >= 0 ? kBands - 1 - cost_band(c[r]) : -1;
-            uint64_t left = __ballot(row >= 0);
-            while (left) {
-                const int rr = __builtin_amdgcn_readlane(row, __builtin_ctzll(left));
-                const uint64_t mr = __ballot(row == rr);
-                if (lane == 0) hist[wave][rr] += __popcll(mr);
-                left &= ~mr;
-            }
+    for (int k = 0; k < kHeadPerThread; ++k) {
+        const int i = t + k * kOrderThreads;
+        if (i < W) {
+            const int h = i / n_qb;
+            work_order[hrank[h] * n_qb + (i - h * n_qb)] = v[k];
         }
-        __builtin_amdgcn_wave_barrier();
-        // exclusive prefix over the rows: where the head's items of each band start
-        if (lane == 0) {
-            int run = hrank[h] * n_qb;
-            for (int rr = 0; rr < kBands; ++rr) {
-                const int n = hist[wave][rr];
-                hist[wave][rr] = run;
-                run += n;
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int r = 0; r < kHeadChunks; ++r) {
-            if (r >= chunks) break;
-            const int row = c[r] >= 0 ? kBands - 1 - cost_band(c[r]) : -1;
-            uint64_t left = __ballot(row >= 0);
-            while (left) {
-                const int rr = __builtin_amdgcn_readlane(row, __builtin_ctzll(left));
-                const uint64_t mr = __ballot(row == rr);
-                const int base = hist[wave][rr];
-                if (row == rr) work_order[base + __popcll(mr & lanes_below())] = h * n_qb + r * kWave + lane;
-                if (lane == 0) hist[wave][rr] = base + __popcll(mr);
-                left &= ~mr;
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -1080,7 +1153,9 @@ __global__ __launch_bounds__(kOrderThreads) void order_head_kernel(const int32_t
 constexpr int kHeadOrderMinItems = 16 * 768;
 
 bool head_major_order(int BH, int n_qb) {
-    return (int64_t)BH * n_qb >= kHeadOrderMinItems && n_qb <= kHeadChunks * kWave && BH <= kHeadMaxBH;
+    const int64_t W = (int64_t)BH * n_qb;
+    return W >= kHeadOrderMinItems && W <= (int64_t)kHeadPerThread * kOrderThreads && n_qb <= kHeadChunks * kWave &&
+           BH <= kOrderThreads;
 }
 
 // --------------------------------------------------------------------- launch
@@ -1162,10 +1237,14 @@ hipError_t launch_select(int D, const SelectArgs &a, int BH, hipStream_t st, int
     if (e != hipSuccess) return e;
     // (fused routing too: its pre-pass writes the costs of the decisions the
     // forward will take)
-    if (head_major_order(BH, a.n_qb))
-        hipLaunchKernelGGL(order_head_kernel, dim3(1), dim3(kOrderThreads), 0, st, (const int32_t *)a.cost,
+    if (head_major_order(BH, a.n_qb)) {
+        hipLaunchKernelGGL(order_head_local, dim3(BH), dim3(kWave), 0, st, (const int32_t *)a.cost, a.work_order,
+                           a.n_qb);
+        hipError_t e2 = hipGetLastError();
+        if (e2 != hipSuccess) return e2;
+        hipLaunchKernelGGL(order_head_place, dim3(1), dim3(kOrderThreads), 0, st, (const int32_t *)a.cost,
                            a.work_order, BH, a.n_qb);
-    else
+    } else
         hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, st, (const int32_t *)a.cost, a.work_order,
                            BH * a.n_qb);
     return hipGetLastError();

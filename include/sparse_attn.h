@@ -161,9 +161,9 @@ enum {
     SA_BUF_WORK_ORDER,    /* int32 [W]                   work items b*H*n_qb + h*n_qb + I
                                                          by cost band floor(log2(cost)),
                                                          highest band first, ascending item
-                                                         within a band; when W >= 12288,
-                                                         n_qb <= 2048 and B*H <= 1024, head-
-                                                         major instead: heads by total cost
+                                                         within a band; when 12288 <= W
+                                                         <= 49152, n_qb <= 2048 and B*H <=
+                                                         1024, head-major instead: heads by total cost
                                                          (highest first, lower index on
                                                          ties), then band (highest first),
                                                          then I                             */

@@ -84,7 +84,8 @@ def check_mask_head(gpu_mask: np.ndarray, q: np.ndarray, k: np.ndarray, cfg, row
     return rt, int(diff.sum()), int(rt.exempt.sum())
 
 
-HEAD_ORDER_MIN_ITEMS = 16 * 768     # work lists at least this long are ordered head-major
+HEAD_ORDER_MIN_ITEMS = 16 * 768     # work lists of HEAD_ORDER_MIN_ITEMS..HEAD_ORDER_MAX_ITEMS items are
+HEAD_ORDER_MAX_ITEMS = 48 * 1024    # ordered head-major
 HEAD_ORDER_MAX_NQB = 32 * 64
 HEAD_ORDER_MAX_BH = 1024
 
@@ -92,12 +93,13 @@ HEAD_ORDER_MAX_BH = 1024
 def expected_work_order(cost: np.ndarray, BH: int, n_qb: int) -> np.ndarray:
     """The forward's work order as the route defines it from the costs: items by cost
     band floor(log2 cost), highest band first, then ascending item; a long list
-    (at least HEAD_ORDER_MIN_ITEMS items) head-major instead: heads by total cost
+    (HEAD_ORDER_MIN_ITEMS to HEAD_ORDER_MAX_ITEMS items) head-major instead: heads by total cost
     (highest first, lower head on ties), then band (highest first), then query block."""
     cost = np.asarray(cost).ravel().astype(np.int64)
     item = np.arange(cost.size)
     band = np.floor(np.log2(np.maximum(cost, 1))).astype(np.int64)
-    if cost.size >= HEAD_ORDER_MIN_ITEMS and n_qb <= HEAD_ORDER_MAX_NQB and BH <= HEAD_ORDER_MAX_BH:
+    if (HEAD_ORDER_MIN_ITEMS <= cost.size <= HEAD_ORDER_MAX_ITEMS and n_qb <= HEAD_ORDER_MAX_NQB
+            and BH <= HEAD_ORDER_MAX_BH):
         hcost = cost.reshape(BH, n_qb).sum(axis=1)
         hrank = np.empty(BH, dtype=np.int64)
         hrank[np.lexsort((np.arange(BH), -hcost))] = np.arange(BH)

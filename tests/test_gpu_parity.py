@@ -416,11 +416,11 @@ def test_work_order_large():
 
 def test_work_order_band_tiles():
     """A long work list with more heads than the head-major order takes (1100 >
-    1024): the global cost-band order, with more items than the ordering
-    workgroup's 448 tiles of 64 hold (two-chunk tiles, chunks loaded in several
-    batches)."""
+    1024; also more than its 49152 items): the global cost-band order, with more
+    items than the ordering workgroup's 448 tiles of 64 hold (two-chunk tiles,
+    chunks loaded in several batches)."""
     m = sa()
-    B, H, N, d = 1, 1100, 2048, 64
+    B, H, N, d = 1, 1100, 4096, 64
     say(f"[case] schedule band tiles B{B} H{H} N{N} d{d}")
     Q, K, V = _spread_heads(B, H, N, d, 11)
     rt = m.route(Q, K, V, m.Config(block_q=64, block_k=64, tau=0.02))
