@@ -942,9 +942,15 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
     // epilogue: O^T accumulator register r of block db holds feature 32db + 8(r/4) + 4h + r%4
     const float lt = row_pair_sum(sm.l_run);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (row_ok) {
+    // The row index is formed again from the lane number rather than kept from
+    // the prologue: held across the tile loops it does not fit the register
+    // budget of three waves per SIMD and goes to scratch memory.
+    int l32e = lane_id() & 31;
+    asm volatile("" : "+v"(l32e));
+    const int qrow_e = I * a.block_q + wave * 32 + l32e;
+    if (qrow_e < a.Nq) {
         if (a.o32) {                     // fp32 output (an intermediate of a later step)
-            float *orow = a.o32 + kv_part * a.split_o + qhead + (size_t)qrow * D;
+            float *orow = a.o32 + kv_part * a.split_o + qhead + (size_t)qrow_e * D;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -953,7 +959,7 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
                                       sm.acc[db][4 * g + 1] * inv, sm.acc[db][4 * g + 2] * inv,
                                       sm.acc[db][4 * g + 3] * inv);
         } else {
-            T *orow = o + qhead + (size_t)qrow * D;
+            T *orow = o + qhead + (size_t)qrow_e * D;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -963,7 +969,7 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
                                   sm.acc[db][4 * g + 3] * inv);
         }
         if (a.lse && h == 0)
-            a.lse[kv_part * a.split_l + (size_t)bh * a.Nq + qrow] = lt > 0.f ? (sm.m_ref + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+            a.lse[kv_part * a.split_l + (size_t)bh * a.Nq + qrow_e] = lt > 0.f ? (sm.m_ref + log2f(lt)) * 0.69314718055994531f : -INFINITY;
     }
 }
 
