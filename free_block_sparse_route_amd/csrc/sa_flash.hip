@@ -974,19 +974,21 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
 }
 
 // Workgroup i runs on GPU die i % 8: the dispatcher deals workgroups to the 8
-// dies (XCDs) in turn.  In each group of 8 * kDieRun consecutive workgroups, die
-// x takes the kDieRun consecutive work positions x * kDieRun + 0..kDieRun-1 of
-// the group, so that neighbouring query blocks, which keep mostly the same key
-// blocks, meet in one die's L2, while the order of the work list holds at the
-// scale of a group.  The last, partial group keeps the plain order.
-constexpr int kDieRun = 32;
+// dies (XCDs) in turn.  In each group of 8 * run consecutive workgroups, die x
+// takes the run consecutive work positions x * run + 0..run-1 of the group, so
+// that neighbouring query blocks, which keep mostly the same key blocks, meet in
+// one die's L2, while the order of the work list holds at the scale of a group.
+// The last, partial group keeps the plain order.  Runs of 32 for lists ordered
+// by cost band alone, 64 for head-major lists (measured best for each).
+constexpr int kDieRunLog2 = 5;
+constexpr int kDieRunHeadMajorLog2 = 6;
 
-__device__ __forceinline__ int grid_position(int i, int W) {
-    constexpr int kGroup = 8 * kDieRun;
-    const int base = i - i % kGroup;
-    if (base + kGroup > W) return i;
+__device__ __forceinline__ int grid_position(int i, int W, int run_log2) {
+    const int group = 8 << run_log2;
+    const int base = i & ~(group - 1);
+    if (base + group > W) return i;
     const int r = i - base;
-    return base + (r & 7) * kDieRun + (r >> 3);
+    return base + ((r & 7) << run_log2) + (r >> 3);
 }
 
 // One workgroup per work item (query block); kSparse takes the item from the
@@ -996,7 +998,7 @@ __global__ __launch_bounds__((FC<D, BQ>::THREADS)) __attribute__((amdgpu_waves_p
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ o,
     FlashArgs a) {
     using C = FC<D, BQ>;
-    const int p = grid_position(blockIdx.x, a.n_items);
+    const int p = grid_position(blockIdx.x, a.n_items, a.die_run_log2);
     // sparse paths take the route's cost-ordered work list (under fused routing
     // the pre-pass costs the decisions the forward takes)
     // (an entry outside [0, n_items) is clamped: a route that does not belong to
@@ -1026,6 +1028,7 @@ static hipError_t launch_flash_t(const void *q, const void *k, const void *v, vo
     FlashArgs args = a;
     if (args.kv_splits < 1 || kSparse) args.kv_splits = 1;
     args.n_items = BH * a.n_qb * args.kv_splits;
+    args.die_run_log2 = kSparse && head_major_order(BH, a.n_qb) ? kDieRunHeadMajorLog2 : kDieRunLog2;
     hipLaunchKernelGGL(kern, dim3(args.n_items), dim3(C::THREADS), 0, st, (const T *)q, (const T *)k,
                        (const T *)v, (T *)o, args);
     return hipGetLastError();

@@ -54,6 +54,7 @@ struct FlashArgs {
     int tau_mode, n_prefix;
     int min_keep;                        // 0 or 1: the floor of one block
     float scale, ln_tau;
+    int die_run_log2;                    // log2 of the work positions a die takes in a row (set at launch)
 };
 
 struct PermuteArgs {
@@ -74,6 +75,8 @@ constexpr size_t kPamaLdsBudget = 128 * 1024;
 constexpr int kFusedMaxWords = 512;              // decision words a fused work item holds in LDS
 int select_group(int n_kb, int D, int n_qb);
 size_t select_lds_bytes(int G, int n_kb, int D);
+// Whether the route orders the work list head-major (else by cost band alone).
+bool head_major_order(int BH, int n_qb);
 
 // Sparse forward when a.kv_idx != nullptr, dense otherwise.
 hipError_t launch_flash(int dtype, int D, int BQ, const void *q, const void *k, const void *v,
