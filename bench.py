@@ -74,6 +74,11 @@ def parse():
                     help="write profiles/flash_<workload>_<tau-mode>_kernel_stats.md from the kernel_stats.csv of a "
                          "rocprofv3 --kernel-trace --stats run of this script (the library's kernels under the "
                          "profiler's own names), then exit")
+    ap.add_argument("--sq-summary", nargs="+", metavar="CSV",
+                    help="write profiles/route_<workload>_<tau-mode>_sq.md from the counter collections of "
+                         "rocprofv3 --pmc passes over this script (SQ_* and GRBM_GUI_ACTIVE counters, one or more "
+                         "passes) with --trace-csv for the durations: per kernel, the counters' means and the "
+                         "issue and wait fractions they give, then exit")
     ap.add_argument("--pmc-command", default="", help="the command the counter runs used (recorded)")
     ap.add_argument("--no-residual-timing", action="store_true",
                     help="skip timing the forward without the residual fold (its share of the forward)")
@@ -290,6 +295,78 @@ def stats_summary(args):
             f.write(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:,.1f} | "
                     f"{float(r['MinNs']) / 1e3:,.1f} | {float(r['MaxNs']) / 1e3:,.1f} | {float(r['Percentage']):.2f} |\n")
         f.write(f"\nKernel source sha256[:16] (sa_flash.hip): {source_hash()}\n")
+    print(path)
+
+
+def sq_summary(args):
+    """Per-kernel SQ counters from one or more rocprofv3 --pmc passes of this
+    script.  The wave counters (SQ_WAVE_CYCLES, SQ_WAIT_ANY, SQ_WAIT_INST_ANY,
+    SQ_ACTIVE_INST_*) count in units of four cycles; their ratios to
+    SQ_WAVE_CYCLES are the fractions of a wave's lifetime.  Resident waves per
+    CU = 4 SQ_WAVE_CYCLES / (GPU cycles x CUs); GPU cycles = GRBM_GUI_ACTIVE /
+    dies (the profiler sums it over the dies); MFMA busy as in --mfma-summary."""
+    import csv
+    n_xcc, simds, cus = 8, 256 * 4, 256
+    dur = {}
+    if args.trace_csv:
+        for r in csv.DictReader(open(args.trace_csv)):
+            dur.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    vals = {}
+    for path in args.sq_summary:
+        info = os.path.join(os.path.dirname(path), os.path.basename(path).replace("counter_collection", "agent_info"))
+        if os.path.exists(info):
+            for r in csv.DictReader(open(info)):
+                if r.get("Name", "").startswith("gfx"):
+                    n_xcc, simds, cus = int(r["Num_Xcc"]), int(r["Simd_Count"]), int(r["Cu_Count"])
+        per = {}
+        for r in csv.DictReader(open(path)):
+            d = per.setdefault((r["Dispatch_Id"], r["Kernel_Name"]), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        for (_, name), d in per.items():
+            k = vals.setdefault(name, {})
+            for c, x in d.items():
+                k.setdefault(c, []).append(x)
+    lib = ("flash_kernel", "pool_kernel", "select_kernel", "order", "pama_kernel", "permute_kernel")
+    path = os.path.join(ROOT, "profiles", f"route_{args.workload}_{args.tau_mode}_sq.md")
+    with open(path, "w") as f:
+        f.write(f"# SQ counters of the library's kernels: {args.workload}, {args.tau_mode} tau\n\n")
+        f.write("rocprofv3 --pmc passes (each a separate run of the same command), with the kernel trace of a "
+                "run for the durations:\n\n")
+        f.write(f"    {args.pmc_command}\n\n")
+        f.write("Wave counters count in units of four cycles. Fractions are of SQ_WAVE_CYCLES (the waves' "
+                "lifetime): waiting to issue (SQ_WAIT_INST_ANY), waiting on a counter (SQ_WAIT_ANY, memory and "
+                "LDS), issuing (SQ_ACTIVE_INST_ANY). Resident waves per CU = 4 SQ_WAVE_CYCLES / (GPU cycles x "
+                f"{cus} CUs); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GPU cycles x {simds} SIMDs); VALU busy = 4 "
+                f"SQ_ACTIVE_INST_VALU / (GPU cycles x {simds} SIMDs) (a wave-64 VALU instruction holds its SIMD "
+                "four cycles).\n\n")
+        f.write("| kernel | avg us | clock GHz | waves | resident waves / CU | wait to issue | wait on counter | "
+                "issuing | MFMA busy | VALU busy | VALU / wave | SALU / wave | LDS / wave |\n"
+                "|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+        mean = lambda d, c: (sum(d[c]) / len(d[c])) if c in d else None
+        for name, d in vals.items():
+            if not any(k in name for k in lib):
+                continue
+            t = dur.get(name)
+            t = sorted(t)[len(t) // 2] if t else None
+            grbm = mean(d, "GRBM_GUI_ACTIVE")
+            cyc = grbm / n_xcc if grbm else None
+            wc = mean(d, "SQ_WAVE_CYCLES")
+            waves = mean(d, "SQ_WAVES")
+            frac = lambda c: "-" if wc is None or c not in d else f"{mean(d, c) / wc:.2f}"
+            per_wave = lambda c: "-" if waves is None or c not in d else f"{mean(d, c) / waves:,.0f}"
+            res = f"{4 * wc / (cyc * cus):.1f}" if wc and cyc else "-"
+            mb = f"{mean(d, 'SQ_VALU_MFMA_BUSY_CYCLES') / (cyc * simds):.2f}" if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in d else "-"
+            vb = f"{4 * mean(d, 'SQ_ACTIVE_INST_VALU') / (cyc * simds):.2f}" if cyc and "SQ_ACTIVE_INST_VALU" in d else "-"
+            f.write(f"| {_short_kernel(name)} | {'-' if t is None else f'{t * 1e6:,.1f}'} | "
+                    f"{'-' if not (t and cyc) else f'{cyc / t / 1e9:.2f}'} | {'-' if waves is None else f'{waves:,.0f}'} | "
+                    f"{res} | {frac('SQ_WAIT_INST_ANY')} | {frac('SQ_WAIT_ANY')} | {frac('SQ_ACTIVE_INST_ANY')} | "
+                    f"{mb} | {vb} | {per_wave('SQ_INSTS_VALU')} | {per_wave('SQ_INSTS_SALU')} | {per_wave('SQ_INSTS_LDS')} |\n")
+        f.write("\nMeans per dispatch of every counter:\n\n| kernel | counter | mean | dispatches |\n|---|---|---|---|\n")
+        for name, d in vals.items():
+            if not any(k in name for k in lib):
+                continue
+            for c in sorted(d):
+                f.write(f"| {_short_kernel(name)} | {c} | {mean(d, c):,.0f} | {len(d[c])} |\n")
     print(path)
 
 

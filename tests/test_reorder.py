@@ -24,6 +24,33 @@ def test_oracle_full_cube_is_a_unit_step_path_from_the_origin(b):
     assert (steps == 1).all()
 
 
+def test_oracle_order_one_curve_is_the_reflected_gray_code():
+    # J. Skilling, "Programming the Hilbert curve" (2004): with one bit plane the
+    # transposed form of index i is i itself, whose Gray decoding gives the axes,
+    # first axis most significant; the curve on the 2x2x2 cube is therefore the
+    # binary reflected Gray code (a different unit-step path from the origin,
+    # e.g. (0,0,0) (0,0,1) (0,1,1) (1,1,1) ..., fails here)
+    pts = grid_points(2, 2, 2, RO.hilbert_order(2, 2, 2))
+    gray = [(i ^ (i >> 1)) for i in range(8)]
+    want = np.array([[(g >> 2) & 1, (g >> 1) & 1, g & 1] for g in gray])
+    assert (pts == want).all()
+
+
+@pytest.mark.parametrize("b", [2, 3])
+def test_oracle_curve_fills_aligned_subcubes_in_turn(b):
+    # self-similarity of a Hilbert curve: every run of 8^k consecutive points
+    # fills one aligned sub-cube of side 2^k (a snake or other unit-step path
+    # through the cube does not)
+    n = 1 << b
+    pts = grid_points(n, n, n, RO.hilbert_order(n, n, n))
+    for k in range(1, b):
+        run, side = 8 ** k, 1 << k
+        for s in range(0, n ** 3, run):
+            corner = pts[s:s + run] // side
+            assert (corner == corner[0]).all(), (k, s)
+            assert len({tuple(p) for p in pts[s:s + run] % side}) == run
+
+
 def test_oracle_index_is_a_bijection_on_the_cube():
     b = 3
     idx = sorted(RO.hilbert_index(t, y, x, b) for t in range(8) for y in range(8) for x in range(8))
