@@ -575,6 +575,9 @@ def main():
     if args.stats_summary:
         stats_summary(args)
         return
+    if args.sq_summary:
+        sq_summary(args)
+        return
 
     import torch
 
