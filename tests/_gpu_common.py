@@ -39,9 +39,12 @@ def oracle_params(cfg) -> R.RouteParams:
 
 
 def run_gpu(Q, K, V, cfg):
+    """Route and forward; O starts as NaN, so that a row no work item wrote (a
+    work order or workgroup mapping that skips an item) fails every check."""
     m = sa()
     rt = m.route(Q, K, V, cfg)
-    O, L = m.forward(Q, K, V, rt, cfg, lse=True)
+    O = torch.full_like(Q, float("nan"))
+    O, L = m.forward(Q, K, V, rt, cfg, out=O, lse=True)
     torch.cuda.synchronize()
     return rt, O, L
 
