@@ -282,7 +282,7 @@ def stats_summary(args):
     the names the profiler prints."""
     import csv
     rows = [r for r in csv.DictReader(open(args.stats_summary))
-            if any(k in r["Name"] for k in ("flash_kernel", "pool_kernel", "select_kernel", "order_kernel",
+            if any(k in r["Name"] for k in ("flash_kernel", "pool_kernel", "select_kernel", "order_",
                                              "pama_kernel", "permute_kernel", "pr_", "probe_gather"))]
     path = os.path.join(ROOT, "profiles", f"flash_{args.workload}_{args.tau_mode}_kernel_stats.md")
     with open(path, "w") as f:
