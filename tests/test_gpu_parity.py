@@ -414,6 +414,29 @@ def test_work_order_large():
     assert list(heads_in_order).index(0) < list(heads_in_order).index(1)
 
 
+@pytest.mark.parametrize("BH,N,bq", [(24, 2048 * 64, 64), (1024, 12 * 64, 64)],
+                         ids=["items_49152_nqb_2048", "heads_1024_items_12288"])
+def test_work_order_head_major_limits(BH, N, bq):
+    """The head-major order at its limits: 49152 items with 2048 query blocks per
+    head (a whole head's costs in one wave's registers, every thread of the
+    placing workgroup holding 48 items), and 1024 heads at the 12288-item
+    threshold (a thread per head ranking all heads)."""
+    m = sa()
+    say(f"[case] schedule limits BH{BH} N{N} block_q{bq}")
+    Q, K, V = _spread_heads(1, BH, N, 64, 13)
+    rt = m.route(Q, K, V, m.Config(block_q=bq, block_k=64, tau=0.02))
+    torch.cuda.synchronize()
+    cost = rt.cost.cpu().numpy()
+    n_qb = cost.shape[-1]
+    assert cost.size in (16 * 768, 48 * 1024) and n_qb <= 32 * 64
+    check_work_order(rt)
+    wo = rt.work_order.cpu().numpy()
+    heads_in_order = wo[::n_qb] // n_qb
+    assert np.all(wo.reshape(BH, n_qb) // n_qb == heads_in_order[:, None])   # each head contiguous
+    del Q, K, V
+    torch.cuda.empty_cache()
+
+
 def test_work_order_band_tiles():
     """A long work list with more heads than the head-major order takes (1100 >
     1024; also more than its 49152 items): the global cost-band order, with more
