@@ -89,6 +89,48 @@ def test_small_parity(case):
     full_check(w, cfg, label="small")
 
 
+def _random_case(seed):
+    """A seeded draw over the configuration space the route and forward accept:
+    head size, block sizes, dtype, ragged grids, every tau mode with its range,
+    cap, floor, dense prefix, Hilbert order, fused routing, the PAMA proxy, batch
+    and heads."""
+    rng = np.random.default_rng(np.random.SeedSequence((2026, seed)))
+    d = int(rng.choice([64, 128]))
+    bq, bk = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+    dt = "f32" if rng.random() < 0.2 else "bf16"
+    while True:
+        grid = (int(rng.integers(1, 6)), int(rng.integers(1, 11)), int(rng.integers(1, 41)))
+        if grid[0] * grid[1] * grid[2] <= 4000:
+            break
+    mode = [R.RELATIVE, R.ABSOLUTE, R.TOPP][int(rng.choice(3, p=[0.5, 0.25, 0.25]))]
+    tau = (float(10 ** rng.uniform(-3, -0.5)) if mode == R.RELATIVE else
+           float(10 ** rng.uniform(-3, -0.3)) if mode == R.ABSOLUTE else float(rng.uniform(0.0, 0.6)))
+    n_text = int(rng.integers(1, 300)) if rng.random() < 0.3 else 0
+    hil = bool(rng.random() < 0.3)
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    fused = bool(mode != R.TOPP and dt == "bf16" and rng.random() < 0.2)
+    N = grid[0] * grid[1] * grid[2] + n_text
+    n_kb = -(-N // bk)
+    mk = 0 if (fused or rng.random() < 0.6) else int(rng.integers(1, n_kb + 1))
+    mn = int(rng.integers(0, 2)) if fused else int(rng.integers(0, 4))
+    qscale = float(rng.uniform(1.0, 10.0))
+    proxy = R.PAMA if (not fused and rng.random() < 0.15) else R.CENTROID
+    return d, bq, bk, dt, grid, mode, tau, n_text, hil, B, H, fused, mk, mn, qscale, proxy
+
+
+@pytest.mark.parametrize("seed", range(48), ids=[f"rand_{i:02d}" for i in range(48)])
+def test_random_config_parity(seed):
+    """Seeded random configurations against the oracle: masks outside the
+    rounding band, every output row and LSE, lists against the mask."""
+    d, bq, bk, dt, grid, mode, tau, n_text, hil, B, H, fused, mk, mn, qscale, proxy = _random_case(seed)
+    w = S.small(f"rand{seed}", B, H, d, grid, bq, bk, tau, dtype=dt, qscale=qscale, n_text=n_text, hilbert=hil,
+                cfg_id=200 + seed)
+    cfg = cfg_for(w, mode=mode, max_keep=mk, min_keep=mn, fused=fused, proxy=proxy)
+    rt, O, L, mask = full_check(w, cfg, label=f"random{' fused' if fused else ''}{' pama' if proxy == R.PAMA else ''}")
+    if mn >= 1:
+        assert (rt.kv_count.cpu().numpy() >= min(mn, rt.n_kb)).all()
+
+
 # PAMA proxy (PARK page, section 5.1): per-query block attention averaged in the
 # query block; the same selection rules on s = ln A
 PAMA_SMALL = [
