@@ -63,7 +63,10 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const T *__restrict_
     // wait for the one before it); rows past the span re-read the span's last
     // row and add nothing.  The loaded words stay raw until they are summed
     // (bf16: 4 registers per 8 elements instead of 8), so that more workgroups
-    // fit a CU and more loads are in flight.
+    // fit a CU and more loads are in flight.  Loads and result stores carry the
+    // non-temporal hint: the inputs stream through once (with the hint the
+    // route took 1.035 instead of 1.10 ms on the stress shape, and the
+    // attention pass after it was no slower).
     constexpr int IT = 128 / RG;
     constexpr int WPL = 8 * sizeof(T) / 4;    // 32-bit words per 8-element load
     uint32_t x[IT][WPL];
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const T *__restrict_
         const T *src = X + (size_t)(r0 + min(g + it * RG, span - 1)) * D + c * 8;
 #pragma unroll
         for (int h = 0; h < WPL / 4; ++h) {
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint32_t *>(src) + 4 * h);
+            const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint32_t *>(src) + 4 * h));
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[it][4 * h + e] = w[e];
         }
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const T *__restrict_
 #pragma unroll
         for (int e = 0; e < 4; ++e) mean[e] = m[e] * inv;
         float *dst = which == 0 ? a.q_mean : which == 1 ? a.k_mean : a.v_mean;
-        *reinterpret_cast<f32x4 *>(dst + ((size_t)bh * nb + J) * D + f) = mean;
+        __builtin_nontemporal_store(mean, reinterpret_cast<f32x4 *>(dst + ((size_t)bh * nb + J) * D + f));
         if (which != 0) {
             // residual tile rows: block J -> group J/32, row J%32 (bf16 of the mean)
             // and row 32 + J%32 (bf16 of what that rounding left)
@@ -148,8 +151,8 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const T *__restrict_
                 hi[e] = (bf16)mean[e];
                 lo[e] = (bf16)(mean[e] - (float)hi[e]);
             }
-            *reinterpret_cast<bf16x4 *>(sp + (size_t)(J % 32) * D + f) = hi;
-            *reinterpret_cast<bf16x4 *>(sp + (size_t)(32 + J % 32) * D + f) = lo;
+            __builtin_nontemporal_store(hi, reinterpret_cast<bf16x4 *>(sp + (size_t)(J % 32) * D + f));
+            __builtin_nontemporal_store(lo, reinterpret_cast<bf16x4 *>(sp + (size_t)(32 + J % 32) * D + f));
             if (J == nb - 1) {
                 const bf16x4 z = {};
                 for (int r = J % 32 + 1; r < 32; ++r) {
