@@ -62,25 +62,42 @@ constexpr int kPermRows = 64;            // rows per workgroup
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(const uint4 *__restrict__ in, uint4 *__restrict__ out,
                                                                const int32_t *__restrict__ perm, PermuteArgs a) {
+    constexpr int kMaxIt = 8;                 // rows per thread: 64 rows / (256 threads / units), units >= 4
     const int bh = blockIdx.y;
     const int units = a.units;
     const int u = threadIdx.x % units;
     const int step = kPermThreads / units;
+    const int r0 = blockIdx.x * kPermRows + threadIdx.x / units;
     const int r_end = min(a.N, (int)(blockIdx.x + 1) * kPermRows);
     const size_t head = (size_t)bh * a.N * units;
-    for (int r = blockIdx.x * kPermRows + threadIdx.x / units; r < r_end; r += step) {
-        // gather: output row r from input row src; scatter: input row r to output row dst
-        int other = r;
+    // every row's permutation entry, then every row's load, then the stores:
+    // the loads of a thread are all in flight together.  Rows are read and
+    // written once, with the non-temporal hint (on one Hunyuan tensor: 0.25
+    // instead of 0.27 ms, 5.9 TB/s, against one row at a time without it).
+    int src[kMaxIt], dst[kMaxIt];
+#pragma unroll
+    for (int k = 0; k < kMaxIt; ++k) {
+        const int r = r0 + k * step;
+        int other = r, ok = r < r_end;
         const int i = r - a.n0;
-        if (i >= 0 && i < a.n_perm) {
+        if (ok && i >= 0 && i < a.n_perm) {
             const int p = perm[i];
-            if (p < 0 || p >= a.n_perm) continue;           // not a permutation entry: row left as is
+            ok = p >= 0 && p < a.n_perm;                     // not a permutation entry: row left as is
             other = a.n0 + p;
         }
-        const int src = a.inverse ? r : other;
-        const int dst = a.inverse ? other : r;
-        out[head + (size_t)dst * units + u] = in[head + (size_t)src * units + u];
+        src[k] = ok ? (a.inverse ? r : other) : -1;
+        dst[k] = ok ? (a.inverse ? other : r) : -1;
     }
+    typedef unsigned int w4 __attribute__((ext_vector_type(4)));
+    const w4 *iw = reinterpret_cast<const w4 *>(in);
+    w4 *ow = reinterpret_cast<w4 *>(out);
+    w4 v[kMaxIt];
+#pragma unroll
+    for (int k = 0; k < kMaxIt; ++k)
+        v[k] = __builtin_nontemporal_load(iw + head + (size_t)(src[k] < 0 ? 0 : src[k]) * units + u);
+#pragma unroll
+    for (int k = 0; k < kMaxIt; ++k)
+        if (dst[k] >= 0) __builtin_nontemporal_store(v[k], ow + head + (size_t)dst[k] * units + u);
 }
 
 hipError_t launch_permute(const void *in, void *out, const int32_t *perm, const PermuteArgs &a, int BH,
