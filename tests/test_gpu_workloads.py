@@ -100,3 +100,15 @@ def test_stress():
     s = S.query_scales(w)
     heads = [(0, int(s.argmin())), (1, int(s.argmax())), (1, int(np.argsort(s)[len(s) // 2]))]
     check_workload(w, [cfg_for(w)], heads, blocks_per_head=4)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["two_kernel", "fused"])
+def test_key_blocks_at_the_limit(fused):
+    """The largest key-block count the route accepts (16368 blocks of 64 tokens,
+    N = 1047552): one proxy row fills a select workgroup's 64 KB of LDS (one query
+    block per workgroup, the row read from LDS), the kept lists run long, and
+    fused routing holds 512 decision words per work item."""
+    w = S.small("limit", 1, 1, 64, (32, 32, 1023), 128, 64, 0.05, qscale=4.0)
+    assert w.n_kb == 16384 - 16                  # the route's key-block limit
+    cfg = cfg_for(w, fused=fused)
+    check_workload(w, [cfg], [(0, 0)], blocks_per_head=1, lists=not fused)
