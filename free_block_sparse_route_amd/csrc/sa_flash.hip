@@ -451,8 +451,11 @@ struct HeadSrc {
 template <typename T, int D>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const TileDesc &t, const HeadSrc<T> &hs, bool value) {
     if (t.kind == kResidual) {
+        // the value half of a residual tile uses only its 32 rows of bf16 means:
+        // the loads of the 32 remainder rows fall outside the range and fetch
+        // nothing (they land as zeros)
         const size_t off = (size_t)(t.row0 / 32) * kTile * D;
-        return buffer_rsrc((value ? hs.vs : hs.ks) + off, kTile * D * 2);
+        return buffer_rsrc((value ? hs.vs : hs.ks) + off, (value ? kTile / 2 : kTile) * D * 2);
     }
     const uint32_t bytes = (uint32_t)(hs.n_rows - t.row0) * (D * sizeof(T));
     return buffer_rsrc((value ? hs.v : hs.k) + (size_t)t.row0 * D, bytes);
