@@ -1043,20 +1043,51 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t *cos
 // then by query block.  A head's neighbouring query blocks, which keep mostly the
 // same key blocks, then run together and share the key and value tiles in the
 // dies' L2 and the Infinity Cache, while the heads' order keeps the most
-// expensive work first.  Two launches:
-//   order_head_local  one wave per head: the head's items sorted stably by band
-//                     into the head's own slot of work_order (its costs held in
-//                     registers, n_qb <= kHeadChunks * 64; band counts and
-//                     running offsets in lane registers, lane r for band row r)
-//   order_head_place  one workgroup: the heads' total costs, their ranks, and each
-//                     head's sorted items moved to slot rank * n_qb (the whole
-//                     list read into registers before any write, W <= 48 * 1024)
+// expensive work first.  One launch, one workgroup per head, no exchange between
+// workgroups: every workgroup sums the costs of all heads itself (each wave whole
+// heads, their loads issued first; W <= 48 * 1024 costs, read from the L2), ranks
+// its own head among them, and one wave then sorts the head's items stably by
+// band (costs held in registers, n_qb <= kHeadChunks * 64; band counts and
+// running offsets in lane registers, lane r for band row r) into the head's slot
+// rank * n_qb of the list.
 constexpr int kHeadChunks = 32;
-constexpr int kHeadPerThread = 48;
+constexpr int kHeadMaxItems = 48 * 1024;
 
-__global__ __launch_bounds__(kWave) void order_head_local(const int32_t *cost, int32_t *work_order, int n_qb) {
-    const int h = blockIdx.x, lane = lane_id();
+__global__ __launch_bounds__(kOrderThreads) void order_head_kernel(const int32_t *cost, int32_t *work_order, int BH,
+                                                                   int n_qb) {
+    __shared__ int32_t hcost[kOrderThreads];
+    __shared__ int32_t rank_of;
+    const int h = blockIdx.x, t = threadIdx.x, lane = lane_id(), wave = t / kWave;
     const int chunks = (n_qb + kWave - 1) / kWave;
+    for (int g = wave; g < BH; g += kOrderThreads / kWave) {
+        int c[kHeadChunks];
+#pragma unroll
+        for (int r = 0; r < kHeadChunks; ++r) {
+            const int I = r * kWave + lane;
+            c[r] = (r < chunks && I < n_qb) ? cost[(size_t)g * n_qb + I] : 0;
+        }
+        int sum = 0;
+#pragma unroll
+        for (int r = 0; r < kHeadChunks; ++r) sum += c[r];
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) sum += __shfl_xor(sum, o, kWave);
+        if (lane == 0) hcost[g] = sum;
+    }
+    if (t == 0) rank_of = 0;
+    __syncthreads();
+    {
+        const int ch = hcost[h];
+        int before = 0;
+        for (int g = t; g < BH; g += kOrderThreads) {
+            const int cg = hcost[g];
+            before += (cg > ch || (cg == ch && g < h)) ? 1 : 0;
+        }
+        before = (int)wave_sum((float)before);          // exact: at most 1024
+        if (lane == 0 && before) atomicAdd(&rank_of, before);
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    const int base_slot = rank_of * n_qb;
     int row[kHeadChunks];
 #pragma unroll
     for (int r = 0; r < kHeadChunks; ++r) {
@@ -1084,7 +1115,7 @@ __global__ __launch_bounds__(kWave) void order_head_local(const int32_t *cost, i
         const int y = __shfl_up(incl, o, kWave);
         if (lane >= o) incl += y;
     }
-    int next = h * n_qb + incl - cnt;               // lane r: where band row r's next item goes
+    int next = base_slot + incl - cnt;              // lane r: where band row r's next item goes
 #pragma unroll
     for (int r = 0; r < kHeadChunks; ++r) {
         if (r >= chunks) break;
@@ -1100,56 +1131,6 @@ __global__ __launch_bounds__(kWave) void order_head_local(const int32_t *cost, i
     }
 }
 
-__global__ __launch_bounds__(kOrderThreads) void order_head_place(const int32_t *cost, int32_t *work_order, int BH,
-                                                                  int n_qb) {
-    __shared__ int32_t hcost[kOrderThreads];
-    __shared__ int32_t hrank[kOrderThreads];
-    const int t = threadIdx.x, lane = lane_id(), wave = t / kWave;
-    const int W = BH * n_qb;
-    // total cost of each head (exact int32 sums): a wave sums whole heads, its
-    // loads all issued first
-    const int chunks = (n_qb + kWave - 1) / kWave;
-    for (int h = wave; h < BH; h += kOrderThreads / kWave) {
-        int c[kHeadChunks];
-#pragma unroll
-        for (int r = 0; r < kHeadChunks; ++r) {
-            const int I = r * kWave + lane;
-            c[r] = (r < chunks && I < n_qb) ? cost[(size_t)h * n_qb + I] : 0;
-        }
-        int sum = 0;
-#pragma unroll
-        for (int r = 0; r < kHeadChunks; ++r) sum += c[r];
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) sum += __shfl_xor(sum, o, kWave);
-        if (lane == 0) hcost[h] = sum;
-    }
-    int v[kHeadPerThread];
-#pragma unroll
-    for (int k = 0; k < kHeadPerThread; ++k) {
-        const int i = t + k * kOrderThreads;
-        v[k] = i < W ? work_order[i] : 0;
-    }
-    __syncthreads();
-    for (int h = t; h < BH; h += kOrderThreads) {
-        const int ch = hcost[h];
-        int rk = 0;
-        for (int g = 0; g < BH; ++g) {
-            const int cg = hcost[g];
-            rk += (cg > ch || (cg == ch && g < h)) ? 1 : 0;
-        }
-        hrank[h] = rk;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kHeadPerThread; ++k) {
-        const int i = t + k * kOrderThreads;
-        if (i < W) {
-            const int h = i / n_qb;
-            work_order[hrank[h] * n_qb + (i - h * n_qb)] = v[k];
-        }
-    }
-}
-
 // The head-major order serves long work lists (many items per workgroup slot of
 // the attention kernel); shorter lists keep the global cost-band order, whose
 // tail balances better.
@@ -1157,8 +1138,7 @@ constexpr int kHeadOrderMinItems = 16 * 768;
 
 bool head_major_order(int BH, int n_qb) {
     const int64_t W = (int64_t)BH * n_qb;
-    return W >= kHeadOrderMinItems && W <= (int64_t)kHeadPerThread * kOrderThreads && n_qb <= kHeadChunks * kWave &&
-           BH <= kOrderThreads;
+    return W >= kHeadOrderMinItems && W <= kHeadMaxItems && n_qb <= kHeadChunks * kWave && BH <= kOrderThreads;
 }
 
 // --------------------------------------------------------------------- launch
@@ -1241,11 +1221,7 @@ hipError_t launch_select(int D, const SelectArgs &a, int BH, hipStream_t st, int
     // (fused routing too: its pre-pass writes the costs of the decisions the
     // forward will take)
     if (head_major_order(BH, a.n_qb)) {
-        hipLaunchKernelGGL(order_head_local, dim3(BH), dim3(kWave), 0, st, (const int32_t *)a.cost, a.work_order,
-                           a.n_qb);
-        hipError_t e2 = hipGetLastError();
-        if (e2 != hipSuccess) return e2;
-        hipLaunchKernelGGL(order_head_place, dim3(1), dim3(kOrderThreads), 0, st, (const int32_t *)a.cost,
+        hipLaunchKernelGGL(order_head_kernel, dim3(BH), dim3(kOrderThreads), 0, st, (const int32_t *)a.cost,
                            a.work_order, BH, a.n_qb);
     } else
         hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, st, (const int32_t *)a.cost, a.work_order,
