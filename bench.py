@@ -478,6 +478,27 @@ def cold_timing(sa, Q, K, V, rt, O, cfg, calls):
             "flush_bytes": FLUSH_BYTES}
 
 
+def stream_copy_rate(reps=10):
+    """A STREAM-like device copy: median GB/s of copying COPY_BYTES, counting the
+    bytes read and the bytes written; the measured reference for the routing's
+    HBM-bound pass beside the published peak."""
+    import torch
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del a, b
+    return 2.0 * COPY_BYTES / (median(ts) * 1e-3) / 1e9
+
+
 def permute_timing(sa, X, w, reps=10):
     """Token reordering of one [B, H, N, d] tensor into the workload's Hilbert
     order (gather) and back (scatter): median ms and GB/s, counting every row
@@ -642,6 +663,7 @@ def main():
                      + 4.0 * w.B * w.H * rt.n_qb * words)            # bit mask
     route_bytes = route_read + route_written
     route_gbs = route_bytes / (route_ms * 1e-3) / 1e9
+    stream_gbs = stream_copy_rate()
 
     # the forward without the residual fold, on the same route: the residual's share
     noresid = None
@@ -701,7 +723,8 @@ def main():
                      "kernel": "flash_kernel (sparse forward with residual)",
                      "flops_per_launch": exact_flops + resid_flops, "avg_launch_ms": fwd_ms},
         "route": {"ms": route_ms, "bytes": route_bytes, "bytes_read": route_read, "bytes_written": route_written,
-                  "GB/s": route_gbs, "frac_hbm": route_gbs / PEAK_HBM_GBS},
+                  "GB/s": route_gbs, "frac_hbm": route_gbs / PEAK_HBM_GBS,
+                  "stream_copy_GB/s": stream_gbs, "frac_stream_copy": route_gbs / stream_gbs},
         "forward_ms": fwd_ms,
         "dense_ms": dense_ms,
         "speedup_vs_dense": (dense_ms / (route_ms + fwd_ms)) if dense_ms else None,
