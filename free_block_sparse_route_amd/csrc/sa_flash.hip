@@ -640,13 +640,27 @@ __device__ __forceinline__ void drop_absent(f32x16 &s, int lim) {
         if (8 * (r >> 2) + (r & 3) >= lim) s[r] = -INFINITY;
 }
 
+// Negligible weights.  The reference m_ref of a row is set from a row maximum
+// (whose weight is then 1) and only moves up, so the row's normaliser is at
+// least 1 from its first tile on.  A weight below 2^-32 of the reference is
+// below 2^-32 of the normaliser: 32 of them add less than 2^-27 to it, below
+// half of its last bit, and their values move the accumulator as little.  The
+// products with such weights are skipped when they hold for all 32 rows of a
+// wave: the P V of an exact half-tile (its weights still enter the normaliser),
+// and the whole fold of a residual tile (kNegligible: its logits lie more than
+// 32 below the reference).
+constexpr float kNegligible = 32.f;
+constexpr float kNegligibleWeight = 2.3283064365386963e-10f;    // 2^-32
+
 // An exact tile in four scheduling regions: S^T of key rows 0..31; S^T of rows
 // 32..63 while the weights of rows 0..31 are formed; P V of keys 0..31 while
 // the weights of keys 32..63 are formed; P V of keys 32..63.  The MFMAs of one
 // half run while the exponentials of the other are computed.  The weights of a
 // half are formed against the current reference without a row maximum; when
 // one may pass 2^kLazy (seen in their sum) the reference moves to the half's
-// row maximum and they are formed again (rare).  Rows at
+// row maximum and they are formed again (rare).  The P V of a half whose
+// weights are all negligible for every row of the wave (below kNegligibleWeight)
+// is not formed; their sum still enters the normaliser.  Rows at
 // or past `valid` (a partial last tile) are dropped.  wait_v() runs before the
 // first read of Vs.  Accumulator register r of lane (h, l32) holds key row
 // 8(r/4) + 4h + r%4 of its 32-row block.
@@ -705,17 +719,19 @@ __device__ __forceinline__ void tile_exact(const unsigned char *Ks, const unsign
         weights_half(r1, c, sm.m_use(), p2, p3, ps_b);
     }
     sm.l_run += ps_b;
-    pv_half<D, BQ>(Vs, 1, ln, p2, p3, sm.acc);
+    if (__ballot(!(ps_b < kNegligibleWeight)) != 0) pv_half<D, BQ>(Vs, 1, ln, p2, p3, sm.acc);
 }
 
 // A split tile (fp32 rows or residual block means): S^T of its hi rows (0..31)
 // plus its lo rows (32..63) gives the logits of its 32 keys; residual tiles add
 // the logit bias log2(n_J) of dropped blocks and drop kept ones, fp32 tiles drop
 // absent rows.  The P^T operands pa, pc serve the 32 keys of either half.
-// Updates the state.  The lane's keys are 4h + kr, kr = 8(r/4) + r%4: the lane
-// part is folded into per-tile values so that each register tests a constant kr.
+// Updates the state and returns true, or returns false for a negligible
+// residual tile (state unchanged, pa and pc unset).  The lane's keys are 4h + kr,
+// kr = 8(r/4) + r%4: the lane part is folded into per-tile values so that each
+// register tests a constant kr.
 template <int D>
-__device__ __forceinline__ void weights_split(f32x16 &s0, const f32x16 &s1, const TileDesc &cur, float c,
+__device__ __forceinline__ bool weights_split(f32x16 &s0, const f32x16 &s1, const TileDesc &cur, float c,
                                               float lg_bk, float lg_last, int n_kb, int h, SoftState<D> &sm,
                                               bf16x8 &pa, bf16x8 &pc) {
     const uint32_t kh = cur.kept >> (4 * h);
@@ -736,6 +752,8 @@ __device__ __forceinline__ void weights_split(f32x16 &s0, const f32x16 &s1, cons
         mx = fmaxf(mx, x);
     }
     if (__ballot(mx > sm.m_ref + kLazy) != 0) sm.move_ref(row_pair_max(mx));
+    // (a row with no reference yet, m_ref = -inf, never counts as negligible)
+    if (cur.kind == kResidual && __ballot(!(mx < sm.m_ref - kNegligible)) == 0) return false;
     const float m_use = sm.m_use();
     float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
@@ -745,6 +763,7 @@ __device__ __forceinline__ void weights_split(f32x16 &s0, const f32x16 &s1, cons
         if (r < 8) pa[r] = (bf16)p; else pc[r - 8] = (bf16)p;
     }
     sm.l_run += ps0 + ps1;
+    return true;
 }
 
 // One work item: the query block I of head bh = item / n_qb, from its first
@@ -913,14 +932,16 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
             s1 = qk_half<D, BQ>(Kc, 1, ln, qf);
         }
         bf16x8 pa, pc;
-        weights_split<D>(s0, s1, cur, c, lg_bk, lg_last, a.n_kb, h, sm, pa, pc);
-        wait_v();
-        pv_half<D, BQ>(Vc, 0, ln, pa, pc, sm.acc);
-        // Residual tiles take their block-mean values in bf16 (the hi rows): the
-        // rounding moves an output by at most 2^-9 of the mean's magnitude times
-        // the dropped blocks' weight, unlike a key-mean rounding, which the
-        // exponential amplifies.  fp32 rows keep both halves.
-        if (cur.kind == kExactSplit) pv_half<D, BQ>(Vc, 1, ln, pa, pc, sm.acc);
+        const bool fold = weights_split<D>(s0, s1, cur, c, lg_bk, lg_last, a.n_kb, h, sm, pa, pc);
+        wait_v();                       // every wave takes the workgroup barrier
+        if (fold) {
+            pv_half<D, BQ>(Vc, 0, ln, pa, pc, sm.acc);
+            // Residual tiles take their block-mean values in bf16 (the hi rows): the
+            // rounding moves an output by at most 2^-9 of the mean's magnitude times
+            // the dropped blocks' weight, unlike a key-mean rounding, which the
+            // exponential amplifies.  fp32 rows keep both halves.
+            if (cur.kind == kExactSplit) pv_half<D, BQ>(Vc, 1, ln, pa, pc, sm.acc);
+        }
     };
     // The stream gives the exact tiles of the kept blocks first, then the split
     // tiles (all tiles of fp32 inputs, the residual tiles of bf16 ones).

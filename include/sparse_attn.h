@@ -66,7 +66,12 @@
  *    sa_params.dtype (bf16 or fp32).  Products run on bf16 matrix cores with
  *    fp32 accumulation; fp32 inputs enter them as bf16 pairs (the rounded
  *    value and its remainder), the softmax weights as bf16.  Routing
- *    (pooling, proxy, threshold) is fp32 throughout.
+ *    (pooling, proxy, threshold) is fp32 throughout.  Products whose softmax
+ *    weights are all below 2^-32 of the running reference of every row of a
+ *    32-row group (at least 2^-32 below the row's normaliser) are skipped:
+ *    the value products of such a 32-key half of an exact tile, and the whole
+ *    fold of such a residual group.  Their sum is below half of the
+ *    normaliser's last fp32 bit.
  *  - One head's keys (N * d elements) must span at most 2^32 - 1 bytes; larger
  *    is SA_ERR_UNSUPPORTED.
  *  - Every tensor pointer is a DEVICE pointer (hipMalloc or equivalent) of the
