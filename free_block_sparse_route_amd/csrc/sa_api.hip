@@ -178,6 +178,9 @@ sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, co
     pa.n_qb = d.n_qb; pa.n_kb = d.n_kb;
     pa.q_mean = r->q_mean; pa.k_mean = r->k_mean; pa.v_mean = r->v_mean;
     pa.kv_split = (sa::bf16 *)r->kv_split; pa.words = d.words;
+    // the select kernel pools the query blocks itself, except under the PAMA
+    // proxy, whose kernel reads Q row by row
+    pa.first = (p->flags & SA_FLAG_PAMA) ? 0 : 1;
     hipError_t e = sa::launch_pool(p->dtype, p->d, q, k, v, pa, (int)d.BH, st);
     if (e != hipSuccess) return hip_fail(e, "route: pool launch");
 
@@ -191,6 +194,7 @@ sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, co
     sa_.ln_tau = p->tau > 0.f ? (float)log((double)p->tau) : -INFINITY;
     sa_.topp_target = 1.f - p->tau;
     sa_.stats_only = (p->flags & SA_FLAG_FUSED) ? 1 : 0;
+    sa_.q = q; sa_.q_bf16 = p->dtype == SA_BF16 ? 1 : 0;
     sa_.q_mean = r->q_mean; sa_.k_mean = r->k_mean;
     sa_.kv_count = r->kv_count; sa_.kv_idx = r->kv_idx; sa_.cost = r->cost;
     sa_.work_order = r->work_order; sa_.kv_mask = r->kv_mask;

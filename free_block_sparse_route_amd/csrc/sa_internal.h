@@ -13,6 +13,7 @@ constexpr int kMaxKeyBlocks = 16384 - 16;       // n_kb limit: one proxy row at 
 
 struct PoolArgs {
     int N, block_q, block_k, n_qb, n_kb, words;
+    int first;                           // first tensor pooled: 0 = Q, K, V; 1 = K, V (select pools Q)
     float *q_mean, *k_mean, *v_mean;
     bf16 *kv_split;                      // [BH][2][words][64][D] hi/lo residual tiles
 };
@@ -24,7 +25,10 @@ struct SelectArgs {
     int stats_only;                      // fused routing pre-pass: row statistics only
     float scale, ln_tau;                 // ln_tau = -inf when tau == 0
     float topp_target;                   // 1 - tau: proxy mass the TOPP mode retains
-    const float *q_mean, *k_mean;
+    const void *q;                       // queries [BH][N][D]: select pools its own query blocks
+    int q_bf16;                          // q's element type: 1 = bf16, 0 = fp32
+    float *q_mean;                       // written by select (pooled there)
+    const float *k_mean;
     int32_t *kv_count, *kv_idx, *cost, *work_order;
     uint32_t *kv_mask;
     float *row_stats;

@@ -2,10 +2,12 @@
 // cost-ordered work list for the attention kernel.
 //
 // pool    one workgroup per (b, h, 128-token span, tensor) reduces the span's
-//         one or two blocks to fp32 means with coalesced 16-byte loads
-//         (HBM-bound; the inputs are read exactly once).  Block centroids: PARK page,
-//         section 4.1.
-// select  one workgroup per (b, h, group of G query blocks): the G proxy rows
+//         one or two blocks of K or V (and, for the PAMA proxy, Q) to fp32 means
+//         with coalesced 16-byte loads (HBM-bound; the inputs are read exactly
+//         once).  Block centroids: PARK page, section 4.1.
+// select  one workgroup per (b, h, group of G query blocks) first pools its G
+//         query blocks (so that these reads of Q overlap the latency-bound
+//         proxy and selection work of other workgroups), then the G proxy rows
 //         s_IJ = scale * qbar_I . kbar_J are computed in fp32 into LDS (never
 //         written to memory, Sol-Attn abstract: no materialised proxy map),
 //         then one wave per row takes the row max / log-sum-exp, compares with
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const T *__restrict_
                                                             const T *__restrict__ v,
                                                             PoolArgs a) {
     // one workgroup per 128-token span of one tensor: one block of 128 or two of 64
-    const int which = blockIdx.z;            // 0 = q, 1 = k, 2 = v
+    const int which = blockIdx.z + a.first;  // 0 = q, 1 = k, 2 = v
     const int bh = blockIdx.y;
     const int bs = which == 0 ? a.block_q : a.block_k;
     const int nb = which == 0 ? a.n_qb : a.n_kb;
@@ -557,6 +559,85 @@ __device__ __forceinline__ void launder(SelectArgs &a) {
     launder_global(a.row_stats);
 }
 
+// The means of a group's query blocks (PARK page, section 4.1), one block per
+// wave at a time: a lane sums one 16-byte chunk of the rows of its row group
+// (the wave loads kWave / CH rows at once, NB loads in flight per lane; rows
+// past a ragged block re-read its last row and add nothing), lane swaps
+// combine the row groups, and lanes 0..CH-1 store the block's means to qs
+// ([g][D] in LDS) and to q_mean.
+template <typename T, int D>
+__device__ __forceinline__ void pool_queries(const T *__restrict__ Q, int bh, int I0, int g_cnt,
+                                             const SelectArgs &a, float *qs) {
+    constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte chunk
+    constexpr int CH = D / EPC;                  // chunks per row: 8, 16 or 32
+    constexpr int RG = kWave / CH;               // rows per wave load
+    constexpr int NB = 64 / RG < 8 ? 64 / RG : 8;
+    static_assert(CH == 8 || CH == 16 || CH == 32, "lane layout");
+    static_assert(64 % (NB * RG) == 0, "a batch of loads divides a block");
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int c = lane % CH, rg = lane / CH;
+    const int bq = a.block_q;
+    for (int g = wave; g < g_cnt; g += kSelectThreads / kWave) {
+        const int r0 = (I0 + g) * bq;
+        const int span = min(bq, a.N - r0);
+        const T *X = Q + ((size_t)bh * a.N + r0) * D + c * EPC;
+        float acc[EPC];
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) acc[i] = 0.f;
+        for (int it0 = 0; it0 < bq; it0 += NB * RG) {
+            u32x4 w[NB];
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int r = min(it0 + j * RG + rg, span - 1);
+                w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(X + (size_t)r * D));
+            }
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const bool in = it0 + j * RG + rg < span;
+                float y[EPC];
+                if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        y[2 * i] = __uint_as_float(w[j][i] << 16);
+                        y[2 * i + 1] = __uint_as_float(w[j][i] & 0xffff0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y[i] = __uint_as_float(w[j][i]);
+                }
+#pragma unroll
+                for (int i = 0; i < EPC; ++i) acc[i] += in ? y[i] : 0.f;
+            }
+        }
+        // the row groups of a chunk sit CH lanes apart
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) {
+            float x = acc[i];
+            const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            x = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+            if constexpr (CH <= 16) {
+                const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+                x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+            }
+            if constexpr (CH == 8)        // lanes 8 apart within a row of 16: rotate by 8
+                x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+            acc[i] = x;
+        }
+        if (lane < CH) {
+            const float inv = 1.f / (float)span;
+            float *dst = a.q_mean + ((size_t)bh * a.n_qb + I0 + g) * D + c * EPC;
+#pragma unroll
+            for (int h = 0; h < EPC / 4; ++h) {
+                f32x4 m;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m[e] = acc[4 * h + e] * inv;
+                *reinterpret_cast<f32x4 *>(qs + g * D + c * EPC + 4 * h) = m;
+                __builtin_nontemporal_store(m, reinterpret_cast<f32x4 *>(dst + 4 * h));
+            }
+        }
+    }
+}
+
 // R: proxy row chunks of 64 held in registers (R * 64 >= n_kb), 0: longer rows
 // are read from LDS.
 template <int D, int G, int R>
@@ -570,6 +651,10 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     const int g_cnt = min(G, a.n_qb - I0);
     const int n = a.n_kb;
     float *S = smem;                                      // [G][n]
+    float *qs = smem;                                     // [G][D] query means, before S is formed
+    if (a.q_bf16) pool_queries<bf16, D>((const bf16 *)a.q, bh, I0, g_cnt, a, qs);
+    else pool_queries<float, D>((const float *)a.q, bh, I0, g_cnt, a, qs);
+    __syncthreads();
     {
         // Proxy rows on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, fp32
         // products and sums): a wave takes 16 key blocks at a time and forms
@@ -584,10 +669,10 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
         float qv[KS];
         {
             const bool ok = i16 < g_cnt;
-            const float *src = a.q_mean + ((size_t)bh * a.n_qb + I0 + (ok ? i16 : 0)) * D + kg * KS;
+            const float *src = qs + (ok ? i16 : 0) * D + kg * KS;
 #pragma unroll
             for (int e = 0; e < KS; e += 4) {
-                const f32x4 y = *reinterpret_cast<const f32x4 *>(src + e);   // row clamped: in bounds
+                const f32x4 y = *reinterpret_cast<const f32x4 *>(src + e);   // row clamped: pooled
                 const f32x4 x = ok ? y : f32x4{};
                 qv[e] = x[0];
                 qv[e + 1] = x[1];
@@ -595,6 +680,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
                 qv[e + 3] = x[3];
             }
         }
+        __syncthreads();                                  // S overwrites qs
         const float *kb = a.k_mean + (size_t)bh * n * D;
         const int n_sl = (n + 15) / 16;
         constexpr int kStride = kSelectThreads / kWave;
@@ -1145,7 +1231,7 @@ bool head_major_order(int BH, int n_qb) {
 template <typename T, int D>
 static hipError_t launch_pool_t(const void *q, const void *k, const void *v, const PoolArgs &a,
                                 int BH, hipStream_t st) {
-    dim3 grid((a.N + 127) / 128, BH, 3);
+    dim3 grid((a.N + 127) / 128, BH, 3 - a.first);
     hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(kPoolThreads), 0, st,
                        (const T *)q, (const T *)k, (const T *)v, a);
     return hipGetLastError();
@@ -1171,8 +1257,9 @@ int select_group(int n_kb, int D, int n_qb) {
 }
 
 size_t select_lds_bytes(int G, int n_kb, int D) {
-    (void)D;
-    return ((size_t)G * n_kb + 3) / 4 * 4 * sizeof(float);
+    // the proxy rows, or the group's query means before them
+    const size_t rows = ((size_t)G * n_kb + 3) / 4 * 4;
+    return (rows > (size_t)G * D ? rows : (size_t)G * D) * sizeof(float);
 }
 
 template <int D, int G, int R>
