@@ -559,37 +559,35 @@ __device__ __forceinline__ void launder(SelectArgs &a) {
     launder_global(a.row_stats);
 }
 
-// The means of a group's query blocks (PARK page, section 4.1), one block per
-// wave at a time: a lane sums one 16-byte chunk of the rows of its row group
-// (the wave loads kWave / CH rows at once, NB loads in flight per lane; rows
-// past a ragged block re-read its last row and add nothing), lane swaps
-// combine the row groups, and lanes 0..CH-1 store the block's means to qs
-// ([g][D] in LDS) and to q_mean.
+// Query-block means inside the select kernel (PARK page, section 4.1), one
+// block per wave at a time: a lane sums one 16-byte chunk of the rows of its row group (the wave
+// loads kWave / CH rows at once, NB loads in flight per lane; rows past a
+// ragged block re-read its last row and add nothing), and lane swaps combine
+// the row groups, so that every lane ends with its chunk's sums.
 template <typename T, int D>
-__device__ __forceinline__ void pool_queries(const T *__restrict__ Q, int bh, int I0, int g_cnt,
-                                             const SelectArgs &a, float *qs) {
-    constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte chunk
-    constexpr int CH = D / EPC;                  // chunks per row: 8, 16 or 32
-    constexpr int RG = kWave / CH;               // rows per wave load
-    constexpr int NB = 64 / RG < 8 ? 64 / RG : 8;
+struct BlockPool {
+    static constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte chunk
+    static constexpr int CH = D / EPC;                  // chunks per row: 8, 16 or 32
+    static constexpr int RG = kWave / CH;               // rows per wave load
+    static constexpr int NB = 64 / RG < 8 ? 64 / RG : 8;
     static_assert(CH == 8 || CH == 16 || CH == 32, "lane layout");
     static_assert(64 % (NB * RG) == 0, "a batch of loads divides a block");
-    const int lane = lane_id(), wave = threadIdx.x / kWave;
-    const int c = lane % CH, rg = lane / CH;
-    const int bq = a.block_q;
-    for (int g = wave; g < g_cnt; g += kSelectThreads / kWave) {
-        const int r0 = (I0 + g) * bq;
-        const int span = min(bq, a.N - r0);
-        const T *X = Q + ((size_t)bh * a.N + r0) * D + c * EPC;
+
+    // means of rows [r0, r0 + span) of X ([rows][D]), a block of bs rows
+    static __device__ __forceinline__ void means(const T *__restrict__ X, int r0, int span, int bs,
+                                                 float (&m)[EPC]) {
+        const int lane = lane_id();
+        const int c = lane % CH, rg = lane / CH;
+        const T *src = X + (size_t)r0 * D + c * EPC;
         float acc[EPC];
 #pragma unroll
         for (int i = 0; i < EPC; ++i) acc[i] = 0.f;
-        for (int it0 = 0; it0 < bq; it0 += NB * RG) {
+        for (int it0 = 0; it0 < bs; it0 += NB * RG) {
             u32x4 w[NB];
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const int r = min(it0 + j * RG + rg, span - 1);
-                w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(X + (size_t)r * D));
+                w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + (size_t)r * D));
             }
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
@@ -610,6 +608,7 @@ __device__ __forceinline__ void pool_queries(const T *__restrict__ Q, int bh, in
             }
         }
         // the row groups of a chunk sit CH lanes apart
+        const float inv = 1.f / (float)span;
 #pragma unroll
         for (int i = 0; i < EPC; ++i) {
             float x = acc[i];
@@ -621,22 +620,32 @@ __device__ __forceinline__ void pool_queries(const T *__restrict__ Q, int bh, in
             }
             if constexpr (CH == 8)        // lanes 8 apart within a row of 16: rotate by 8
                 x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
-            acc[i] = x;
+            m[i] = x * inv;
         }
-        if (lane < CH) {
-            const float inv = 1.f / (float)span;
-            float *dst = a.q_mean + ((size_t)bh * a.n_qb + I0 + g) * D + c * EPC;
+    }
+
+    // The group's g_cnt query blocks, wave w taking blocks w, w + 8, ...:
+    // their means go to qs ([g][D] in LDS) and to q_mean.
+    static __device__ __forceinline__ void run(const SelectArgs &a, int bh, int I0, int g_cnt, float *qs) {
+        const int lane = lane_id(), wave = threadIdx.x / kWave;
+        const int c = lane % CH;
+        const T *X = (const T *)a.q + (size_t)bh * a.N * D;
+        for (int g = wave; g < g_cnt; g += kSelectThreads / kWave) {
+            const int r0 = (I0 + g) * a.block_q;
+            float m[EPC];
+            means(X, r0, min(a.block_q, a.N - r0), a.block_q, m);
+            if (lane < CH) {
+                float *dst = a.q_mean + ((size_t)bh * a.n_qb + I0 + g) * D + c * EPC;
 #pragma unroll
-            for (int h = 0; h < EPC / 4; ++h) {
-                f32x4 m;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) m[e] = acc[4 * h + e] * inv;
-                *reinterpret_cast<f32x4 *>(qs + g * D + c * EPC + 4 * h) = m;
-                __builtin_nontemporal_store(m, reinterpret_cast<f32x4 *>(dst + 4 * h));
+                for (int h = 0; h < EPC / 4; ++h) {
+                    const f32x4 x = {m[4 * h], m[4 * h + 1], m[4 * h + 2], m[4 * h + 3]};
+                    *reinterpret_cast<f32x4 *>(qs + g * D + c * EPC + 4 * h) = x;
+                    __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(dst + 4 * h));
+                }
             }
         }
     }
-}
+};
 
 // R: proxy row chunks of 64 held in registers (R * 64 >= n_kb), 0: longer rows
 // are read from LDS.
@@ -652,8 +661,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     const int n = a.n_kb;
     float *S = smem;                                      // [G][n]
     float *qs = smem;                                     // [G][D] query means, before S is formed
-    if (a.q_bf16) pool_queries<bf16, D>((const bf16 *)a.q, bh, I0, g_cnt, a, qs);
-    else pool_queries<float, D>((const float *)a.q, bh, I0, g_cnt, a, qs);
+    if (a.q_bf16) BlockPool<bf16, D>::run(a, bh, I0, g_cnt, qs);
+    else BlockPool<float, D>::run(a, bh, I0, g_cnt, qs);
     __syncthreads();
     {
         // Proxy rows on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, fp32

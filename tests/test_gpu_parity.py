@@ -328,34 +328,54 @@ def test_identical_keys_make_residual_exact():
         assert np.abs(o - O_ref).max() <= 3e-2
 
 
+def _check_means_and_tiles(w, rt, Qc, Kc, Vc):
+    """Block means against the oracle's pooling (fp32 accumulation against fp64:
+    relative 1e-5) on every head, and the residual tiles: hi rows = bf16 of the
+    mean, lo rows = bf16 of the remainder, zero rows past the last block."""
+    bq, bk = w.block_q, w.block_k
+    qm, km, vm = (t.cpu().double().numpy() for t in (rt.q_mean, rt.k_mean, rt.v_mean))
+    for b in range(w.B):
+        for h in range(w.H):
+            q, k, v = head_np(Qc, b, h), head_np(Kc, b, h), head_np(Vc, b, h)
+            for got, ref in ((qm[b, h], R.pool(q, bq)), (km[b, h], R.pool(k, bk)), (vm[b, h], R.pool(v, bk))):
+                scale = np.abs(ref).max()
+                assert np.abs(got - ref).max() <= 1e-5 * scale, (b, h)
+    split = rt.kv_split.cpu()                                  # [B, H, 2, words, 64, d]
+    n_kb = rt.n_kb
+    for which, means in ((0, rt.k_mean), (1, rt.v_mean)):
+        mf = means.cpu()                                       # [B, H, n_kb, d] fp32
+        hi = mf.to(torch.bfloat16)
+        lo = (mf - hi.float()).to(torch.bfloat16)
+        t = split[:, :, which].reshape(w.B, w.H, -1, 64, w.d)  # [B, H, groups, 64, d]
+        rows = t.shape[2] * 32
+        got_hi = t[:, :, :, :32].reshape(w.B, w.H, rows, w.d)
+        got_lo = t[:, :, :, 32:].reshape(w.B, w.H, rows, w.d)
+        assert torch.equal(got_hi[:, :, :n_kb], hi) and torch.equal(got_lo[:, :, :n_kb], lo), which
+        assert not got_hi[:, :, n_kb:].any() and not got_lo[:, :, n_kb:].any(), which
+
+
 @pytest.mark.parametrize("dt,bq,bk", [("bf16", 128, 64), ("f32", 64, 128)])
 def test_route_means_and_residual_tiles(dt, bq, bk):
-    """The route's block means against the oracle's pooling (fp32 accumulation
-    against fp64: relative 1e-5), and the residual tiles: hi rows = bf16 of the
-    mean, lo rows = bf16 of the remainder, zero rows past the last block."""
+    """The route's block means and residual tiles on a small launch (the pool
+    kernel pools keys and values, the select kernel the queries)."""
     w = S.small("means", 1, 2, 64 if dt == "f32" else 128, (3, 7, 19), bq, bk, 0.01, dtype=dt)
     say(f"[case] means {dt} {bq}x{bk} N{w.N}")
     Qc, Kc, Vc, Q, K, V = make(w)
     rt, _, _ = run_gpu(Q, K, V, cfg_for(w))
-    qm, km, vm = (t.cpu().double().numpy() for t in (rt.q_mean, rt.k_mean, rt.v_mean))
-    split = rt.kv_split.cpu()
-    for h in range(w.H):
-        q, k, v = head_np(Qc, 0, h), head_np(Kc, 0, h), head_np(Vc, 0, h)
-        for got, ref in ((qm[0, h], R.pool(q, bq)), (km[0, h], R.pool(k, bk)), (vm[0, h], R.pool(v, bk))):
-            scale = np.abs(ref).max()
-            assert np.abs(got - ref).max() <= 1e-5 * scale
-        for which, means in ((0, km[0, h]), (1, vm[0, h])):
-            t = split[0, h, which].reshape(-1, 64, w.d)          # [groups, 64, d]
-            n_kb = means.shape[0]
-            mf = torch.from_numpy(means).float()
-            hi = mf.to(torch.bfloat16)
-            lo = (mf - hi.float()).to(torch.bfloat16)
-            for J in range(t.shape[0] * 32):
-                g, r = divmod(J, 32)
-                if J < n_kb:
-                    assert torch.equal(t[g, r], hi[J]) and torch.equal(t[g, 32 + r], lo[J])
-                else:
-                    assert not t[g, r].any() and not t[g, 32 + r].any()
+    _check_means_and_tiles(w, rt, Qc, Kc, Vc)
+
+
+@pytest.mark.parametrize("B,H,grid,bq,bk,dt", [(1, 256, (5, 7, 233), 64, 128, "bf16"),
+                                               (2, 256, (1, 13, 315), 64, 64, "f32")])
+def test_route_means_large_launch(B, H, grid, bq, bk, dt):
+    """The same checks on launches of 2048 select workgroups (16 query blocks
+    each, pooled by the workgroup itself) over 256 and 512 heads; ragged last
+    blocks (N = 8155 and 4095)."""
+    w = S.small("means_big", B, H, 64, grid, bq, bk, 0.01, dtype=dt)
+    say(f"[case] means large launch {dt} B{B} H{H} N{w.N} {bq}x{bk}")
+    Qc, Kc, Vc, Q, K, V = make(w)
+    rt, _, _ = run_gpu(Q, K, V, cfg_for(w))
+    _check_means_and_tiles(w, rt, Qc, Kc, Vc)
 
 
 def test_deterministic_and_route_reuse():
