@@ -573,25 +573,21 @@ struct BlockPool {
     static_assert(CH == 8 || CH == 16 || CH == 32, "lane layout");
     static_assert(64 % (NB * RG) == 0, "a batch of loads divides a block");
 
-    // means of rows [r0, r0 + span) of X ([rows][D]), a block of bs rows
-    static __device__ __forceinline__ void means(const T *__restrict__ X, int r0, int span, int bs,
-                                                 float (&m)[EPC]) {
-        const int lane = lane_id();
-        const int c = lane % CH, rg = lane / CH;
-        const T *src = X + (size_t)r0 * D + c * EPC;
-        float acc[EPC];
-#pragma unroll
-        for (int i = 0; i < EPC; ++i) acc[i] = 0.f;
+    // sums of the rows of a block of bs rows at src (this lane's chunk), of
+    // which the first span are present (kRagged: span < bs)
+    template <bool kRagged>
+    static __device__ __forceinline__ void sums(const T *__restrict__ src, int span, int bs, int rg,
+                                                float (&acc)[EPC]) {
         for (int it0 = 0; it0 < bs; it0 += NB * RG) {
             u32x4 w[NB];
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const int r = min(it0 + j * RG + rg, span - 1);
+                const int r = kRagged ? min(it0 + j * RG + rg, span - 1) : it0 + j * RG + rg;
                 w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + (size_t)r * D));
             }
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const bool in = it0 + j * RG + rg < span;
+                const bool in = !kRagged || it0 + j * RG + rg < span;
                 float y[EPC];
                 if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -607,6 +603,20 @@ struct BlockPool {
                 for (int i = 0; i < EPC; ++i) acc[i] += in ? y[i] : 0.f;
             }
         }
+    }
+
+    // means of rows [r0, r0 + span) of X ([rows][D]), a block of bs rows
+    static __device__ __forceinline__ void means(const T *__restrict__ X, int r0, int span, int bs,
+                                                 float (&m)[EPC]) {
+        const int lane = lane_id();
+        const int c = lane % CH, rg = lane / CH;
+        const T *src = X + (size_t)r0 * D + c * EPC;
+        float acc[EPC];
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) acc[i] = 0.f;
+        // every block but a ragged last one is whole: no clamp, no masked adds
+        if (span == bs) sums<false>(src, span, bs, rg, acc);
+        else sums<true>(src, span, bs, rg, acc);
         // the row groups of a chunk sit CH lanes apart
         const float inv = 1.f / (float)span;
 #pragma unroll
