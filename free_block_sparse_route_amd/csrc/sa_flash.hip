@@ -76,6 +76,7 @@ struct TileDesc {
     int row0;      // first token (exact) or first pooled block (residual)
     int valid;     // rows of the tile that exist
     uint32_t kept; // residual: kept bits of the tile's 32 pooled blocks (1 past n_kb)
+    float lo;      // residual: bound on the norms of its key-mean remainder rows (inf: none)
 };
 
 // The tile sequence of one work item; every thread steps it identically and
@@ -87,6 +88,7 @@ struct TileDesc {
 struct TileStream {
     const kconst<int32_t> *list;
     const kconst<uint32_t> *mask;
+    const kconst<float> *lo_max;   // the head's remainder-norm bounds, or null
     int cnt, li, sub;
     int exact_rows, exact_kind;
     int dense_tiles, t;
@@ -146,6 +148,7 @@ struct TileStream {
                 o.row0 = cur * 32;
                 o.valid = kTile;
                 o.kept = bits | ~vmask;
+                o.lo = lo_max ? lo_max[cur] : INFINITY;
                 return true;
             }
         }
@@ -158,6 +161,7 @@ struct TileStream {
 // word that holds a dropped block: the same tile order as a route's lists.
 struct BitStream {
     const uint32_t *lw;       // decision words in LDS
+    const kconst<float> *lo_max;   // the head's remainder-norm bounds, or null
     int words, wi, sub, rt, n_rt;
     int exact_rows, exact_kind;
     uint32_t bits;            // kept bits of word wi not yet visited
@@ -203,6 +207,7 @@ struct BitStream {
                 o.row0 = cur * 32;
                 o.valid = kTile;
                 o.kept = kept | ~vmask;
+                o.lo = lo_max ? lo_max[cur] : INFINITY;
                 return true;
             }
         }
@@ -766,6 +771,33 @@ __device__ __forceinline__ bool weights_split(f32x16 &s0, const f32x16 &s1, cons
     return true;
 }
 
+// Early test of a residual tile from the bf16 part of its key means alone: the
+// remainder rows add c q_i . lo_J to a logit, at most qnc * t.lo in size
+// (Cauchy-Schwarz, with the bounds of both norms).  Returns true when even
+// with that added (and a slack over the fp32 rounding of the full logit) every
+// dropped block's logit lies more than kNegligible below the reference for
+// all 32 rows of the wave: weights_split would then find the tile negligible,
+// so it is skipped without forming the remainder part.
+template <int D>
+__device__ __forceinline__ bool residual_negligible(const f32x16 &s0, const TileDesc &t, float c, float lg_bk,
+                                                    float lg_last, int n_kb, int h, const SoftState<D> &sm,
+                                                    float qnc) {
+    const float margin = qnc * t.lo;
+    if (!(margin < INFINITY)) return false;        // no bound for this tile
+    const uint32_t kh = t.kept >> (4 * h);
+    const int last = n_kb - 1 - t.row0 - 4 * h;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int kr = 8 * (r >> 2) + (r & 3);
+        const bool drop = ((kh >> kr) & 1u) == 0;
+        mx = fmaxf(mx, drop ? s0[r] * c + (kr == last ? lg_last : lg_bk) : -INFINITY);
+    }
+    const float ub = mx == -INFINITY ? -INFINITY
+                                     : mx + margin * (1.f + 1.f / 256.f) + fabsf(mx) * (1.f / 1048576.f) + 1.f / 64.f;
+    return __ballot(!(ub < sm.m_ref - kNegligible)) == 0;
+}
+
 // One work item: the query block I of head bh = item / n_qb, from its first
 // tile to its output rows.  kSparse: kept-list and residual tiles from a route;
 // otherwise every key tile (dense).  LDS: K0/V0 and K1/V1, one tile each.
@@ -849,6 +881,10 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
             ts.n_rt = 0;
         }
     }
+    // bf16 residual tiles may be found negligible before their remainder part
+    // is formed (residual_negligible): the route's per-tile bounds
+    ts.lo_max = (kSparse && !kF32 && a.k_lo_max) ? (const kconst<float> *)(a.k_lo_max + (size_t)bh * a.mask_words)
+                                                 : nullptr;
     ts.prime(a);
     HeadSrc<T> hs;
     hs.k = k + head;
@@ -859,6 +895,25 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
     const float lg_bk = log2f((float)a.block_k);
     const float lg_last = log2f((float)(a.N - (a.n_kb - 1) * a.block_k));
     const float c = a.scale_log2;
+    // c times an upper bound on the norms of the wave's 32 query rows (raised by
+    // 2^-10 over the rounding of the sums and the root): with a tile's bound
+    // on its remainder rows it bounds what they add to any logit of the tile
+    float qnc = INFINITY;
+    if constexpr (kSparse && !kF32) {
+        if (a.k_lo_max) {
+            float ss = 0.f;
+#pragma unroll
+            for (int c2 = 0; c2 < D / 16; ++c2)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = (float)qf[c2][e];
+                    ss = fmaf(x, x, ss);
+                }
+            const float m = wave_max(row_pair_sum(ss));
+            qnc = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(__builtin_sqrtf(m)))) *
+                  (1.f + 1.f / 1024.f) * c;
+        }
+    }
 
     SoftState<D> sm;
 #pragma unroll
@@ -922,17 +977,24 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
     };
     auto split = [&](const unsigned char *Kc, const unsigned char *Vc, auto &wait_v) {
         f32x16 s0, s1;
+        bf16x8 pa, pc;
+        bool fold;
         if constexpr (kF32) {
             f32x16 s2[2];
             qk_tile<D, BQ, true>(Kc, ln, qf, ql, s2);
             s0 = s2[0];
             s1 = s2[1];
+            fold = weights_split<D>(s0, s1, cur, c, lg_bk, lg_last, a.n_kb, h, sm, pa, pc);
         } else {
+            // bf16 split tiles are residual tiles: the key means' bf16 part
+            // first, and the remainder part only if the tile may matter
             s0 = qk_half<D, BQ>(Kc, 0, ln, qf);
-            s1 = qk_half<D, BQ>(Kc, 1, ln, qf);
+            fold = !residual_negligible<D>(s0, cur, c, lg_bk, lg_last, a.n_kb, h, sm, qnc);
+            if (fold) {
+                s1 = qk_half<D, BQ>(Kc, 1, ln, qf);
+                fold = weights_split<D>(s0, s1, cur, c, lg_bk, lg_last, a.n_kb, h, sm, pa, pc);
+            }
         }
-        bf16x8 pa, pc;
-        const bool fold = weights_split<D>(s0, s1, cur, c, lg_bk, lg_last, a.n_kb, h, sm, pa, pc);
         wait_v();                       // every wave takes the workgroup barrier
         if (fold) {
             pv_half<D, BQ>(Vc, 0, ln, pa, pc, sm.acc);

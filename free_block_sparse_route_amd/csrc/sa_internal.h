@@ -32,6 +32,8 @@ struct SelectArgs {
     int32_t *kv_count, *kv_idx, *cost, *work_order;
     uint32_t *kv_mask;
     float *row_stats;
+    const bf16 *kv_split;                // residual tiles written by pool (read for the bounds)
+    float *k_lo_max;                     // [BH][mask_words] remainder-row norm bound per residual tile
 };
 
 struct FlashArgs {
@@ -49,6 +51,7 @@ struct FlashArgs {
     int n_items;                         // B * H * n_qb
     const uint32_t *kv_mask;
     const bf16 *kv_split;                // [BH][2][words][64][D] hi/lo residual tiles
+    const float *k_lo_max;               // [BH][words] remainder-row norm bounds, or null (no early skip)
     float *lse;                          // nullable
     // fused routing (kv_idx unused): the decisions are taken in the kernel
     // from the block means and the pre-pass row statistics, and written out

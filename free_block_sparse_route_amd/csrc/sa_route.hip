@@ -657,6 +657,39 @@ struct BlockPool {
     }
 };
 
+// Bounds for the forward's early test of residual tiles: for each residual
+// tile of the head (group g of 32 key blocks), an upper bound on the Euclidean
+// norm of its 32 key-mean remainder rows, as stored by the pool kernel.  A
+// wave per tile, the tiles dealt over the head's select workgroups: lane
+// (r, half) sums the exact squares of half of remainder row r in fp32, the two
+// halves meet by a lane swap, the wave takes the largest row, and the bound is
+// its square root raised by 2^-10 (over the rounding of the sums and the root).
+template <int D>
+__device__ __forceinline__ void remainder_bounds(const SelectArgs &a, int bh, int grp, int n_grp) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int r = lane >> 1, hf = lane & 1;
+    constexpr int NL = D / 16;                     // 16-byte loads per half row
+    for (int g = grp + wave * n_grp; g < a.mask_words; g += (kSelectThreads / kWave) * n_grp) {
+        const bf16 *row = a.kv_split + ((size_t)bh * 2 * a.mask_words + g) * 64 * D + (size_t)(32 + r) * D +
+                          hf * (D / 2);
+        u32x4 w[NL];
+#pragma unroll
+        for (int j = 0; j < NL; ++j) w[j] = *reinterpret_cast<const u32x4 *>(row + 8 * j);
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x0 = __uint_as_float(w[j][i] << 16), x1 = __uint_as_float(w[j][i] & 0xffff0000u);
+                ss = fmaf(x0, x0, ss);
+                ss = fmaf(x1, x1, ss);
+            }
+        ss += dpp_f(ss, 0xB1);                     // the row's other half (lane ^ 1)
+        const float m = wave_max(ss);
+        if (lane == 0) a.k_lo_max[(size_t)bh * a.mask_words + g] = __builtin_sqrtf(m) * (1.f + 1.f / 1024.f);
+    }
+}
+
 // R: proxy row chunks of 64 held in registers (R * 64 >= n_kb), 0: longer rows
 // are read from LDS.
 template <int D, int G, int R>
@@ -673,6 +706,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     float *qs = smem;                                     // [G][D] query means, before S is formed
     if (a.q_bf16) BlockPool<bf16, D>::run(a, bh, I0, g_cnt, qs);
     else BlockPool<float, D>::run(a, bh, I0, g_cnt, qs);
+    remainder_bounds<D>(a, bh, I0 / G, n_grp);
     __syncthreads();
     {
         // Proxy rows on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, fp32

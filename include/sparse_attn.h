@@ -172,6 +172,16 @@ enum {
                                                          (highest first, lower index on
                                                          ties), then band (highest first),
                                                          then I                             */
+    SA_BUF_K_LO_MAX,      /* fp32 [B,H,words]            for each residual tile: an upper
+                                                         bound on the Euclidean norm of its
+                                                         32 key-mean remainder rows (the
+                                                         forward skips a tile whose logits
+                                                         are provably negligible without
+                                                         forming their remainder part);
+                                                         written by centroid routes only:
+                                                         a route under SA_FLAG_PAMA leaves
+                                                         it unset and the forward of such
+                                                         a route does not read it          */
     SA_ROUTE_NBUF
 };
 
@@ -186,6 +196,7 @@ typedef struct sa_route {
     float    *row_stats;
     int32_t  *cost;
     int32_t  *work_order;
+    float    *k_lo_max;
     int32_t   kv_idx_cap;     /* row length of kv_idx, >= sparse_attn_kv_idx_cap(p) */
 } sa_route;
 
