@@ -302,6 +302,33 @@ def test_early_residual_test_changes_nothing(fused):
     assert torch.equal(O1, O2) and torch.equal(L1, L2)
 
 
+def test_pama_route_bounds_unused():
+    """A PAMA route does not write the remainder bounds and its forward does not
+    read them: bounds of NaN (read, they would turn every early test off) and of
+    -inf (read, they would skip every residual tile) give bitwise the same
+    output and LSE."""
+    m = sa()
+    w = S.small("pama_lo", 1, 2, 128, (4, 12, 40), 128, 64, 0.1, qscale=4.0)
+    say(f"[case] PAMA route ignores the bounds N{w.N}")
+    _, _, _, Q, K, V = make(w)
+    cfg = cfg_for(w, mode=R.TOPP, proxy=R.PAMA)
+    rt = m.route(Q, K, V, cfg)
+    rt.k_lo_max.fill_(float("nan"))
+    O1, L1 = m.forward(Q, K, V, rt, cfg, lse=True)
+    rt.k_lo_max.fill_(float("-inf"))
+    O2, L2 = m.forward(Q, K, V, rt, cfg, lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+    # control: a centroid route's forward reads them (-inf bounds drop its residual tiles)
+    cfg_c = cfg_for(w, mode=R.TOPP)
+    rt_c = m.route(Q, K, V, cfg_c)
+    O3 = m.forward(Q, K, V, rt_c, cfg_c)
+    rt_c.k_lo_max.fill_(float("-inf"))
+    O4 = m.forward(Q, K, V, rt_c, cfg_c)
+    torch.cuda.synchronize()
+    assert not torch.equal(O3, O4)
+
+
 # ----------------------------------------------------------------------------- dense path
 @pytest.mark.parametrize("d,bq,bk,dt", [(128, 128, 128, "bf16"), (128, 128, 64, "bf16"), (64, 64, 64, "f32"),
                                         (128, 64, 128, "bf16")])
