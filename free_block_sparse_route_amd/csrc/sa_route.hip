@@ -7,7 +7,8 @@
 //         once).  Block centroids: PARK page, section 4.1.
 // select  one workgroup per (b, h, group of G query blocks) first pools its G
 //         query blocks (so that these reads of Q overlap the latency-bound
-//         proxy and selection work of other workgroups), then the G proxy rows
+//         proxy and selection work of other workgroups) and a share of the
+//         head's residual-tile remainder bounds, then the G proxy rows
 //         s_IJ = scale * qbar_I . kbar_J are computed in fp32 into LDS (never
 //         written to memory, Sol-Attn abstract: no materialised proxy map),
 //         then one wave per row takes the row max / log-sum-exp, compares with
