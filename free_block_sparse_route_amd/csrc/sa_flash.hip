@@ -13,10 +13,7 @@
 //                   is skipped
 // and folds both kinds into the same running max and normaliser.  A split tile
 // holds bf16(x) in rows 0..31 and bf16(x - bf16(x)) in rows 32..63, so the same
-// 64-column MFMA sequence yields hi + lo products (about 2^-16 relative).  A
-// bf16 residual tile forms its hi products first: with the route's bound on
-// its remainder rows, a tile whose logits are provably negligible for every
-// row of the wave skips its lo products and its P V.
+// 64-column MFMA sequence yields hi + lo products (about 2^-16 relative).
 //
 // Products are formed transposed: S^T = K Q^T and O^T = V^T P^T.  The MFMA
 // accumulator then gives each lane one query row (lane & 31) and 32 of the
