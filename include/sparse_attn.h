@@ -209,8 +209,9 @@ int32_t sparse_attn_kv_idx_cap(const sa_params *p);
  * to bytes[0..SA_ROUTE_NBUF-1].  Host only; no HIP calls. */
 sa_status sparse_attn_route_sizes(const sa_params *p, int32_t kv_idx_cap, size_t *bytes);
 
-/* Step 1 (routing).  Reads q, k, v once; writes every buffer of *r.  Nothing
- * of size n_qb x n_kb is written except the kv_idx lists and the bit mask. */
+/* Step 1 (routing).  Reads q, k, v once; writes every buffer of *r (k_lo_max
+ * only without SA_FLAG_PAMA, which may then be NULL).  Nothing of size
+ * n_qb x n_kb is written except the kv_idx lists and the bit mask. */
 sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, const void *v,
                             const sa_route *r, void *stream);
 
