@@ -26,7 +26,7 @@ FLAG_PAMA = 2
 FLAG_FUSED = 4
 CENTROID, PAMA = 0, 1          # routing proxy
 BUFFERS = ("kv_count", "kv_idx", "kv_mask", "q_mean", "k_mean", "v_mean", "kv_split", "row_stats", "cost",
-           "work_order", "k_lo_max")
+           "work_order", "k_bounds")
 
 
 class SaParams(ctypes.Structure):
@@ -192,7 +192,7 @@ class Route:
         self.row_stats = torch.empty((B, H, self.n_qb, 2), dtype=torch.float32, **e)
         self.cost = torch.empty((B, H, self.n_qb), dtype=torch.int32, **e)
         self.work_order = torch.empty((B * H * self.n_qb,), dtype=torch.int32, **e)
-        self.k_lo_max = torch.empty((B, H, words), dtype=torch.float32, **e)
+        self.k_bounds = torch.empty((B, H, words, 2), dtype=torch.float32, **e)
         for name, nbytes in zip(BUFFERS, sizes):
             t = getattr(self, name)
             if t.numel() * t.element_size() != nbytes:

@@ -152,7 +152,7 @@ sa_status sparse_attn_route_sizes(const sa_params *p, int32_t kv_idx_cap, size_t
     bytes[SA_BUF_ROW_STATS] = rows * 2 * 4;
     bytes[SA_BUF_COST] = rows * 4;
     bytes[SA_BUF_WORK_ORDER] = rows * 4;
-    bytes[SA_BUF_K_LO_MAX] = (size_t)d.BH * d.words * 4;
+    bytes[SA_BUF_K_BOUNDS] = (size_t)d.BH * d.words * 2 * 4;
     return SA_OK;
 }
 
@@ -168,7 +168,7 @@ sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, co
         (s = check_ptr(r->k_mean, "route.k_mean")) || (s = check_ptr(r->v_mean, "route.v_mean")) ||
         (s = check_ptr(r->kv_split, "route.kv_split")) || (s = check_ptr(r->row_stats, "route.row_stats")) || (s = check_ptr(r->cost, "route.cost")) ||
         (s = check_ptr(r->work_order, "route.work_order")) ||
-        (!(p->flags & SA_FLAG_PAMA) && (s = check_ptr(r->k_lo_max, "route.k_lo_max"))))
+        (!(p->flags & SA_FLAG_PAMA) && (s = check_ptr(r->k_bounds, "route.k_bounds"))))
         return s;
     if (r->kv_idx_cap < min_cap(p))
         return fail(SA_ERR_CAPACITY, "route.kv_idx_cap %d < required %d", r->kv_idx_cap, min_cap(p));
@@ -202,7 +202,7 @@ sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, co
     sa_.work_order = r->work_order; sa_.kv_mask = r->kv_mask;
     sa_.row_stats = r->row_stats;
     sa_.kv_split = (const sa::bf16 *)r->kv_split;
-    sa_.k_lo_max = r->k_lo_max;
+    sa_.k_bounds = r->k_bounds;
     e = sa::launch_select(p->d, sa_, (int)d.BH, st, p->dtype, (p->flags & SA_FLAG_PAMA) ? q : nullptr);
     if (e != hipSuccess) return hip_fail(e, "route: select launch");
     return SA_OK;
@@ -223,8 +223,8 @@ static sa_status run_flash(const sa_params *p, const void *q, const void *k, con
     if (r) {
         fa.kv_idx_cap = r->kv_idx_cap;
         fa.residual = ((p->flags & SA_FLAG_NO_RESIDUAL) || no_residual) ? 0 : 1;
-        // the remainder-norm bounds of a centroid route (a PAMA route has none)
-        fa.k_lo_max = (fa.residual && !(p->flags & SA_FLAG_PAMA)) ? r->k_lo_max : nullptr;
+        // the residual-tile norm bounds of a centroid route (a PAMA route has none)
+        fa.k_bounds = (fa.residual && !(p->flags & SA_FLAG_PAMA)) ? r->k_bounds : nullptr;
         fa.kv_count = r->kv_count; fa.kv_idx = r->kv_idx; fa.work_order = r->work_order;
         fa.kv_mask = r->kv_mask; fa.kv_split = (const sa::bf16 *)r->kv_split;
         if (p->flags & SA_FLAG_FUSED) {
@@ -258,7 +258,7 @@ sa_status sparse_attn_forward(const sa_params *p, const void *q, const void *k, 
         (s = check_ptr(r->kv_mask, "route.kv_mask")) ||
         (s = check_ptr(r->kv_split, "route.kv_split")) ||
         (s = check_ptr(r->work_order, "route.work_order")) ||
-        (!(p->flags & (SA_FLAG_PAMA | SA_FLAG_NO_RESIDUAL)) && (s = check_ptr(r->k_lo_max, "route.k_lo_max"))))
+        (!(p->flags & (SA_FLAG_PAMA | SA_FLAG_NO_RESIDUAL)) && (s = check_ptr(r->k_bounds, "route.k_bounds"))))
         return s;
     if ((p->flags & SA_FLAG_FUSED) &&
         ((s = check_ptr(r->q_mean, "route.q_mean")) || (s = check_ptr(r->k_mean, "route.k_mean")) ||

@@ -65,6 +65,8 @@ template <int D> __device__ __forceinline__ int swz_v(int r) {
     return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 enum : int {
     kExact = 0,        // 64 bf16 tokens of a kept block
     kExactSplit = 1,   // 32 fp32 tokens of a kept block (fp32 inputs)
@@ -77,6 +79,7 @@ struct TileDesc {
     int valid;     // rows of the tile that exist
     uint32_t kept; // residual: kept bits of the tile's 32 pooled blocks (1 past n_kb)
     float lo;      // residual: bound on the norms of its key-mean remainder rows (inf: none)
+    float kmax;    // residual: bound on the norms of its key means (inf: none)
 };
 
 // The tile sequence of one work item; every thread steps it identically and
@@ -88,7 +91,7 @@ struct TileDesc {
 struct TileStream {
     const kconst<int32_t> *list;
     const kconst<uint32_t> *mask;
-    const kconst<float> *lo_max;   // the head's remainder-norm bounds, or null
+    const kconst<f32x2> *bounds;   // the head's residual-tile norm bounds, or null
     int cnt, li, sub;
     int exact_rows, exact_kind;
     int dense_tiles, t;
@@ -148,7 +151,9 @@ struct TileStream {
                 o.row0 = cur * 32;
                 o.valid = kTile;
                 o.kept = bits | ~vmask;
-                o.lo = lo_max ? lo_max[cur] : INFINITY;
+                const f32x2 bd = bounds ? (f32x2)bounds[cur] : f32x2{INFINITY, INFINITY};
+                o.kmax = bd.x;
+                o.lo = bd.y;
                 return true;
             }
         }
@@ -161,7 +166,7 @@ struct TileStream {
 // word that holds a dropped block: the same tile order as a route's lists.
 struct BitStream {
     const uint32_t *lw;       // decision words in LDS
-    const kconst<float> *lo_max;   // the head's remainder-norm bounds, or null
+    const kconst<f32x2> *bounds;   // the head's residual-tile norm bounds, or null
     int words, wi, sub, rt, n_rt;
     int exact_rows, exact_kind;
     uint32_t bits;            // kept bits of word wi not yet visited
@@ -207,7 +212,9 @@ struct BitStream {
                 o.row0 = cur * 32;
                 o.valid = kTile;
                 o.kept = kept | ~vmask;
-                o.lo = lo_max ? lo_max[cur] : INFINITY;
+                const f32x2 bd = bounds ? (f32x2)bounds[cur] : f32x2{INFINITY, INFINITY};
+                o.kmax = bd.x;
+                o.lo = bd.y;
                 return true;
             }
         }
@@ -798,6 +805,21 @@ __device__ __forceinline__ bool residual_negligible(const f32x16 &s0, const Tile
     return __ballot(!(ub < sm.m_ref - kNegligible)) == 0;
 }
 
+// Test of a residual tile from norms alone, before any of its products: a
+// dropped block's logit c q_i . kbar_J + log2 n_J is at most qnc * t.kmax +
+// log2 block_k (Cauchy-Schwarz with the bounds of both norms; the last block's
+// bias is the smaller).  True when that, with a slack over the fp32 rounding
+// of the logit, lies more than kNegligible below the reference of every row
+// of the wave: residual_negligible would then hold as well, so the tile is
+// skipped without changing any result.
+template <int D>
+__device__ __forceinline__ bool residual_negligible_by_norms(const TileDesc &t, float qnc, float lg_bk,
+                                                             const SoftState<D> &sm) {
+    const float ub = qnc * t.kmax * (1.f + 1.f / 256.f) + lg_bk + 1.f / 64.f;
+    if (!(ub < INFINITY)) return false;             // no bound for this tile
+    return __ballot(!(ub < sm.m_ref - kNegligible)) == 0;
+}
+
 // One work item: the query block I of head bh = item / n_qb, from its first
 // tile to its output rows.  kSparse: kept-list and residual tiles from a route;
 // otherwise every key tile (dense).  LDS: K0/V0 and K1/V1, one tile each.
@@ -883,8 +905,9 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
     }
     // bf16 residual tiles may be found negligible before their remainder part
     // is formed (residual_negligible): the route's per-tile bounds
-    ts.lo_max = (kSparse && !kF32 && a.k_lo_max) ? (const kconst<float> *)(a.k_lo_max + (size_t)bh * a.mask_words)
-                                                 : nullptr;
+    ts.bounds = (kSparse && !kF32 && a.k_bounds)
+                    ? (const kconst<f32x2> *)(a.k_bounds + (size_t)bh * a.mask_words * 2)
+                    : nullptr;
     ts.prime(a);
     HeadSrc<T> hs;
     hs.k = k + head;
@@ -900,7 +923,7 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
     // on its remainder rows it bounds what they add to any logit of the tile
     float qnc = INFINITY;
     if constexpr (kSparse && !kF32) {
-        if (a.k_lo_max) {
+        if (a.k_bounds) {
             float ss = 0.f;
 #pragma unroll
             for (int c2 = 0; c2 < D / 16; ++c2)
@@ -986,10 +1009,14 @@ __device__ __forceinline__ void run_item(int item, const T *__restrict__ q, cons
             s1 = s2[1];
             fold = weights_split<D>(s0, s1, cur, c, lg_bk, lg_last, a.n_kb, h, sm, pa, pc);
         } else {
-            // bf16 split tiles are residual tiles: the key means' bf16 part
-            // first, and the remainder part only if the tile may matter
-            s0 = qk_half<D, BQ>(Kc, 0, ln, qf);
-            fold = !residual_negligible<D>(s0, cur, c, lg_bk, lg_last, a.n_kb, h, sm, qnc);
+            // bf16 split tiles are residual tiles: first a test from the
+            // norms alone, then the key means' bf16 part, and the remainder
+            // part only if the tile may still matter
+            fold = !residual_negligible_by_norms<D>(cur, qnc, lg_bk, sm);
+            if (fold) {
+                s0 = qk_half<D, BQ>(Kc, 0, ln, qf);
+                fold = !residual_negligible<D>(s0, cur, c, lg_bk, lg_last, a.n_kb, h, sm, qnc);
+            }
             if (fold) {
                 s1 = qk_half<D, BQ>(Kc, 1, ln, qf);
                 fold = weights_split<D>(s0, s1, cur, c, lg_bk, lg_last, a.n_kb, h, sm, pa, pc);

@@ -33,7 +33,7 @@ struct SelectArgs {
     uint32_t *kv_mask;
     float *row_stats;
     const bf16 *kv_split;                // residual tiles written by pool (read for the bounds)
-    float *k_lo_max;                     // [BH][mask_words] remainder-row norm bound per residual tile
+    float *k_bounds;                     // [BH][mask_words][2] key-mean and remainder norm bounds per residual tile
 };
 
 struct FlashArgs {
@@ -51,7 +51,7 @@ struct FlashArgs {
     int n_items;                         // B * H * n_qb
     const uint32_t *kv_mask;
     const bf16 *kv_split;                // [BH][2][words][64][D] hi/lo residual tiles
-    const float *k_lo_max;               // [BH][words] remainder-row norm bounds, or null (no early skip)
+    const float *k_bounds;               // [BH][words][2] key-mean and remainder norm bounds, or null (no early tests)
     float *lse;                          // nullable
     // fused routing (kv_idx unused): the decisions are taken in the kernel
     // from the block means and the pre-pass row statistics, and written out

@@ -8,7 +8,7 @@
 // select  one workgroup per (b, h, group of G query blocks) first pools its G
 //         query blocks (so that these reads of Q overlap the latency-bound
 //         proxy and selection work of other workgroups) and a share of the
-//         head's residual-tile remainder bounds, then the G proxy rows
+//         head's residual-tile norm bounds, then the G proxy rows
 //         s_IJ = scale * qbar_I . kbar_J are computed in fp32 into LDS (never
 //         written to memory, Sol-Attn abstract: no materialised proxy map),
 //         then one wave per row takes the row max / log-sum-exp, compares with
@@ -658,36 +658,49 @@ struct BlockPool {
     }
 };
 
-// Bounds for the forward's early test of residual tiles: for each residual
-// tile of the head (group g of 32 key blocks), an upper bound on the Euclidean
-// norm of its 32 key-mean remainder rows, as stored by the pool kernel.  A
-// wave per tile, the tiles dealt over the head's select workgroups: lane
-// (r, half) sums the exact squares of half of remainder row r in fp32, the two
-// halves meet by a lane swap, the wave takes the largest row, and the bound is
-// its square root raised by 2^-10 (over the rounding of the sums and the root).
+// Bounds for the forward's early tests of residual tiles: for each residual
+// tile of the head (group g of 32 key blocks), upper bounds on the Euclidean
+// norms of its 32 key-mean remainder rows and of its 32 key means as the
+// forward forms them (bf16 part plus remainder, both as the pool kernel stored
+// them).  A wave per tile, the tiles dealt over the head's select workgroups:
+// lane (r, half) sums the squares of half of row r in fp32 (the bf16 part plus
+// remainder is exact in fp32), the two halves meet by a lane swap, the wave
+// takes the largest row, and a bound is its square root raised by 2^-10 (over
+// the rounding of the squares, the sums and the root).
 template <int D>
-__device__ __forceinline__ void remainder_bounds(const SelectArgs &a, int bh, int grp, int n_grp) {
+__device__ __forceinline__ void residual_bounds(const SelectArgs &a, int bh, int grp, int n_grp) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int r = lane >> 1, hf = lane & 1;
     constexpr int NL = D / 16;                     // 16-byte loads per half row
     for (int g = grp + wave * n_grp; g < a.mask_words; g += (kSelectThreads / kWave) * n_grp) {
-        const bf16 *row = a.kv_split + ((size_t)bh * 2 * a.mask_words + g) * 64 * D + (size_t)(32 + r) * D +
-                          hf * (D / 2);
-        u32x4 w[NL];
+        const bf16 *hi_row = a.kv_split + ((size_t)bh * 2 * a.mask_words + g) * 64 * D + (size_t)r * D + hf * (D / 2);
+        const bf16 *lo_row = hi_row + 32 * D;
+        u32x4 wh[NL], wl[NL];
 #pragma unroll
-        for (int j = 0; j < NL; ++j) w[j] = *reinterpret_cast<const u32x4 *>(row + 8 * j);
-        float ss = 0.f;
+        for (int j = 0; j < NL; ++j) {
+            wh[j] = *reinterpret_cast<const u32x4 *>(hi_row + 8 * j);
+            wl[j] = *reinterpret_cast<const u32x4 *>(lo_row + 8 * j);
+        }
+        float ss_lo = 0.f, ss_mean = 0.f;
 #pragma unroll
         for (int j = 0; j < NL; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float x0 = __uint_as_float(w[j][i] << 16), x1 = __uint_as_float(w[j][i] & 0xffff0000u);
-                ss = fmaf(x0, x0, ss);
-                ss = fmaf(x1, x1, ss);
+                const float l0 = __uint_as_float(wl[j][i] << 16), l1 = __uint_as_float(wl[j][i] & 0xffff0000u);
+                const float m0 = __uint_as_float(wh[j][i] << 16) + l0;
+                const float m1 = __uint_as_float(wh[j][i] & 0xffff0000u) + l1;
+                ss_lo = fmaf(l0, l0, ss_lo);
+                ss_lo = fmaf(l1, l1, ss_lo);
+                ss_mean = fmaf(m0, m0, ss_mean);
+                ss_mean = fmaf(m1, m1, ss_mean);
             }
-        ss += dpp_f(ss, 0xB1);                     // the row's other half (lane ^ 1)
-        const float m = wave_max(ss);
-        if (lane == 0) a.k_lo_max[(size_t)bh * a.mask_words + g] = __builtin_sqrtf(m) * (1.f + 1.f / 1024.f);
+        ss_lo += dpp_f(ss_lo, 0xB1);               // the row's other half (lane ^ 1)
+        ss_mean += dpp_f(ss_mean, 0xB1);
+        const float lo = wave_max(ss_lo), mean = wave_max(ss_mean);
+        if (lane == 0) {
+            const float2 b = {__builtin_sqrtf(mean) * (1.f + 1.f / 1024.f), __builtin_sqrtf(lo) * (1.f + 1.f / 1024.f)};
+            *reinterpret_cast<float2 *>(a.k_bounds + ((size_t)bh * a.mask_words + g) * 2) = b;
+        }
     }
 }
 
@@ -707,7 +720,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     float *qs = smem;                                     // [G][D] query means, before S is formed
     if (a.q_bf16) BlockPool<bf16, D>::run(a, bh, I0, g_cnt, qs);
     else BlockPool<float, D>::run(a, bh, I0, g_cnt, qs);
-    remainder_bounds<D>(a, bh, I0 / G, n_grp);
+    residual_bounds<D>(a, bh, I0 / G, n_grp);
     __syncthreads();
     {
         // Proxy rows on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, fp32

@@ -172,16 +172,19 @@ enum {
                                                          (highest first, lower index on
                                                          ties), then band (highest first),
                                                          then I                             */
-    SA_BUF_K_LO_MAX,      /* fp32 [B,H,words]            for each residual tile: an upper
-                                                         bound on the Euclidean norm of its
-                                                         32 key-mean remainder rows (the
-                                                         forward skips a tile whose logits
-                                                         are provably negligible without
-                                                         forming their remainder part);
-                                                         written by centroid routes only:
-                                                         a route under SA_FLAG_PAMA leaves
-                                                         it unset and the forward of such
-                                                         a route does not read it          */
+    SA_BUF_K_BOUNDS,      /* fp32 [B,H,words,2]          for each residual tile, upper
+                                                         bounds on the Euclidean norms of
+                                                         [0] its 32 key means as the forward
+                                                         forms them (bf16 part plus
+                                                         remainder) and [1] its 32 key-mean
+                                                         remainder rows; the forward drops
+                                                         a tile whose logits they prove
+                                                         negligible, unloaded ([0]) or after
+                                                         its bf16 part ([1]); written by
+                                                         centroid routes only: a route under
+                                                         SA_FLAG_PAMA leaves it unset and
+                                                         the forward of such a route does
+                                                         not read it                       */
     SA_ROUTE_NBUF
 };
 
@@ -196,7 +199,7 @@ typedef struct sa_route {
     float    *row_stats;
     int32_t  *cost;
     int32_t  *work_order;
-    float    *k_lo_max;
+    float    *k_bounds;
     int32_t   kv_idx_cap;     /* row length of kv_idx, >= sparse_attn_kv_idx_cap(p) */
 } sa_route;
 
@@ -209,7 +212,7 @@ int32_t sparse_attn_kv_idx_cap(const sa_params *p);
  * to bytes[0..SA_ROUTE_NBUF-1].  Host only; no HIP calls. */
 sa_status sparse_attn_route_sizes(const sa_params *p, int32_t kv_idx_cap, size_t *bytes);
 
-/* Step 1 (routing).  Reads q, k, v once; writes every buffer of *r (k_lo_max
+/* Step 1 (routing).  Reads q, k, v once; writes every buffer of *r (k_bounds
  * only without SA_FLAG_PAMA, which may then be NULL).  Nothing of size
  * n_qb x n_kb is written except the kv_idx lists and the bit mask. */
 sa_status sparse_attn_route(const sa_params *p, const void *q, const void *k, const void *v,

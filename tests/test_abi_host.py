@@ -183,7 +183,7 @@ def test_route_sizes_wan13b():
     assert s["kv_mask"] == 12 * 256 * 8 * 4
     assert s["k_mean"] == 12 * 256 * 128 * 4
     assert s["work_order"] == 12 * 256 * 4
-    assert s["k_lo_max"] == 12 * 8 * 4
+    assert s["k_bounds"] == 12 * 8 * 2 * 4
     with pytest.raises(B.SparseAttnError) as e:
         B.route_sizes(p, cap - 1)
     assert e.value.status == B.SA_ERR_CAPACITY
@@ -228,16 +228,16 @@ def test_misaligned_device_pointers_rejected_before_launch():
     assert B.lib.sparse_attn_forward(ctypes.byref(p), bad, good, good, ctypes.byref(r), good, None, None) == \
         B.SA_ERR_INVALID_ARG
     assert b"aligned" in B.lib.sparse_attn_last_error()
-    r_bad = B.SaRoute(*([good] * (len(B.BUFFERS) - 1) + [bad]), 1 << 10)      # k_lo_max misaligned
+    r_bad = B.SaRoute(*([good] * (len(B.BUFFERS) - 1) + [bad]), 1 << 10)      # k_bounds misaligned
     assert B.lib.sparse_attn_route(ctypes.byref(p), good, good, good, ctypes.byref(r_bad), None) == \
         B.SA_ERR_INVALID_ARG
-    assert b"k_lo_max" in B.lib.sparse_attn_last_error()
+    assert b"k_bounds" in B.lib.sparse_attn_last_error()
     # the forward reads the bounds only of a centroid route with the residual fold
     assert B.lib.sparse_attn_forward(ctypes.byref(p), good, good, good, ctypes.byref(r_bad), good, None, None) == \
         B.SA_ERR_INVALID_ARG
     # a centroid route writes the bounds, also under SA_FLAG_NO_RESIDUAL
-    r_null = B.SaRoute(*([good] * (len(B.BUFFERS) - 1) + [0]), 1 << 10)      # k_lo_max NULL
+    r_null = B.SaRoute(*([good] * (len(B.BUFFERS) - 1) + [0]), 1 << 10)      # k_bounds NULL
     assert B.lib.sparse_attn_route(ctypes.byref(params(flags=B.FLAG_NO_RESIDUAL)), good, good, good,
                                    ctypes.byref(r_null), None) == B.SA_ERR_INVALID_ARG
-    assert b"k_lo_max" in B.lib.sparse_attn_last_error()
+    assert b"k_bounds" in B.lib.sparse_attn_last_error()
     assert B.lib.sparse_attn_permute_tokens(1, 1, 64, 64, 0, 0, 0, None, 0, bad, good, None) == B.SA_ERR_INVALID_ARG

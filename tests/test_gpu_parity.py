@@ -258,35 +258,39 @@ def test_no_residual_flag():
 
 
 # ----------------------------------------------------------------------------- early residual test
-def _remainder_norm_max(rt):
-    """Largest Euclidean norm of each residual tile's key-mean remainder rows,
-    in fp64 from the route's own tiles: [B, H, words]."""
+def _residual_norm_max(rt):
+    """Largest Euclidean norms, per residual tile, of its key means as the
+    forward forms them (bf16 part plus remainder) and of its remainder rows,
+    in fp64 from the route's own tiles: [B, H, words, 2]."""
     t = rt.kv_split[:, :, 0].cpu().double()                 # [B, H, words, 64, d]
-    return t[:, :, :, 32:].pow(2).sum(-1).sqrt().amax(-1)
+    hi, lo = t[:, :, :, :32], t[:, :, :, 32:]
+    return torch.stack([(hi + lo).pow(2).sum(-1).sqrt().amax(-1), lo.pow(2).sum(-1).sqrt().amax(-1)], -1)
 
 
 @pytest.mark.parametrize("d,bq,bk,dt,fused", [(128, 128, 64, "bf16", False), (64, 64, 128, "bf16", False),
                                               (128, 128, 128, "bf16", True), (64, 64, 64, "f32", False)])
-def test_remainder_bounds(d, bq, bk, dt, fused):
-    """k_lo_max bounds the norms of every residual tile's remainder rows from
-    above, within 2^-9 of the largest (zero for tiles past the last block)."""
+def test_residual_bounds(d, bq, bk, dt, fused):
+    """k_bounds bounds the norms of every residual tile's key means and of its
+    remainder rows from above, within 2^-9 of the largest (zero for tiles past
+    the last block)."""
     w = S.small("lob", 2, 3, d, (5, 9, 29), bq, bk, 0.02, dtype=dt)
-    say(f"[case] remainder bounds d{d} {bq}x{bk} {dt} fused={fused} N{w.N}")
+    say(f"[case] residual bounds d{d} {bq}x{bk} {dt} fused={fused} N{w.N}")
     _, _, _, Q, K, V = make(w)
     rt = sa().route(Q, K, V, cfg_for(w, fused=fused))
     torch.cuda.synchronize()
-    ref = _remainder_norm_max(rt)
-    got = rt.k_lo_max.cpu().double()
+    ref = _residual_norm_max(rt)
+    got = rt.k_bounds.cpu().double()
     assert (got >= ref).all() and (got <= ref * (1 + 2.0 ** -9)).all()
 
 
 @pytest.mark.parametrize("fused", [False, True])
 def test_early_residual_test_changes_nothing(fused):
-    """The forward's early test of a residual tile (from the key means' bf16
-    part and the route's remainder bounds) skips only tiles that the full test
-    finds negligible: output and LSE are bitwise those of the same forward with
-    the bounds set to +inf, which turns the early test off.  Sharp queries and
-    64-token key blocks, so that most residual tiles are negligible."""
+    """The forward's early tests of a residual tile (from the norms alone, then
+    from the key means' bf16 part, with the route's bounds) skip only tiles
+    that the full test finds negligible: output and LSE are bitwise those of
+    the same forward with the bounds set to +inf, which turns the early tests
+    off.  Sharp queries and 64-token key blocks, so that most residual tiles
+    are negligible."""
     m = sa()
     w = S.small("skip", 1, 4, 128, (8, 16, 48), 128, 64, 0.02, qscale=12.0)
     say(f"[case] early residual test fused={fused} N{w.N}")
@@ -295,8 +299,8 @@ def test_early_residual_test_changes_nothing(fused):
     rt = m.route(Q, K, V, cfg)
     O1, L1 = m.forward(Q, K, V, rt, cfg, lse=True)
     torch.cuda.synchronize()
-    assert torch.isfinite(rt.k_lo_max).all()
-    rt.k_lo_max.fill_(float("inf"))
+    assert torch.isfinite(rt.k_bounds).all()
+    rt.k_bounds.fill_(float("inf"))
     O2, L2 = m.forward(Q, K, V, rt, cfg, lse=True)
     torch.cuda.synchronize()
     assert torch.equal(O1, O2) and torch.equal(L1, L2)
@@ -313,9 +317,9 @@ def test_pama_route_bounds_unused():
     _, _, _, Q, K, V = make(w)
     cfg = cfg_for(w, mode=R.TOPP, proxy=R.PAMA)
     rt = m.route(Q, K, V, cfg)
-    rt.k_lo_max.fill_(float("nan"))
+    rt.k_bounds.fill_(float("nan"))
     O1, L1 = m.forward(Q, K, V, rt, cfg, lse=True)
-    rt.k_lo_max.fill_(float("-inf"))
+    rt.k_bounds.fill_(float("-inf"))
     O2, L2 = m.forward(Q, K, V, rt, cfg, lse=True)
     torch.cuda.synchronize()
     assert torch.equal(O1, O2) and torch.equal(L1, L2)
@@ -323,7 +327,7 @@ def test_pama_route_bounds_unused():
     cfg_c = cfg_for(w, mode=R.TOPP)
     rt_c = m.route(Q, K, V, cfg_c)
     O3 = m.forward(Q, K, V, rt_c, cfg_c)
-    rt_c.k_lo_max.fill_(float("-inf"))
+    rt_c.k_bounds.fill_(float("-inf"))
     O4 = m.forward(Q, K, V, rt_c, cfg_c)
     torch.cuda.synchronize()
     assert not torch.equal(O3, O4)
